@@ -1,0 +1,268 @@
+"""Benchmark of the SRFT-rotated int4 KV-cache hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+
+One step is one decode step of the hot path over every layer of the workload (layers folded
+into the batch): append-quantize the new token's K and V (write path), then fused
+dequant + decode attention over the whole cache (read path).  The fp16-KV decode of the same
+build and the bulk (prefill) quantize are timed the same way and reported beside it.
+
+Timing: each measured unit is captured in a HIP graph that runs it over R different copies of
+the cache (R copies span >= 1 GB, four times the MI355X Infinity Cache), so every rep reads
+cold data; graphs are replayed back-to-back between HIP events after W warm-up steps, bracketed
+by device synchronizations.  Inputs are resident in HBM before the timed region starts.
+
+Prints ONE JSON line (rank 0).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+COLD_BYTES = 1 << 30
+METRIC = "decode-attn effective KV GB/s & % HBM peak; quantize Mvectors/s; vs fp16-KV"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=0, help="timed steps (default: 4 graph replays)")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    return ap.parse_args()
+
+
+class Timer:
+    """Replay a list of captured graphs K times between HIP events on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, graphs, steps, warmup):
+        torch = self.torch
+        R = len(graphs)
+        for i in range(warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        t0 = time.perf_counter()
+        ev[0].record()
+        for i in range(steps):
+            graphs[i % R].replay()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        total = ev[0].elapsed_time(ev[steps])
+        return {"ms_mean": total / steps, "ms_median": statistics.median(per),
+                "ms_p10": float(np.percentile(per, 10)), "ms_p90": float(np.percentile(per, 90)),
+                "wall_ms_per_step": 1e3 * wall / steps}
+
+
+def capture(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # warm (allocations, first-launch work) outside the capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def cpu_baseline(w, budget_s):
+    """Time the CPU oracle, as it stands, on a bounded sample of the same workload."""
+    from kv_cache_quantization_srft_amd import synth
+    from oracle import kvq_oracle as O
+
+    s = synth.signs(w)
+    layers_done, t_dec, t_q, vec_q = 0, 0.0, 0.0, 0
+    t_start = time.perf_counter()
+    layer = 0
+    while layers_done < 1 or time.perf_counter() - t_start < budget_s:
+        k = synth.kv(w, layer, synth.K_TENSOR)
+        v = synth.kv(w, layer, synth.V_TENSOR)
+        q = synth.query(w, layer)
+        lk = O.calibrate_lambda(k, s, w.n_cal)[:, :, None, :] if w.calibrate else 1.0
+        lv = O.calibrate_lambda(v, s, w.n_cal)[:, :, None, :] if w.calibrate else 1.0
+        t0 = time.perf_counter()
+        kc, ks = O.quantize(k, s, lk, w.k_bits)
+        vc, vs = O.quantize(v, s, lv, w.v_bits)
+        t1 = time.perf_counter()
+        O.decode_attention_quantized(q, kc, ks, vc, vs, s, s, lk, lv, w.seq_len)
+        t2 = time.perf_counter()
+        t_q += t1 - t0
+        t_dec += t2 - t1
+        vec_q += k.size // w.head_dim + v.size // w.head_dim
+        layers_done += 1
+        layer = (layer + 1) % w.layers
+    bytes_layer = w.batch * w.kv_heads * w.seq_len * (w.head_dim * (w.k_bits + w.v_bits) // 8 + 2 * 2 * w.head_dim // 16)
+    return {
+        "value": bytes_layer * layers_done / t_dec / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": (f"{layers_done} of {w.layers} layers: oracle decode (dequantize K,V by O(d^2) DFT + attention "
+                   f"over {w.seq_len} tokens, {w.q_heads} heads); numpy float64, single thread"),
+        "decode_ms_per_layer": 1e3 * t_dec / layers_done,
+        "quantize_Mvectors_per_s": vec_q / t_q / 1e6,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "detail": "multi-GPU sharding is a design note only (DESIGN.md)"}))
+        sys.exit(2)
+    import torch
+
+    from kv_cache_quantization_srft_amd import kvq, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = synth.WORKLOADS[args.workload]
+    L, B, H, Hq, d, S = w.layers, w.batch, w.kv_heads, w.q_heads, w.head_dim, w.seq_len
+    LB = L * B
+    log(f"workload {w.name}: layers {L} batch {B} kv {H} q {Hq} d {d} seq {S} K{w.k_bits}V{w.v_bits}")
+    s = torch.from_numpy(synth.signs(w)).cuda()
+    lay = kvq.make_layout(LB, H, Hq, d, S, k_bits=w.k_bits, v_bits=w.v_bits)
+
+    # ---- synthetic cache, resident in HBM (layers folded into the batch) ----
+    t0 = time.perf_counter()
+    if w.cid in (4, 5):
+        kx = torch.cat([synth.torch_kv(w, l, synth.K_TENSOR, "cuda") for l in range(L)])
+        vx = torch.cat([synth.torch_kv(w, l, synth.V_TENSOR, "cuda") for l in range(L)])
+    else:
+        kx = torch.from_numpy(np.concatenate([synth.kv(w, l, synth.K_TENSOR) for l in range(L)])).cuda()
+        vx = torch.from_numpy(np.concatenate([synth.kv(w, l, synth.V_TENSOR) for l in range(L)])).cuda()
+    q = torch.from_numpy(np.concatenate([synth.query(w, l) for l in range(L)])).cuda()
+    log(f"generated inputs in {time.perf_counter() - t0:.1f}s")
+
+    lam_k = lam_v = None
+    if w.calibrate:
+        lam_k = torch.empty(LB * H * d, dtype=torch.float32, device="cuda")
+        lam_v = torch.empty_like(lam_k)
+        kvq.kvq_calibrate_lambda(lay, kx, S, w.n_cal, s, 0, lam_k)
+        kvq.kvq_calibrate_lambda(lay, vx, S, w.n_cal, s, 0, lam_v)
+    lbs = H * d if w.calibrate else 0
+
+    def new_planes():
+        return (torch.empty(kvq.kvq_codes_bytes(lay, w.k_bits), dtype=torch.uint8, device="cuda"),
+                torch.empty(kvq.kvq_scales_bytes(lay) // 2, dtype=torch.int16, device="cuda"),
+                torch.empty(kvq.kvq_codes_bytes(lay, w.v_bits), dtype=torch.uint8, device="cuda"),
+                torch.empty(kvq.kvq_scales_bytes(lay) // 2, dtype=torch.int16, device="cuda"))
+
+    def quantize_all(p, xk, xv):
+        kvq.kvq_quantize(lay, w.k_bits, xk, 0, S, s, 0, lam_k, lbs, p[0], p[1])
+        kvq.kvq_quantize(lay, w.v_bits, xv, 0, S, s, 0, lam_v, lbs, p[2], p[3])
+
+    base = new_planes()
+    quantize_all(base, kx, vx)
+    torch.cuda.synchronize()
+
+    q_bytes = sum(t.numel() * t.element_size() for t in base)
+    f16_bytes = 2 * kx.numel() * 2
+    n_q = max(1, -(-COLD_BYTES // q_bytes))
+    n_f = max(1, -(-COLD_BYTES // f16_bytes))
+    planes = [base] + [tuple(t.clone() for t in base) for _ in range(n_q - 1)]
+    kv16 = [(kx, vx)] + [(kx.clone(), vx.clone()) for _ in range(n_f - 1)]
+    torch.cuda.synchronize()
+    log(f"cache copies: {n_q} quantized x {q_bytes / 1e6:.1f} MB, {n_f} fp16 x {f16_bytes / 1e6:.1f} MB")
+
+    ws = torch.empty(kvq.kvq_decode_attn_workspace_bytes(lay, S), dtype=torch.uint8, device="cuda")
+    out = torch.empty(LB * Hq * d, dtype=torch.float32, device="cuda")
+    out16 = torch.empty_like(out)
+    # the step's new token: the last cache position of every layer, re-quantized in place
+    k_new = kx[:, :, S - 1:S].contiguous()
+    v_new = vx[:, :, S - 1:S].contiguous()
+
+    def decode(p):
+        kvq.kvq_decode_attn(lay, q, p[0], p[1], p[2], p[3], S, None, s, s, 0, lam_k, lam_v, lbs, 0.0, ws, out)
+
+    def step(p):
+        kvq.kvq_quantize(lay, w.k_bits, k_new, S - 1, 1, s, 0, lam_k, lbs, p[0], p[1])
+        kvq.kvq_quantize(lay, w.v_bits, v_new, S - 1, 1, s, 0, lam_v, lbs, p[2], p[3])
+        decode(p)
+
+    def graph_over(copies, fn):
+        return [capture(torch, lambda c=c: fn(c)) for c in copies]
+
+    timer = Timer(torch)
+    R = len(planes)
+    steps = args.steps if args.steps > 0 else 4 * R
+    g_step = graph_over(planes, step)
+    res_step = timer.run(g_step, steps, args.warmup)
+    g_dec = graph_over(planes, decode)
+    res_dec = timer.run(g_dec, steps, args.warmup)
+    g_f16 = graph_over(kv16, lambda kv: kvq.kvq_decode_attn_fp16(lay, q, kv[0], kv[1], S, None, 0.0, ws, out16))
+    res_f16 = timer.run(g_f16, max(steps, 4 * len(kv16)), args.warmup)
+    # bulk quantize: all layers, K and V, from rotating fp16 copies into rotating planes
+    g_bq = [capture(torch, lambda i=i: quantize_all(planes[i % R], *kv16[i % len(kv16)]))
+            for i in range(max(R, len(kv16)))]
+    res_bq = timer.run(g_bq, 2 * len(g_bq), args.warmup)
+    del g_step, g_dec, g_f16, g_bq
+
+    dec_bytes = q_bytes  # every code and scale byte of the cache is read once per decode step
+    n_vec = 2 * LB * H * S
+    bq_bytes = n_vec * 2 * d + q_bytes
+    dec_gbps = dec_bytes / (res_dec["ms_mean"] * 1e-3) / 1e9
+    step_gbps = dec_bytes / (res_step["ms_mean"] * 1e-3) / 1e9
+    f16_gbps = f16_bytes / (res_f16["ms_mean"] * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(step_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res_step["ms_mean"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": L, "batch": B, "kv_heads": H, "q_heads": Hq, "head_dim": d,
+                   "seq_len": S, "k_bits": w.k_bits, "v_bits": w.v_bits, "group": 16,
+                   "lambda": "calibrated (first 512 tokens)" if w.calibrate else "1",
+                   "storage": f"int{w.k_bits} K / int{w.v_bits} V codes + fp16 group scales",
+                   "parallelism": "single GPU; layers folded into the batch", "cold_cache_copies": R},
+        "step_breakdown": {"step": res_step, "decode_only": res_dec},
+        "decode": {"GBps": round(dec_gbps, 2), "frac_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                   "bytes_per_step": dec_bytes, "ms": round(res_dec["ms_mean"], 5)},
+        "fp16_decode": {"GBps": round(f16_gbps, 2), "frac_hbm_peak": round(f16_gbps / HBM_PEAK_GBPS, 4),
+                        "bytes_per_step": f16_bytes, "ms": round(res_f16["ms_mean"], 5),
+                        "speedup_quantized_vs_fp16": round(res_f16["ms_mean"] / res_dec["ms_mean"], 3),
+                        "fp16_equivalent_GBps_of_quantized": round(f16_bytes / (res_dec["ms_mean"] * 1e-3) / 1e9, 2)},
+        "quantize_bulk": {"Mvectors_per_s": round(n_vec / (res_bq["ms_mean"] * 1e-3) / 1e6, 2),
+                          "GBps_moved": round(bq_bytes / (res_bq["ms_mean"] * 1e-3) / 1e9, 2),
+                          "frac_hbm_peak": round(bq_bytes / (res_bq["ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                          "vectors": n_vec, "ms": round(res_bq["ms_mean"], 5)},
+        "roofline": {"bound": "hbm", "kernel": "kvq_decode_attn (whole call)",
+                     "achieved": round(dec_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": dec_bytes},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle sample")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

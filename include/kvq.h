@@ -1,0 +1,179 @@
+/*
+ * kvq.h -- C ABI of libkvq: SRFT-rotated low-bit KV-cache quantization and fused
+ * single-token decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * Method (sources are web pages, cited by title and section):
+ *   [QF] "When Quantization Is Free: An int4 KV Cache That Outruns fp16 on Apple Silicon",
+ *        gist.science explainer, technical summary, Methodology 1 (SRFT(x) = pack(F diag(s) x),
+ *        F the unitary DFT, s a fixed random sign vector), Methodology 2 (one fused write kernel:
+ *        sign, FFT, Hermitian pack, per-channel lambda, per-group absmax, signed int4/int8
+ *        rounding, nibble packing) and Methodology 3 (per-channel + per-group-of-16 scaling).
+ *   [KS] xugj520 article on KVSplit, "核心技术创新": keys 8-bit, values 4-bit (K8V4).
+ *   [GM] hotdry blog on Gemini KV caches on Apple Silicon, "Flash Attention 与 Metal 内核融合":
+ *        tiled attention with an online softmax.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless the comment says "host".  The caller owns and
+ *     allocates every buffer; the library allocates nothing, frees nothing and keeps no
+ *     pointer after the call returns.
+ *   - Every compute call is asynchronous on `stream` (a hipStream_t passed as void*; NULL is the
+ *     default stream).  Launch errors are reported as KVQ_ERR_HIP; faults during execution
+ *     surface at the caller's next synchronization.
+ *   - Arguments are validated on the host before any HIP call.  On any error the call returns
+ *     without launching work and leaves every output untouched; kvq_last_error_message() then
+ *     holds a thread-local description.
+ *   - Plane, input and output pointers must be 16-byte aligned (KVQ_ERR_MISALIGNED otherwise);
+ *     sign and lambda vectors must be 4-byte aligned.
+ *   - The library is reentrant and thread-safe; calls on distinct streams may overlap.
+ *   - Non-finite inputs give unspecified (but in-range) codes.
+ *
+ * Cache layout ("planes"; separate code and scale planes per tensor)
+ *   For a tensor quantized with `bits` (4 or 8), head dimension d and group size 16:
+ *     codes : uint8 [batch, kv_heads, capacity, d*bits/8]
+ *             int4: byte j of a token holds channel 2j in its low nibble and channel 2j+1 in its
+ *             high nibble, each a two's-complement 4-bit code in [-7, 7];
+ *             int8: one two's-complement byte per channel, codes in [-127, 127].
+ *     scales: fp16  [batch, kv_heads, capacity, d/16], one scale per group of 16 consecutive
+ *             channels of the rotated vector.
+ *   Channel c of the rotated vector is the real, norm-preserving layout of the unitary DFT of
+ *   s*x: c=0 -> Re X0, c=1 -> Re X_{d/2}, c=2k -> sqrt2 Re Xk, c=2k+1 -> sqrt2 Im Xk (0<k<d/2),
+ *   with Xk = d^-1/2 sum_n s_n x_n exp(-2 pi i k n / d).
+ *   `batch` may fold layers (batch = layers x sequences): sign and lambda take a batch stride.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, q_heads % kv_heads != 0, range */
+  KVQ_ERR_UNSUPPORTED = 2,      /* head_dim not 128/256, group != 16, bits not 4/8, G > 64 */
+  KVQ_ERR_MISALIGNED = 3,       /* a pointer violates the alignment rule above */
+  KVQ_ERR_WORKSPACE_TOO_SMALL = 4,
+  KVQ_ERR_HIP = 5               /* a HIP runtime call or kernel launch failed */
+} kvq_status;
+
+/* Host struct describing one quantized cache (passed by const pointer, read during the call). */
+typedef struct {
+  int32_t batch;      /* sequences (optionally x layers); >= 1                                */
+  int32_t kv_heads;   /* >= 1                                                                   */
+  int32_t q_heads;    /* multiple of kv_heads; GQA ratio G = q_heads / kv_heads; head h reads  */
+                      /* kv head h / G                                                          */
+  int32_t head_dim;   /* d: 128 or 256                                                          */
+  int32_t group_size; /* 16                                                                     */
+  int32_t k_bits;     /* 4 or 8                                                                 */
+  int32_t v_bits;     /* 4                                                                      */
+  int32_t capacity;   /* tokens allocated per (sequence, kv head): the token stride of planes   */
+} kvq_layout;
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t kvq_version(void);
+
+/* Name of a status code (static string). */
+const char* kvq_status_string(kvq_status status);
+
+/* Thread-local text describing the last failed call on this thread ("" if none). */
+const char* kvq_last_error_message(void);
+
+/* Bytes of one code plane: batch * kv_heads * capacity * head_dim * bits / 8.
+ * Footprint formula of the hotdry blog ("INT8/INT4 量化策略") with b-bit codes.
+ * Returns 0 if the layout or bits are invalid. Host-only, no HIP call. */
+size_t kvq_codes_bytes(const kvq_layout* layout, int32_t bits);
+
+/* Bytes of one scale plane: batch * kv_heads * capacity * (head_dim / 16) * 2.  0 if invalid. */
+size_t kvq_scales_bytes(const kvq_layout* layout);
+
+/*
+ * kvq_quantize -- the write path ([QF] Methodology 2 and 3).
+ * For every vector x = x_f16[b, h, t, :] (t < n_tok) writes token pos + t of row (b, h):
+ *   u      = SRFT_s(x) / lambda                  (s = sign row b, lambda = lambda row (b, h))
+ *   scale  = fp16(max_{c in group} |u_c| / qmax) (round to nearest even, saturated at 65504)
+ *   code_c = clamp(round_half_even(u_c / scale), -qmax, qmax), 0 where scale == 0
+ * qmax = 7 (bits 4) or 127 (bits 8).  The code decision is taken in float32.
+ *   bits      : 4 or 8 (the tensor's width; use layout->k_bits for K, layout->v_bits for V)
+ *   x_f16     : fp16 [batch, kv_heads, n_tok, head_dim], contiguous
+ *   pos,n_tok : 0 <= pos, 1 <= n_tok, pos + n_tok <= capacity
+ *   sign      : float [*, head_dim] of +-1; row b starts at b * sign_batch_stride (0 = shared)
+ *   lambda    : float [*, kv_heads, head_dim], > 0; row b at b * lambda_batch_stride (0 = shared);
+ *               NULL means lambda = 1
+ *   codes     : code plane (see layout above); scales: scale plane
+ * Only the written tokens' bytes change.
+ */
+kvq_status kvq_quantize(const kvq_layout* layout, int32_t bits, const void* x_f16, int32_t pos,
+                        int32_t n_tok, const float* sign, int64_t sign_batch_stride,
+                        const float* lambda, int64_t lambda_batch_stride, void* codes,
+                        void* scales, void* stream);
+
+/*
+ * kvq_dequantize -- inverse of the write path, for inspection and tests.
+ *   out[b, h, t, :] = s * SRFT^-1(lambda * code * scale) for tokens pos .. pos+n_tok-1,
+ *   out: float [batch, kv_heads, n_tok, head_dim], contiguous.  Other arguments as kvq_quantize.
+ */
+kvq_status kvq_dequantize(const kvq_layout* layout, int32_t bits, const void* codes,
+                          const void* scales, int32_t pos, int32_t n_tok, const float* sign,
+                          int64_t sign_batch_stride, const float* lambda,
+                          int64_t lambda_batch_stride, float* out, void* stream);
+
+/*
+ * kvq_calibrate_lambda -- per-channel calibration of lambda (the pages call lambda "learned or
+ * calibrated", [QF] Methodology 2): lambda[b, h, c] = max_{t < n_cal} |SRFT_s(x[b, h, t])_c|,
+ * replaced by 1 where that maximum is 0.
+ *   x_f16  : fp16 [batch, kv_heads, n_tok, head_dim] contiguous; 1 <= n_cal <= n_tok
+ *   lambda : float [batch, kv_heads, head_dim] output
+ */
+kvq_status kvq_calibrate_lambda(const kvq_layout* layout, const void* x_f16, int32_t n_tok,
+                                int32_t n_cal, const float* sign, int64_t sign_batch_stride,
+                                float* lambda, void* stream);
+
+/* Workspace bytes kvq_decode_attn / kvq_decode_attn_fp16 need for any seq_len <= max_seq_len.
+ * 0 if the layout is invalid. */
+size_t kvq_decode_attn_workspace_bytes(const kvq_layout* layout, int32_t max_seq_len);
+
+/*
+ * kvq_decode_attn -- fused dequant + single-token decode attention over the quantized cache
+ * ([GM] tiled attention with online softmax; [QF] Methodology 1 rotation).  For every sequence
+ * b and query head h (kv head j = h / G), with L = seq_lens ? seq_lens[b] : seq_len:
+ *   out[b, h] = sum_{t<L} softmax_t(sm_scale * q[b,h] . x_hat_K[b,j,t]) x_hat_V[b,j,t]
+ * where x_hat = s * SRFT^-1(lambda * code * scale).  Computed in the rotated domain: the query is
+ * rotated once, scores and the value sum use the codes directly, and the output is
+ * inverse-rotated once.
+ *   q_f16        : fp16 [batch, q_heads, head_dim] contiguous
+ *   k_codes, ... : the four planes (K with layout->k_bits, V with layout->v_bits)
+ *   seq_len      : 1 <= seq_len <= capacity (the maximum length when seq_lens is given)
+ *   seq_lens     : device int32 [batch] or NULL; entries are clamped to [0, seq_len]; a sequence
+ *                  of length 0 gets a zero output
+ *   sign_k/v     : float [*, head_dim] +-1, row stride sign_batch_stride (0 = shared)
+ *   lambda_k/v   : float [*, kv_heads, head_dim] or NULL (= 1), row stride lambda_batch_stride
+ *   sm_scale     : softmax scale; <= 0 selects 1/sqrt(head_dim)
+ *   workspace    : >= kvq_decode_attn_workspace_bytes(layout, seq_len) bytes, 256-byte aligned,
+ *                  contents irrelevant on entry; in use until the work on `stream` completes
+ *   out          : float [batch, q_heads, head_dim]
+ */
+kvq_status kvq_decode_attn(const kvq_layout* layout, const void* q_f16, const void* k_codes,
+                           const void* k_scales, const void* v_codes, const void* v_scales,
+                           int32_t seq_len, const int32_t* seq_lens, const float* sign_k,
+                           const float* sign_v, int64_t sign_batch_stride, const float* lambda_k,
+                           const float* lambda_v, int64_t lambda_batch_stride, float sm_scale,
+                           void* workspace, size_t workspace_bytes, float* out, void* stream);
+
+/*
+ * kvq_decode_attn_fp16 -- the same decode attention over an unquantized fp16 cache (the
+ * comparator): k_f16, v_f16 are fp16 [batch, kv_heads, capacity, head_dim]; no rotation, no
+ * lambda.  layout->k_bits/v_bits are ignored.  Other arguments as kvq_decode_attn.
+ */
+kvq_status kvq_decode_attn_fp16(const kvq_layout* layout, const void* q_f16, const void* k_f16,
+                                const void* v_f16, int32_t seq_len, const int32_t* seq_lens,
+                                float sm_scale, void* workspace, size_t workspace_bytes,
+                                float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,249 @@
+// C ABI of libkvq (declared in include/kvq.h): host-side validation, error reporting and
+// dispatch to the gfx950 kernels.  Validation runs before any HIP call, so a rejected call
+// launches nothing and touches no output.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvq_status fail(kvq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = std::string(kvq_status_string(st)) + ": " + buf;
+  return st;
+}
+
+kvq_status ok() {
+  g_last_error.clear();
+  return KVQ_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Checks shared by every entry point that takes a layout.
+kvq_status check_layout(const kvq_layout* L, const char* fn) {
+  if (!L) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: layout is NULL", fn);
+  if (L->batch < 1 || L->kv_heads < 1 || L->capacity < 1)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: batch (%d), kv_heads (%d) and capacity (%d) must be >= 1", fn,
+                L->batch, L->kv_heads, L->capacity);
+  if (L->head_dim != 128 && L->head_dim != 256)
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 128, 256)", fn, L->head_dim);
+  if (L->group_size != 16) return fail(KVQ_ERR_UNSUPPORTED, "%s: group_size %d (supported: 16)", fn, L->group_size);
+  const long long rows = (long long)L->batch * L->kv_heads;
+  if (rows * (long long)L->capacity > (1LL << 40))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: batch*kv_heads*capacity too large", fn);
+  return KVQ_OK;
+}
+
+kvq_status check_bits(int bits, const char* fn, const char* what) {
+  if (bits != 4 && bits != 8) return fail(KVQ_ERR_UNSUPPORTED, "%s: %s %d (supported: 4, 8)", fn, what, bits);
+  return KVQ_OK;
+}
+
+kvq_status check_ptr(const void* p, size_t align, const char* fn, const char* name) {
+  if (!p) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: %s is NULL", fn, name);
+  if (!aligned(p, align)) return fail(KVQ_ERR_MISALIGNED, "%s: %s is not %zu-byte aligned", fn, name, align);
+  return KVQ_OK;
+}
+
+kvq_status check_opt_ptr(const void* p, size_t align, const char* fn, const char* name) {
+  if (p && !aligned(p, align)) return fail(KVQ_ERR_MISALIGNED, "%s: %s is not %zu-byte aligned", fn, name, align);
+  return KVQ_OK;
+}
+
+kvq_status check_range(const kvq_layout* L, int32_t pos, int32_t n_tok, const char* fn) {
+  if (pos < 0 || n_tok < 1 || (long long)pos + n_tok > L->capacity)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: token range [pos=%d, pos+n_tok=%lld) must lie in [0, capacity=%d)", fn,
+                pos, (long long)pos + n_tok, L->capacity);
+  long long tiles = ((long long)n_tok + 255) / 256;
+  if ((long long)L->batch * L->kv_heads * tiles > 0x7fffffffLL)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: too many vectors for one call", fn);
+  return KVQ_OK;
+}
+
+kvq_status check_strides(int64_t sign_bs, int64_t lambda_bs, const char* fn) {
+  if (sign_bs < 0 || lambda_bs < 0) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: batch strides must be >= 0", fn);
+  return KVQ_OK;
+}
+
+kvq_status hip_status(hipError_t e, const char* fn) {
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+#define KVQ_TRY(expr)               \
+  do {                              \
+    kvq_status _s = (expr);         \
+    if (_s != KVQ_OK) return _s;    \
+  } while (0)
+
+kvq_status check_decode_common(const kvq_layout* L, const void* q, int32_t seq_len, const int32_t* seq_lens,
+                               float sm_scale, void* workspace, size_t workspace_bytes, float* out,
+                               const char* fn) {
+  if (L->q_heads < 1 || L->q_heads % L->kv_heads != 0)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: q_heads (%d) must be a positive multiple of kv_heads (%d)", fn,
+                L->q_heads, L->kv_heads);
+  if (L->q_heads / L->kv_heads > 64)
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: GQA ratio %d (supported: <= 64)", fn, L->q_heads / L->kv_heads);
+  if (seq_len < 1 || seq_len > L->capacity)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: seq_len %d must lie in [1, capacity=%d]", fn, seq_len, L->capacity);
+  if (!std::isfinite(sm_scale)) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: sm_scale is not finite", fn);
+  KVQ_TRY(check_ptr(q, 16, fn, "q"));
+  KVQ_TRY(check_ptr(out, 16, fn, "out"));
+  KVQ_TRY(check_opt_ptr(seq_lens, 4, fn, "seq_lens"));
+  KVQ_TRY(check_ptr(workspace, 256, fn, "workspace"));
+  const size_t need = kvq_impl::decode_workspace_bytes(L->batch, L->kv_heads, L->q_heads, L->head_dim, seq_len);
+  if (workspace_bytes < need)
+    return fail(KVQ_ERR_WORKSPACE_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need);
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvq_version(void) { return 100; }
+
+const char* kvq_status_string(kvq_status s) {
+  switch (s) {
+    case KVQ_OK:
+      return "KVQ_OK";
+    case KVQ_ERR_INVALID_ARGUMENT:
+      return "KVQ_ERR_INVALID_ARGUMENT";
+    case KVQ_ERR_UNSUPPORTED:
+      return "KVQ_ERR_UNSUPPORTED";
+    case KVQ_ERR_MISALIGNED:
+      return "KVQ_ERR_MISALIGNED";
+    case KVQ_ERR_WORKSPACE_TOO_SMALL:
+      return "KVQ_ERR_WORKSPACE_TOO_SMALL";
+    case KVQ_ERR_HIP:
+      return "KVQ_ERR_HIP";
+  }
+  return "KVQ_UNKNOWN_STATUS";
+}
+
+const char* kvq_last_error_message(void) { return g_last_error.c_str(); }
+
+size_t kvq_codes_bytes(const kvq_layout* L, int32_t bits) {
+  if (check_layout(L, "kvq_codes_bytes") != KVQ_OK || (bits != 4 && bits != 8)) return 0;
+  return size_t(L->batch) * L->kv_heads * L->capacity * size_t(L->head_dim) * bits / 8;
+}
+
+size_t kvq_scales_bytes(const kvq_layout* L) {
+  if (check_layout(L, "kvq_scales_bytes") != KVQ_OK) return 0;
+  return size_t(L->batch) * L->kv_heads * L->capacity * size_t(L->head_dim / L->group_size) * 2;
+}
+
+kvq_status kvq_quantize(const kvq_layout* L, int32_t bits, const void* x_f16, int32_t pos, int32_t n_tok,
+                        const float* sign, int64_t sign_batch_stride, const float* lambda,
+                        int64_t lambda_batch_stride, void* codes, void* scales, void* stream) {
+  const char* fn = "kvq_quantize";
+  KVQ_TRY(check_layout(L, fn));
+  KVQ_TRY(check_bits(bits, fn, "bits"));
+  KVQ_TRY(check_range(L, pos, n_tok, fn));
+  KVQ_TRY(check_ptr(x_f16, 16, fn, "x"));
+  KVQ_TRY(check_ptr(sign, 4, fn, "sign"));
+  KVQ_TRY(check_opt_ptr(lambda, 4, fn, "lambda"));
+  KVQ_TRY(check_ptr(codes, 16, fn, "codes"));
+  KVQ_TRY(check_ptr(scales, 16, fn, "scales"));
+  KVQ_TRY(check_strides(sign_batch_stride, lambda_batch_stride, fn));
+  kvq_impl::QuantArgs a{L->batch, L->kv_heads, L->head_dim, bits, L->capacity, pos, n_tok, x_f16, sign,
+                        sign_batch_stride, lambda, lambda_batch_stride, codes, scales};
+  return hip_status(kvq_impl::launch_quantize(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+kvq_status kvq_dequantize(const kvq_layout* L, int32_t bits, const void* codes, const void* scales, int32_t pos,
+                          int32_t n_tok, const float* sign, int64_t sign_batch_stride, const float* lambda,
+                          int64_t lambda_batch_stride, float* out, void* stream) {
+  const char* fn = "kvq_dequantize";
+  KVQ_TRY(check_layout(L, fn));
+  KVQ_TRY(check_bits(bits, fn, "bits"));
+  KVQ_TRY(check_range(L, pos, n_tok, fn));
+  KVQ_TRY(check_ptr(codes, 16, fn, "codes"));
+  KVQ_TRY(check_ptr(scales, 16, fn, "scales"));
+  KVQ_TRY(check_ptr(sign, 4, fn, "sign"));
+  KVQ_TRY(check_opt_ptr(lambda, 4, fn, "lambda"));
+  KVQ_TRY(check_ptr(out, 16, fn, "out"));
+  KVQ_TRY(check_strides(sign_batch_stride, lambda_batch_stride, fn));
+  kvq_impl::DequantArgs a{L->batch, L->kv_heads, L->head_dim, bits, L->capacity, pos, n_tok, codes, scales, sign,
+                          sign_batch_stride, lambda, lambda_batch_stride, out};
+  return hip_status(kvq_impl::launch_dequantize(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+kvq_status kvq_calibrate_lambda(const kvq_layout* L, const void* x_f16, int32_t n_tok, int32_t n_cal,
+                                const float* sign, int64_t sign_batch_stride, float* lambda, void* stream) {
+  const char* fn = "kvq_calibrate_lambda";
+  KVQ_TRY(check_layout(L, fn));
+  if (n_tok < 1 || n_cal < 1 || n_cal > n_tok)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: need 1 <= n_cal (%d) <= n_tok (%d)", fn, n_cal, n_tok);
+  KVQ_TRY(check_ptr(x_f16, 16, fn, "x"));
+  KVQ_TRY(check_ptr(sign, 4, fn, "sign"));
+  KVQ_TRY(check_ptr(lambda, 4, fn, "lambda"));
+  KVQ_TRY(check_strides(sign_batch_stride, 0, fn));
+  kvq_impl::CalibArgs a{L->batch, L->kv_heads, L->head_dim, n_tok, n_cal, x_f16, sign, sign_batch_stride, lambda};
+  return hip_status(kvq_impl::launch_calibrate(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+size_t kvq_decode_attn_workspace_bytes(const kvq_layout* L, int32_t max_seq_len) {
+  if (check_layout(L, "kvq_decode_attn_workspace_bytes") != KVQ_OK) return 0;
+  if (L->q_heads < 1 || L->q_heads % L->kv_heads != 0 || max_seq_len < 1) return 0;
+  return kvq_impl::decode_workspace_bytes(L->batch, L->kv_heads, L->q_heads, L->head_dim, max_seq_len);
+}
+
+kvq_status kvq_decode_attn(const kvq_layout* L, const void* q_f16, const void* k_codes, const void* k_scales,
+                           const void* v_codes, const void* v_scales, int32_t seq_len, const int32_t* seq_lens,
+                           const float* sign_k, const float* sign_v, int64_t sign_batch_stride,
+                           const float* lambda_k, const float* lambda_v, int64_t lambda_batch_stride,
+                           float sm_scale, void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  const char* fn = "kvq_decode_attn";
+  KVQ_TRY(check_layout(L, fn));
+  KVQ_TRY(check_bits(L->k_bits, fn, "k_bits"));
+  if (L->v_bits != 4) return fail(KVQ_ERR_UNSUPPORTED, "%s: v_bits %d (supported: 4)", fn, L->v_bits);
+  KVQ_TRY(check_decode_common(L, q_f16, seq_len, seq_lens, sm_scale, workspace, workspace_bytes, out, fn));
+  KVQ_TRY(check_ptr(k_codes, 16, fn, "k_codes"));
+  KVQ_TRY(check_ptr(k_scales, 16, fn, "k_scales"));
+  KVQ_TRY(check_ptr(v_codes, 16, fn, "v_codes"));
+  KVQ_TRY(check_ptr(v_scales, 16, fn, "v_scales"));
+  KVQ_TRY(check_ptr(sign_k, 4, fn, "sign_k"));
+  KVQ_TRY(check_ptr(sign_v, 4, fn, "sign_v"));
+  KVQ_TRY(check_opt_ptr(lambda_k, 4, fn, "lambda_k"));
+  KVQ_TRY(check_opt_ptr(lambda_v, 4, fn, "lambda_v"));
+  KVQ_TRY(check_strides(sign_batch_stride, lambda_batch_stride, fn));
+  const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt(float(L->head_dim));
+  const kvq_impl::DecodePlan p =
+      kvq_impl::plan_decode(L->batch, L->kv_heads, L->q_heads, L->head_dim, seq_len, seq_len);
+  kvq_impl::DecodeArgs a{L->batch,   L->kv_heads, L->q_heads, L->head_dim, L->k_bits,   L->v_bits,
+                         L->capacity, seq_len,    seq_lens,   q_f16,       k_codes,     k_scales,
+                         v_codes,    v_scales,    sign_k,     sign_v,      sign_batch_stride, lambda_k,
+                         lambda_v,   lambda_batch_stride,     scale,       workspace,   out};
+  return hip_status(kvq_impl::launch_decode(a, p, static_cast<hipStream_t>(stream)), fn);
+}
+
+kvq_status kvq_decode_attn_fp16(const kvq_layout* L, const void* q_f16, const void* k_f16, const void* v_f16,
+                                int32_t seq_len, const int32_t* seq_lens, float sm_scale, void* workspace,
+                                size_t workspace_bytes, float* out, void* stream) {
+  const char* fn = "kvq_decode_attn_fp16";
+  KVQ_TRY(check_layout(L, fn));
+  KVQ_TRY(check_decode_common(L, q_f16, seq_len, seq_lens, sm_scale, workspace, workspace_bytes, out, fn));
+  KVQ_TRY(check_ptr(k_f16, 16, fn, "k"));
+  KVQ_TRY(check_ptr(v_f16, 16, fn, "v"));
+  const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt(float(L->head_dim));
+  const kvq_impl::DecodePlan p =
+      kvq_impl::plan_decode(L->batch, L->kv_heads, L->q_heads, L->head_dim, seq_len, seq_len);
+  kvq_impl::DecodeF16Args a{L->batch, L->kv_heads, L->q_heads, L->head_dim, L->capacity, seq_len, seq_lens,
+                            q_f16,    k_f16,       v_f16,      scale,       workspace,   out};
+  return hip_status(kvq_impl::launch_decode_f16(a, p, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // extern "C"

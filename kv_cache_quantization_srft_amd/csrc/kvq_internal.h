@@ -1,0 +1,97 @@
+// Internal launch interface between the C ABI (kvq_api.cpp) and the HIP kernels.
+// Arguments arrive here already validated; launchers only compute grids and launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvq_impl {
+
+struct QuantArgs {
+  int batch, kv_heads, head_dim, bits, capacity;
+  int pos, n_tok;
+  const void* x;  // fp16 [batch, kv_heads, n_tok, d]
+  const float* sign;
+  int64_t sign_bs;
+  const float* lambda;  // nullable
+  int64_t lambda_bs;
+  void* codes;
+  void* scales;
+};
+
+struct DequantArgs {
+  int batch, kv_heads, head_dim, bits, capacity;
+  int pos, n_tok;
+  const void* codes;
+  const void* scales;
+  const float* sign;
+  int64_t sign_bs;
+  const float* lambda;
+  int64_t lambda_bs;
+  float* out;
+};
+
+struct CalibArgs {
+  int batch, kv_heads, head_dim;
+  int n_tok, n_cal;
+  const void* x;
+  const float* sign;
+  int64_t sign_bs;
+  float* lambda;
+};
+
+// Split of a decode call into work-groups (shared by the quantized and the fp16 kernels).
+struct DecodePlan {
+  int heads_per_tile;  // query heads handled by one work-group
+  int head_tiles;      // G / heads_per_tile
+  int chunk;           // tokens per work-group
+  int n_chunks;        // ceil(seq_len / chunk)
+  int max_chunks;      // chunk count the workspace is sized for
+};
+
+struct DecodeArgs {
+  int batch, kv_heads, q_heads, head_dim, k_bits, v_bits, capacity;
+  int seq_len;
+  const int32_t* seq_lens;  // nullable
+  const void* q;
+  const void* k_codes;
+  const void* k_scales;
+  const void* v_codes;
+  const void* v_scales;
+  const float* sign_k;
+  const float* sign_v;
+  int64_t sign_bs;
+  const float* lambda_k;
+  const float* lambda_v;
+  int64_t lambda_bs;
+  float sm_scale;
+  void* workspace;
+  float* out;
+};
+
+struct DecodeF16Args {
+  int batch, kv_heads, q_heads, head_dim, capacity;
+  int seq_len;
+  const int32_t* seq_lens;
+  const void* q;
+  const void* k;
+  const void* v;
+  float sm_scale;
+  void* workspace;
+  float* out;
+};
+
+// Host-side planning (pure host code, no HIP call).
+DecodePlan plan_decode(int batch, int kv_heads, int q_heads, int head_dim, int seq_len,
+                       int max_seq_len);
+size_t decode_workspace_bytes(int batch, int kv_heads, int q_heads, int head_dim,
+                              int max_seq_len);
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
+hipError_t launch_calibrate(const CalibArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream);
+hipError_t launch_decode_f16(const DecodeF16Args& a, const DecodePlan& p, hipStream_t stream);
+
+}  // namespace kvq_impl

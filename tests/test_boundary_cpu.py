@@ -1,0 +1,187 @@
+"""The C-ABI library loads, exports every declared symbol, and validates arguments on the host.
+
+No GPU is needed: every call here fails validation, which happens before any HIP call, so the
+fake device pointers below are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import threading
+
+import pytest
+
+from kv_cache_quantization_srft_amd import kvq
+from oracle import kvq_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+P = ctypes.c_void_p
+GOOD = P(1 << 20)      # aligned fake device pointer (never dereferenced)
+MIS = P((1 << 20) + 4)  # 4-byte aligned, not 16-byte aligned
+NULL = P(0)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kvq.LIB_PATH):
+        pytest.skip("libkvq.so not built")
+    return kvq.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(kvq.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(kvq_\w+)$", out, flags=re.M))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(L, n)
+
+
+def test_version_and_status_strings(L):
+    assert kvq.kvq_version() >= 100
+    for code, name in kvq.STATUS_NAMES.items():
+        assert L.kvq_status_string(code).decode() == name
+
+
+def layout(**kw):
+    base = dict(batch=2, kv_heads=2, q_heads=12, head_dim=128, capacity=64, k_bits=4, v_bits=4)
+    base.update(kw)
+    return kvq.make_layout(**base)
+
+
+def test_footprint_matches_oracle(L):
+    for d, kb, vb in ((128, 4, 4), (256, 8, 4)):
+        lay = layout(head_dim=d, k_bits=kb, v_bits=vb, capacity=4096, batch=3)
+        total = kvq.kvq_codes_bytes(lay, kb) + kvq.kvq_codes_bytes(lay, vb) + 2 * kvq.kvq_scales_bytes(lay)
+        assert total == O.quantized_kv_bytes(1, 2, d, 4096, kb, vb, batch=3)
+    assert kvq.kvq_codes_bytes(layout(head_dim=96), 4) == 0
+    assert kvq.kvq_codes_bytes(layout(), 3) == 0
+
+
+def test_workspace_bytes_monotonic(L):
+    lay = layout()
+    sizes = [kvq.kvq_decode_attn_workspace_bytes(lay, s) for s in (1, 64, 4096, 65536)]
+    assert all(s > 0 for s in sizes)
+    assert sizes == sorted(sizes)
+    assert kvq.kvq_decode_attn_workspace_bytes(layout(q_heads=5), 64) == 0
+
+
+def quantize(L, lay, bits=4, x=GOOD, pos=0, n_tok=4, sign=GOOD, sbs=0, lam=NULL, lbs=0, codes=GOOD, scales=GOOD):
+    return L.kvq_quantize(ctypes.byref(lay), bits, x, pos, n_tok, sign, sbs, lam, lbs, codes, scales, NULL)
+
+
+def msg(L):
+    return L.kvq_last_error_message().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(lay=dict(head_dim=96)), 2, "head_dim"),
+    (dict(lay=dict(head_dim=64)), 2, "head_dim"),
+    (dict(lay=dict(batch=0)), 1, "batch"),
+    (dict(bits=3), 2, "bits"),
+    (dict(pos=62, n_tok=4), 1, "token range"),
+    (dict(pos=-1), 1, "token range"),
+    (dict(n_tok=0), 1, "token range"),
+    (dict(x=NULL), 1, "x is NULL"),
+    (dict(x=MIS), 3, "x is not 16-byte"),
+    (dict(codes=MIS), 3, "codes"),
+    (dict(scales=NULL), 1, "scales"),
+    (dict(sign=P((1 << 20) + 2)), 3, "sign"),
+    (dict(sbs=-1), 1, "stride"),
+])
+def test_quantize_validation(L, kw, status, needle):
+    lay = layout(**kw.pop("lay", {}))
+    st = quantize(L, lay, **kw)
+    assert st == status
+    assert needle in msg(L)
+
+
+def test_group_size_unsupported(L):
+    lay = layout()
+    lay.group_size = 32
+    assert quantize(L, lay) == 2 and "group_size" in msg(L)
+
+
+def test_dequantize_and_calibrate_validation(L):
+    lay = layout()
+    st = L.kvq_dequantize(ctypes.byref(lay), 8, GOOD, GOOD, 0, 65, GOOD, 0, NULL, 0, GOOD, NULL)
+    assert st == 1 and "token range" in msg(L)
+    st = L.kvq_dequantize(ctypes.byref(lay), 4, GOOD, GOOD, 0, 1, GOOD, 0, NULL, 0, MIS, NULL)
+    assert st == 3 and "out" in msg(L)
+    st = L.kvq_calibrate_lambda(ctypes.byref(lay), GOOD, 16, 17, GOOD, 0, GOOD, NULL)
+    assert st == 1 and "n_cal" in msg(L)
+    st = L.kvq_calibrate_lambda(ctypes.byref(lay), GOOD, 16, 0, GOOD, 0, GOOD, NULL)
+    assert st == 1
+
+
+def decode(L, lay, q=GOOD, seq_len=16, seq_lens=NULL, sm=0.0, ws=GOOD, ws_bytes=1 << 30, out=GOOD, kc=GOOD,
+           lam=NULL):
+    return L.kvq_decode_attn(ctypes.byref(lay), q, kc, GOOD, GOOD, GOOD, seq_len, seq_lens, GOOD, GOOD, 0, lam,
+                             lam, 0, ctypes.c_float(sm), ws, ws_bytes, out, NULL)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(lay=dict(q_heads=5)), 1, "multiple of kv_heads"),
+    (dict(lay=dict(q_heads=2 * 65)), 2, "GQA"),
+    (dict(lay=dict(v_bits=8)), 2, "v_bits"),
+    (dict(lay=dict(k_bits=2)), 2, "k_bits"),
+    (dict(seq_len=0), 1, "seq_len"),
+    (dict(seq_len=65), 1, "seq_len"),
+    (dict(q=MIS), 3, "q is not"),
+    (dict(out=NULL), 1, "out"),
+    (dict(ws=P((1 << 20) + 16)), 3, "workspace"),
+    (dict(ws_bytes=16), 4, "workspace has 16 bytes"),
+    (dict(sm=float("nan")), 1, "sm_scale"),
+    (dict(kc=MIS), 3, "k_codes"),
+    (dict(seq_lens=P((1 << 20) + 2)), 3, "seq_lens"),
+])
+def test_decode_validation(L, kw, status, needle):
+    lay = layout(**kw.pop("lay", {}))
+    assert decode(L, lay, **kw) == status
+    assert needle in msg(L)
+
+
+def test_fp16_decode_validation(L):
+    lay = layout()
+    st = L.kvq_decode_attn_fp16(ctypes.byref(lay), GOOD, MIS, GOOD, 16, NULL, ctypes.c_float(0), GOOD, 1 << 30,
+                                GOOD, NULL)
+    assert st == 3 and "k is not" in msg(L)
+    st = L.kvq_decode_attn_fp16(ctypes.byref(lay), GOOD, GOOD, GOOD, 65, NULL, ctypes.c_float(0), GOOD, 1 << 30,
+                                GOOD, NULL)
+    assert st == 1
+
+
+def test_error_message_is_thread_local(L):
+    lay = layout(head_dim=96)
+    assert quantize(L, lay) == 2
+    main_msg = msg(L)
+    seen = {}
+
+    def worker():
+        seen["before"] = L.kvq_last_error_message().decode()
+        quantize(L, layout(), bits=3)
+        seen["after"] = L.kvq_last_error_message().decode()
+
+    t = threading.Thread(target=worker)
+    t.start()
+    t.join()
+    assert seen["before"] == ""
+    assert "bits" in seen["after"]
+    assert msg(L) == main_msg
+
+
+def test_binding_requires_device_tensors(L):
+    torch = pytest.importorskip("torch")
+    lay = layout()
+    x = torch.zeros(2 * 2 * 4 * 128, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        kvq.kvq_quantize(lay, 4, x, 0, 4, x, 0, None, 0, x, x, stream=0)
