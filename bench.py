@@ -7,10 +7,11 @@ into the batch): append-quantize the new token's K and V (write path), then fuse
 dequant + decode attention over the whole cache (read path).  The fp16-KV decode of the same
 build and the bulk (prefill) quantize are timed the same way and reported beside it.
 
-Timing: each measured unit is captured in a HIP graph that runs it over R different copies of
-the cache (R copies span >= 1 GB, four times the MI355X Infinity Cache), so every rep reads
-cold data; graphs are replayed back-to-back between HIP events after W warm-up steps, bracketed
-by device synchronizations.  Inputs are resident in HBM before the timed region starts.
+Timing: the K timed steps of each measured unit are captured in one HIP graph, step i reading
+cache copy i mod R (R copies span >= 1 GB, four times the MI355X Infinity Cache), so every step
+reads cold data and host launch overhead is paid once per graph.  A graph of W warm-up steps runs
+first; the timed replay is bracketed by device synchronizations and HIP events.  Inputs are
+resident in HBM before the timed region starts.
 
 Prints ONE JSON line (rank 0).
 """
@@ -19,7 +20,6 @@ from __future__ import annotations
 import argparse
 import json
 import os
-import statistics
 import sys
 import time
 
@@ -40,7 +40,7 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=0, help="timed steps (default: 4 graph replays)")
+    ap.add_argument("--steps", type=int, default=0, help="timed steps (default: 4 x the cache copies)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -49,30 +49,39 @@ def parse():
 
 
 class Timer:
-    """Replay a list of captured graphs K times between HIP events on the current stream."""
+    """Time exactly `steps` steps: one HIP graph holds them all (each step on the next cache
+    copy), so host launch overhead is paid once per graph, not per step.  A separate graph of
+    `warmup` steps runs first; the timed replay is bracketed by device synchronizations and HIP
+    events on the capturing stream; it is repeated `repeats` times for the spread."""
 
     def __init__(self, torch):
         self.torch = torch
 
-    def run(self, graphs, steps, warmup):
+    def run(self, step_fn, n_copies, steps, warmup, repeats=3):
         torch = self.torch
-        R = len(graphs)
-        for i in range(warmup):
-            graphs[i % R].replay()
-        torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-        t0 = time.perf_counter()
-        ev[0].record()
-        for i in range(steps):
-            graphs[i % R].replay()
-            ev[i + 1].record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-        total = ev[0].elapsed_time(ev[steps])
-        return {"ms_mean": total / steps, "ms_median": statistics.median(per),
-                "ms_p10": float(np.percentile(per, 10)), "ms_p90": float(np.percentile(per, 90)),
-                "wall_ms_per_step": 1e3 * wall / steps}
+        if warmup > 0:
+            gw = capture(torch, lambda: [step_fn(i % n_copies) for i in range(warmup)])
+            gw.replay()
+            torch.cuda.synchronize()
+            del gw
+        g = capture(torch, lambda: [step_fn(i % n_copies) for i in range(steps)])
+        times = []
+        for _ in range(repeats):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            times.append((e0.elapsed_time(e1), wall))
+        del g
+        first = times[0]
+        per = [t / steps for t, _ in times]
+        return {"ms_mean": first[0] / steps, "wall_ms_per_step": 1e3 * first[1] / steps,
+                "ms_repeats": per, "ms_min": min(per), "ms_max": max(per)}
 
 
 def capture(torch, fn):
@@ -80,7 +89,7 @@ def capture(torch, fn):
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        fn()  # warm (allocations, first-launch work) outside the capture
+        fn()  # warm (first-launch work) outside the capture
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
@@ -200,23 +209,17 @@ def main():
         kvq.kvq_quantize(lay, w.v_bits, v_new, S - 1, 1, s, 0, lam_v, lbs, p[2], p[3])
         decode(p)
 
-    def graph_over(copies, fn):
-        return [capture(torch, lambda c=c: fn(c)) for c in copies]
-
     timer = Timer(torch)
     R = len(planes)
     steps = args.steps if args.steps > 0 else 4 * R
-    g_step = graph_over(planes, step)
-    res_step = timer.run(g_step, steps, args.warmup)
-    g_dec = graph_over(planes, decode)
-    res_dec = timer.run(g_dec, steps, args.warmup)
-    g_f16 = graph_over(kv16, lambda kv: kvq.kvq_decode_attn_fp16(lay, q, kv[0], kv[1], S, None, 0.0, ws, out16))
-    res_f16 = timer.run(g_f16, max(steps, 4 * len(kv16)), args.warmup)
+    res_step = timer.run(lambda i: step(planes[i]), R, steps, args.warmup)
+    res_dec = timer.run(lambda i: decode(planes[i]), R, steps, args.warmup)
+    Rf = len(kv16)
+    res_f16 = timer.run(lambda i: kvq.kvq_decode_attn_fp16(lay, q, kv16[i][0], kv16[i][1], S, None, 0.0, ws, out16),
+                        Rf, max(steps, 4 * Rf), args.warmup)
     # bulk quantize: all layers, K and V, from rotating fp16 copies into rotating planes
-    g_bq = [capture(torch, lambda i=i: quantize_all(planes[i % R], *kv16[i % len(kv16)]))
-            for i in range(max(R, len(kv16)))]
-    res_bq = timer.run(g_bq, 2 * len(g_bq), args.warmup)
-    del g_step, g_dec, g_f16, g_bq
+    nb = max(R, Rf)
+    res_bq = timer.run(lambda i: quantize_all(planes[i % R], *kv16[i % Rf]), nb, 2 * nb, args.warmup)
 
     dec_bytes = q_bytes  # every code and scale byte of the cache is read once per decode step
     n_vec = 2 * LB * H * S

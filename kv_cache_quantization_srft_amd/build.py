@@ -21,12 +21,12 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libkvq.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["kvq_quant.hip", "kvq_decode.hip", "kvq_api.cpp"]
+SOURCES = ["kvq_quant.hip", "kvq_decode_q.hip", "kvq_decode_f16.hip", "kvq_plan.cpp", "kvq_api.cpp"]
 ARCH = "gfx950"
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
+    "-fconstexpr-steps=100000000", "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
 ]
 
 

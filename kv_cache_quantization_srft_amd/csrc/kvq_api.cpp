@@ -222,7 +222,7 @@ kvq_status kvq_decode_attn(const kvq_layout* L, const void* q_f16, const void* k
   KVQ_TRY(check_strides(sign_batch_stride, lambda_batch_stride, fn));
   const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt(float(L->head_dim));
   const kvq_impl::DecodePlan p =
-      kvq_impl::plan_decode(L->batch, L->kv_heads, L->q_heads, L->head_dim, seq_len, seq_len);
+      kvq_impl::plan_decode(L->batch, L->kv_heads, L->q_heads, L->head_dim, seq_len, seq_len, false);
   kvq_impl::DecodeArgs a{L->batch,   L->kv_heads, L->q_heads, L->head_dim, L->k_bits,   L->v_bits,
                          L->capacity, seq_len,    seq_lens,   q_f16,       k_codes,     k_scales,
                          v_codes,    v_scales,    sign_k,     sign_v,      sign_batch_stride, lambda_k,
@@ -240,7 +240,7 @@ kvq_status kvq_decode_attn_fp16(const kvq_layout* L, const void* q_f16, const vo
   KVQ_TRY(check_ptr(v_f16, 16, fn, "v"));
   const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt(float(L->head_dim));
   const kvq_impl::DecodePlan p =
-      kvq_impl::plan_decode(L->batch, L->kv_heads, L->q_heads, L->head_dim, seq_len, seq_len);
+      kvq_impl::plan_decode(L->batch, L->kv_heads, L->q_heads, L->head_dim, seq_len, seq_len, true);
   kvq_impl::DecodeF16Args a{L->batch, L->kv_heads, L->q_heads, L->head_dim, L->capacity, seq_len, seq_lens,
                             q_f16,    k_f16,       v_f16,      scale,       workspace,   out};
   return hip_status(kvq_impl::launch_decode_f16(a, p, static_cast<hipStream_t>(stream)), fn);

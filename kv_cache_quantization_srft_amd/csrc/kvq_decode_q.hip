@@ -1,0 +1,573 @@
+// Fused dequant + single-token decode attention over the SRFT-rotated quantized cache (gfx950).
+//
+// The rotation is orthogonal ("When Quantization Is Free", technical summary, Methodology 1),
+// so attention runs in the rotated domain without reconstructing K or V:
+//   score_t = (SRFT_sK(q) * lambda_K * sm_scale * log2 e) . (code_K,t * scale_K,t)      [log2 units]
+//   out     = s_V * SRFT^-1( lambda_V * sum_t p_t code_V,t * scale_V,t / sum_t p_t )
+//
+// Three launches per call:
+//   qprep_kernel : one work-group per (sequence, kv head, head tile).  Rotates the query heads
+//                  (O(d^2) with an LDS twiddle table), splits every rotated channel into a
+//                  16-bit integer (two int8 digits, per-head step sigma) laid out exactly as the
+//                  A operand of the score MFMA.
+//   decode_kernel: one work-group of 4 waves per (unit, chunk of tokens).  Each wave walks
+//                  64-token superblocks:
+//     scores : v_mfma_i32_16x16x64_i8.  A rows are (head, group) pairs holding the query digits
+//              of one group of 16 channels (block diagonal); B is the packed K codes widened to
+//              bytes (x16 for int4: one shift and one mask per 8 codes, no unpacking).  The exact
+//              integer group dots are scaled by the fp16 group scales in fp32.
+//     softmax: online, per head, over 16-lane DPP rows.
+//     values : v_mfma_f32_16x16x32_f16 per group of 16 channels.  The V codes of the superblock
+//              are staged in LDS and read with ds_read_b64_tr_b4 so that every lane holds 16
+//              tokens of one channel; B = code * scale split exactly into fp16 hi + lo,
+//              A = p split into fp16 hi + lo (three products per tile, fp32 accumulation).
+//   The work-group merges its waves and writes a chunk partial.
+//   merge_kernel : one work-group per (unit, head) merges the chunks, applies lambda_V and the
+//                  inverse rotation, and writes the output.  (Merging inside the main kernel
+//                  would need device-scope release/acquire fences per work-group, which on this
+//                  chip write back and invalidate the whole L2 of the XCD.)
+#include <algorithm>
+
+#include "kvq_decode_common.h"
+
+namespace kvq_impl {
+namespace {
+
+using namespace dec;
+
+constexpr int kSB = 64;  // tokens per wave superblock
+
+// ------------------------------------------------------------------------------------------
+// Prologue: query digits.
+// ------------------------------------------------------------------------------------------
+// Channel held by byte b (0..15) of the widened K codes of one group.
+template <int KB>
+__host__ __device__ constexpr int kbyte_channel(int b) {
+  // int4: dwords hold 16x[c0 c2 c4 c6], 16x[c1 c3 c5 c7], 16x[c8 c10 c12 c14], 16x[c9 ...]
+  return KB == 8 ? b : ((b >> 2) & 2 ? 8 : 0) + 2 * (b & 3) + ((b >> 2) & 1);
+}
+
+template <int D, int KB>
+__global__ __launch_bounds__(kThreads) void qprep_kernel(const uint16_t* __restrict__ q, int q_heads, int kv_heads,
+                                                         int head_tile, int head_tiles,
+                                                         const float* __restrict__ sign, int64_t sign_bs,
+                                                         const float* __restrict__ lambda, int64_t lambda_bs,
+                                                         float scale, uint4* __restrict__ qdig,
+                                                         float* __restrict__ qsig) {
+  constexpr int NS = D / 64;
+  constexpr int NB = D / 16, NSTEP = D / 32;
+  __shared__ float qh[16][D];  // rotated, scaled query
+  __shared__ __align__(16) uint32_t smask[D / 2];
+  __shared__ float sig[16];
+  const int unit = blockIdx.x;
+  const int ht = unit % head_tiles;
+  const int bk = unit / head_tiles;
+  const int kvh = bk % kv_heads;
+  const int b = bk / kv_heads;
+  const int G = q_heads / kv_heads;
+  const int h0 = kvh * G + ht * head_tile;
+  const int GT = head_tile;
+  const int nrb = (GT + 3) / 4;
+  for (int i = threadIdx.x; i < D / 2; i += kThreads) {
+    const float* s = sign + b * sign_bs;
+    smask[i] = (s[2 * i] < 0.0f ? 0x8000u : 0u) | (s[2 * i + 1] < 0.0f ? 0x80000000u : 0u);
+  }
+  __syncthreads();
+  // q_hat[h][c] = sum_n Q[c][n] s_n q[h][n] * lambda_c * scale as MFMAs: A = the fp16 query
+  // (exact, signs flipped in the fp16 bits), B = the forward table (16 Q as fp16 hi + lo).
+  {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int n16 = lane & 15, r4 = lane >> 4;
+    v8h aq[NSTEP];
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (n16 < GT) {
+        v = *reinterpret_cast<const uint4*>(q + (int64_t(b) * q_heads + h0 + n16) * D + 32 * s + 8 * r4);
+        const uint4 m = *reinterpret_cast<const uint4*>(smask + (32 * s + 8 * r4) / 2);
+        v.x ^= m.x;
+        v.y ^= m.y;
+        v.z ^= m.z;
+        v.w ^= m.w;
+      }
+      aq[s] = as_v8h(v.x, v.y, v.z, v.w);
+    }
+    const MfmaQTable<D>& T = mqtable<D>();
+    for (int cb = w; cb < NB; cb += kWaves) {
+      uint4 bh[NSTEP], bl[NSTEP];
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s) {
+        bh[s] = ld4(T.fwd_hi[cb][s][lane]);
+        bl[s] = ld4(T.fwd_lo[cb][s][lane]);
+      }
+      v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], as_v8h(bh[s].x, bh[s].y, bh[s].z, bh[s].w), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], as_v8h(bl[s].x, bl[s].y, bl[s].z, bl[s].w), acc, 0, 0, 0);
+      }
+      const int c = 16 * cb + n16;
+      const float lam = (lambda ? lambda[b * lambda_bs + int64_t(kvh) * D + c] : 1.0f) * scale * 0.0625f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = 4 * r4 + i;
+        if (h < GT) qh[h][c] = acc[i] * lam;
+      }
+    }
+  }
+  __syncthreads();
+  // per-head step: the largest |q_hat| maps to 32639 so both digits fit int8 (wave h%4 reduces)
+  {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    for (int h = wv; h < 16; h += kWaves) {
+      float mx = 0.0f;
+      if (h < GT)
+        for (int c = lane; c < D; c += 64) mx = fmaxf(mx, fabsf(qh[h][c]));
+      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      if (lane == 0) {
+        sig[h] = mx > 0.0f ? mx / 32639.0f : 1.0f;
+        // score multiplier: step, times 1/16 for int4 codes widened as 16*code
+        qsig[int64_t(unit) * 16 + h] = (h < GT ? sig[h] : 0.0f) * (KB == 4 ? 0.0625f : 1.0f);
+      }
+    }
+  }
+  __syncthreads();
+  // A operand of the score MFMA for (row block rb, step s, digit dg): lane l holds row
+  // r = l%16 = (head 4rb + r/4, slot j = r%4) and k bytes of lane group l/16; it is non-zero
+  // only when l/16 == j, where the 16 bytes are the digits of group g = j*NS + s.
+  const int total = nrb * NS * 2 * 64;
+  for (int i = threadIdx.x; i < total; i += kThreads) {
+    const int lane = i & 63;
+    const int blk = i >> 6;  // (rb * NS + s) * 2 + dg
+    const int dg = blk & 1;
+    const int s = (blk >> 1) % NS;
+    const int rb = (blk >> 1) / NS;
+    const int r = lane & 15, kg = lane >> 4;
+    const int h = 4 * rb + (r >> 2), j = r & 3;
+    uint32_t wv[4] = {0u, 0u, 0u, 0u};
+    if (kg == j && h < GT) {
+      const int g = j * NS + s;
+      const float inv = 1.0f / sig[h];
+#pragma unroll
+      for (int bt = 0; bt < 16; ++bt) {
+        const int c = 16 * g + kbyte_channel<KB>(bt);
+        int Q = static_cast<int>(rintf(qh[h][c] * inv));
+        Q = min(max(Q, -32639), 32639);
+        const int hi = (Q + 128) >> 8;
+        const int lo = Q - 256 * hi;
+        const int v = dg == 0 ? hi : lo;
+        wv[bt >> 2] |= (uint32_t(v) & 0xffu) << (8 * (bt & 3));
+      }
+    }
+    qdig[(int64_t(unit) * (total >> 6) + blk) * 64 + lane] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Main kernel.
+// ------------------------------------------------------------------------------------------
+template <int D, int KB>
+struct QGeom {
+  static constexpr int NS = D / 64;             // score MFMA steps (64 channels each)
+  static constexpr int NG = D / 16;             // groups of 16 channels
+  static constexpr int KRB = D * KB / 8;        // K code bytes per token
+  static constexpr int VRB = D / 2;             // V code bytes per token (int4)
+  static constexpr int KLB = KRB / 4;           // K code bytes per lane per 16-token block
+  static constexpr int KLW = KLB / 4;           // ... in dwords
+  static constexpr int VLU = kSB * VRB / 64 / 16;  // 16-byte V units per lane per superblock
+  static constexpr int SLW = NG * 2 / 4;        // scale dwords per token
+  // LDS (bytes) per wave: V codes, V scales (transposed, k order), K scales, P, alpha
+  static constexpr int LDS_V = kSB * VRB;
+  static constexpr int LDS_S = NG * kSB * 2;
+  static constexpr int LDS_K = kSB * NG * 2;
+  static constexpr int LDS_P = 16 * kSB * 4;
+  static constexpr int LDS_WAVE = LDS_V + LDS_S + LDS_K + LDS_P + 16 * 4;
+  static constexpr int LDS_EPI = (kWaves * 16 * 2 + kWaves * (D == 128 ? 16 : 8) * D) * 4;
+  static constexpr int LDS = (kWaves * LDS_WAVE > LDS_EPI ? kWaves * LDS_WAVE : LDS_EPI);
+};
+
+// Widen the int4 codes of one group (2 dwords, 16 codes) to the 16 int8 bytes 16*code.
+__device__ __forceinline__ v4i widen_int4(uint32_t w0, uint32_t w1) {
+  return v4i{int((w0 << 4) & 0xf0f0f0f0u), int(w0 & 0xf0f0f0f0u), int((w1 << 4) & 0xf0f0f0f0u),
+             int(w1 & 0xf0f0f0f0u)};
+}
+
+// 8 nibbles (tokens r = 0..7 of one channel) -> 4 fp16 pairs of code values,
+// pairs hold tokens (0,4), (1,5), (2,6), (3,7).
+__device__ __forceinline__ void nibbles_to_half_pairs(uint32_t x, uint32_t (&p)[4]) {
+  x ^= 0x88888888u;  // offset binary: nibble = code + 8
+  const v2h off = {static_cast<_Float16>(-1032.0f), static_cast<_Float16>(-1032.0f)};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t t = ((x >> (4 * i)) & 0x000f000fu) | 0x64006400u;  // halves 1024 + code + 8
+    const v2h c = __builtin_bit_cast(v2h, t) + off;
+    p[i] = __builtin_bit_cast(uint32_t, c);
+  }
+}
+
+// Global data of one 64-token superblock held in registers (prefetched one superblock ahead).
+template <int D, int KB>
+struct SBRegs {
+  using Gm = QGeom<D, KB>;
+  uint32_t kw[4][Gm::KLW];  // K codes: 16-token block sb, token n16, lane group r4's bytes
+  uint32_t ksw[Gm::SLW];    // K scales of token base + lane
+  uint4 vw[Gm::VLU];        // V codes, coalesced 16-byte units
+  uint32_t vsw[Gm::SLW];    // V scales of token base + lane
+};
+
+template <int D, int KB>
+__device__ __forceinline__ void load_superblock(SBRegs<D, KB>& r, const uint8_t* __restrict__ kc,
+                                                const uint16_t* __restrict__ ks, const uint8_t* __restrict__ vc,
+                                                const uint16_t* __restrict__ vs, int64_t rowbase, int base,
+                                                int last_tok, int lane) {
+  using Gm = QGeom<D, KB>;
+  const int n16 = lane & 15, r4 = lane >> 4;
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) {
+    const int t = min(base + 16 * sb + n16, last_tok);
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(kc + (rowbase + t) * Gm::KRB + r4 * Gm::KLB);
+#pragma unroll
+    for (int i = 0; i < Gm::KLW; i += 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(src + i);
+      r.kw[sb][i] = v.x;
+      r.kw[sb][i + 1] = v.y;
+      r.kw[sb][i + 2] = v.z;
+      r.kw[sb][i + 3] = v.w;
+    }
+  }
+  const int tl = min(base + lane, last_tok);
+  {
+    const uint32_t* s = reinterpret_cast<const uint32_t*>(ks + (rowbase + tl) * Gm::NG);
+#pragma unroll
+    for (int i = 0; i < Gm::SLW; i += 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(s + i);
+      r.ksw[i] = v.x;
+      r.ksw[i + 1] = v.y;
+      r.ksw[i + 2] = v.z;
+      r.ksw[i + 3] = v.w;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < Gm::VLU; ++i) {
+    const int f = i * 64 + lane;  // 16-byte unit index in the superblock
+    const int tk = f / (Gm::VRB / 16);
+    const int piece = f - tk * (Gm::VRB / 16);
+    const int t = min(base + tk, last_tok);
+    r.vw[i] = *reinterpret_cast<const uint4*>(vc + (rowbase + t) * Gm::VRB + piece * 16);
+  }
+  {
+    const uint32_t* s = reinterpret_cast<const uint32_t*>(vs + (rowbase + tl) * Gm::NG);
+#pragma unroll
+    for (int i = 0; i < Gm::SLW; i += 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(s + i);
+      r.vsw[i] = v.x;
+      r.vsw[i + 1] = v.y;
+      r.vsw[i + 2] = v.z;
+      r.vsw[i + 3] = v.w;
+    }
+  }
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Everything one wave does with one superblock already in registers.
+template <int D, int KB, int NRB>
+__device__ __forceinline__ void process_superblock(const SBRegs<D, KB>& r, int base, int t_end, int lane,
+                                                   const v4i (&aop)[NRB][D / 64][2], const float (&sig)[NRB],
+                                                   float (&m_run)[NRB], float (&l_run)[NRB], v4f (&acc)[D / 16],
+                                                   uint8_t* vtile, uint16_t* stile, uint16_t* ktile, float* ptile,
+                                                   float* atile) {
+  using Gm = QGeom<D, KB>;
+  constexpr int NS = Gm::NS, NG = Gm::NG;
+  const int n16 = lane & 15, r4 = lane >> 4;
+
+  // ---------------- stage V codes, V scales (k order, / 16) and K scales in LDS ----------------
+#pragma unroll
+  for (int i = 0; i < Gm::VLU; ++i) *reinterpret_cast<uint4*>(vtile + (i * 64 + lane) * 16) = r.vw[i];
+  {
+    const bool valid = base + lane < t_end;
+    const int pos = 16 * (lane >> 4) + kpos16(lane & 15);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const uint32_t bits = (r.vsw[g >> 1] >> (16 * (g & 1))) & 0xffffu;
+      // scale / 16 keeps code * scale inside the fp16 range; undone by the merge
+      const float sv = valid ? static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(bits))) * 0.0625f : 0.0f;
+      stile[g * kSB + pos] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(sv));
+    }
+    uint32_t* kt = reinterpret_cast<uint32_t*>(ktile + lane * NG);
+#pragma unroll
+    for (int i = 0; i < Gm::SLW; i += 4)
+      *reinterpret_cast<uint4*>(kt + i) = make_uint4(r.ksw[i], r.ksw[i + 1], r.ksw[i + 2], r.ksw[i + 3]);
+  }
+  wave_sync_lds();
+
+  // ---------------- scores (int8 MFMA, exact integer group dots) ----------------
+  float sc[4][NRB];
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) {
+    v4i bop[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if constexpr (KB == 4)
+        bop[s] = widen_int4(r.kw[sb][2 * s], r.kw[sb][2 * s + 1]);
+      else
+        bop[s] = v4i{int(r.kw[sb][4 * s]), int(r.kw[sb][4 * s + 1]), int(r.kw[sb][4 * s + 2]),
+                     int(r.kw[sb][4 * s + 3])};
+    }
+    uint32_t kraw[Gm::SLW];
+    {
+      const uint32_t* kt = reinterpret_cast<const uint32_t*>(ktile + (16 * sb + n16) * NG);
+#pragma unroll
+      for (int i = 0; i < Gm::SLW; i += 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(kt + i);
+        kraw[i] = v.x;
+        kraw[i + 1] = v.y;
+        kraw[i + 2] = v.z;
+        kraw[i + 3] = v.w;
+      }
+    }
+    float ksf[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      ksf[g] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t((kraw[g >> 1] >> (16 * (g & 1))) & 0xffffu)));
+    const bool valid = base + 16 * sb + n16 < t_end;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      float s_acc = 0.0f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const v4i zero = {0, 0, 0, 0};
+        const v4i chi = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[rb][s][0], bop[s], zero, 0, 0, 0);
+        const v4i clo = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[rb][s][1], bop[s], zero, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int dot = chi[i] * 256 + clo[i];
+          s_acc = fmaf(static_cast<float>(dot), ksf[i * NS + s], s_acc);
+        }
+      }
+      sc[sb][rb] = valid ? s_acc * sig[rb] : -INFINITY;
+    }
+  }
+
+  // ---------------- online softmax per head (16-lane rows) ----------------
+  bool rescale = false;
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    float mb = fmaxf(fmaxf(sc[0][rb], sc[1][rb]), fmaxf(sc[2][rb], sc[3][rb]));
+    mb = row_max16(mb);
+    const float mn = fmaxf(m_run[rb], mb);
+    const float alpha = exp2_guard(m_run[rb], mn);
+    rescale |= mn != m_run[rb];
+    m_run[rb] = mn;
+    float psum = 0.0f;
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      const float p = exp2_guard(sc[sb][rb], mn);
+      psum += p;
+      ptile[(4 * rb + r4) * kSB + 16 * sb + kpos16(n16)] = p;
+    }
+    l_run[rb] = l_run[rb] * alpha + psum;
+    if (n16 == 0) atile[4 * rb + r4] = alpha;
+  }
+  wave_sync_lds();
+  if (__builtin_amdgcn_ballot_w64(rescale) != 0ull) {
+    const float4 al = *reinterpret_cast<const float4*>(atile + 4 * r4);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      acc[g][0] *= al.x;
+      acc[g][1] *= al.y;
+      acc[g][2] *= al.z;
+      acc[g][3] *= al.w;
+    }
+  }
+
+  // ---------------- A operands: p of head n16 for tokens 16*r4 + (0..15), hi + lo ----------------
+  uint32_t ahi[2][4], alo[2][4];
+  {
+    const float* pr = ptile + n16 * kSB + 16 * r4;
+#pragma unroll
+    for (int hblk = 0; hblk < 2; ++hblk) {
+      const float4 p0 = *reinterpret_cast<const float4*>(pr + 8 * hblk);
+      const float4 p1 = *reinterpret_cast<const float4*>(pr + 8 * hblk + 4);
+      split_pair(p0.x, p0.y, ahi[hblk][0], alo[hblk][0]);
+      split_pair(p0.z, p0.w, ahi[hblk][1], alo[hblk][1]);
+      split_pair(p1.x, p1.y, ahi[hblk][2], alo[hblk][2]);
+      split_pair(p1.z, p1.w, ahi[hblk][3], alo[hblk][3]);
+    }
+  }
+  const v8h a_hi[2] = {as_v8h(ahi[0][0], ahi[0][1], ahi[0][2], ahi[0][3]),
+                       as_v8h(ahi[1][0], ahi[1][1], ahi[1][2], ahi[1][3])};
+  const v8h a_lo[2] = {as_v8h(alo[0][0], alo[0][1], alo[0][2], alo[0][3]),
+                       as_v8h(alo[1][0], alo[1][1], alo[1][2], alo[1][3])};
+
+  // ---------------- values (fp16 MFMA over LDS-transposed codes) ----------------
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    // lane r of each 16-lane group points at token 16*r4 + r, group g
+    lds_v2i_t* src = (lds_v2i_t*)(vtile + (16 * r4 + n16) * Gm::VRB + 8 * g);
+    const v2i_t tr = __builtin_amdgcn_ds_read_tr4_b64_v2i32(src);
+    const uint4 s0 = *reinterpret_cast<const uint4*>(stile + g * kSB + 16 * r4);
+    const uint4 s1 = *reinterpret_cast<const uint4*>(stile + g * kSB + 16 * r4 + 8);
+    const uint32_t sp[2][4] = {{s0.x, s0.y, s0.z, s0.w}, {s1.x, s1.y, s1.z, s1.w}};
+#pragma unroll
+    for (int hblk = 0; hblk < 2; ++hblk) {
+      uint32_t cp[4];
+      nibbles_to_half_pairs(uint32_t(hblk == 0 ? tr.x : tr.y), cp);
+      uint32_t bh[4], bl[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const v2h c = __builtin_bit_cast(v2h, cp[i]);
+        const v2h sc2 = __builtin_bit_cast(v2h, sp[hblk][i]);
+        const v2h hi = c * sc2;
+        const v2h lo = __builtin_elementwise_fma(c, sc2, -hi);
+        bh[i] = __builtin_bit_cast(uint32_t, hi);
+        bl[i] = __builtin_bit_cast(uint32_t, lo);
+      }
+      const v8h b_hi = as_v8h(bh[0], bh[1], bh[2], bh[3]);
+      const v8h b_lo = as_v8h(bl[0], bl[1], bl[2], bl[3]);
+      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[hblk], b_hi, acc[g], 0, 0, 0);
+      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[hblk], b_lo, acc[g], 0, 0, 0);
+      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo[hblk], b_hi, acc[g], 0, 0, 0);
+    }
+  }
+  // the next superblock overwrites this wave's tiles
+  wave_sync_lds();
+}
+
+template <int D, int KB, int NRB>
+__global__ __launch_bounds__(kThreads) void decode_kernel(
+    const uint8_t* __restrict__ kc, const uint16_t* __restrict__ ks, const uint8_t* __restrict__ vc,
+    const uint16_t* __restrict__ vs, const int32_t* __restrict__ seq_lens, int seq_len, int kv_heads, int q_heads,
+    int capacity, int head_tile, int head_tiles, int chunk, int n_chunks, int max_chunks,
+    const uint4* __restrict__ qdig, const float* __restrict__ qsig, float* __restrict__ pml,
+    float* __restrict__ pacc) {
+  using Gm = QGeom<D, KB>;
+  constexpr int NS = Gm::NS, NG = Gm::NG;
+  __shared__ __align__(16) uint8_t smem[Gm::LDS];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r4 = lane >> 4;
+  const int ch = blockIdx.x % n_chunks;
+  const int64_t unit = blockIdx.x / n_chunks;
+  const int ht = int(unit % head_tiles);
+  const int bk = int(unit / head_tiles);
+  const int kvh = bk % kv_heads;
+  const int b = bk / kv_heads;
+  (void)ht;
+  int L = seq_len;
+  if (seq_lens) L = min(max(seq_lens[b], 0), seq_len);
+  const int t_begin = ch * chunk;
+  const int t_end = min(L, t_begin + chunk);
+  const int64_t rowbase = (int64_t(b) * kv_heads + kvh) * capacity;
+  const int last_tok = max(L - 1, 0);
+  constexpr int kStride = kWaves * kSB;
+
+  // first superblock's loads go out before anything else
+  SBRegs<D, KB> ra;
+  int base = t_begin + w * kSB;
+  if (base < t_end) load_superblock<D, KB>(ra, kc, ks, vc, vs, rowbase, base, last_tok, lane);
+
+  uint8_t* wbase = smem + w * Gm::LDS_WAVE;
+  uint8_t* vtile = wbase;
+  uint16_t* stile = reinterpret_cast<uint16_t*>(wbase + Gm::LDS_V);
+  uint16_t* ktile = reinterpret_cast<uint16_t*>(wbase + Gm::LDS_V + Gm::LDS_S);
+  float* ptile = reinterpret_cast<float*>(wbase + Gm::LDS_V + Gm::LDS_S + Gm::LDS_K);
+  float* atile = reinterpret_cast<float*>(wbase + Gm::LDS_V + Gm::LDS_S + Gm::LDS_K + Gm::LDS_P);
+
+  // query digits (A operands) and per-head multipliers
+  v4i aop[NRB][NS][2];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int dg = 0; dg < 2; ++dg) {
+        const uint4 v = qdig[(unit * (NRB * NS * 2) + (rb * NS + s) * 2 + dg) * 64 + lane];
+        aop[rb][s][dg] = v4i{int(v.x), int(v.y), int(v.z), int(v.w)};
+      }
+  float sig[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) sig[rb] = qsig[unit * 16 + 4 * rb + r4];
+
+  // P rows never produced by a score row block and alpha of such heads stay neutral
+  for (int i = lane; i < 16 * kSB; i += 64) ptile[i] = 0.0f;
+  if (lane < 16) atile[lane] = 1.0f;
+
+  float m_run[NRB], l_run[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.0f;
+  }
+  v4f acc[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) acc[g] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  while (base < t_end) {
+    process_superblock<D, KB, NRB>(ra, base, t_end, lane, aop, sig, m_run, l_run, acc, vtile, stile, ktile, ptile,
+                                   atile);
+    base += kStride;
+    if (base < t_end) load_superblock<D, KB>(ra, kc, ks, vc, vs, rowbase, base, last_tok, lane);
+  }
+
+  PartialArgs e;
+  e.head_tile = head_tile;
+  e.max_chunks = max_chunks;
+  e.chunk_index = ch;
+  e.unit = unit;
+  e.pml = pml;
+  e.pacc = pacc;
+  store_partial<D, NRB>(m_run, l_run, acc, [](int k, int rr) { return 4 * k + rr; }, e,
+                        reinterpret_cast<float*>(smem));
+}
+
+template <int D, int KB>
+hipError_t launch_q(const DecodeArgs& a, const DecodePlan& p, const WsLayout& w, hipStream_t s) {
+  char* ws = static_cast<char*>(a.workspace);
+  auto* qdig = reinterpret_cast<uint4*>(ws + w.qdig);
+  auto* qsig = reinterpret_cast<float*>(ws + w.qsig);
+  auto* pml = reinterpret_cast<float*>(ws + w.pml);
+  auto* pacc = reinterpret_cast<float*>(ws + w.pacc);
+  const int units = a.batch * a.kv_heads * p.head_tiles;
+  hipLaunchKernelGGL((qprep_kernel<D, KB>), dim3(units), dim3(kThreads), 0, s, static_cast<const uint16_t*>(a.q),
+                     a.q_heads, a.kv_heads, p.head_tile, p.head_tiles, a.sign_k, a.sign_bs, a.lambda_k, a.lambda_bs,
+                     a.sm_scale * kLog2e, qdig, qsig);
+  const dim3 grid(units * p.n_chunks), block(kThreads);
+  auto* kc = static_cast<const uint8_t*>(a.k_codes);
+  auto* ks = static_cast<const uint16_t*>(a.k_scales);
+  auto* vc = static_cast<const uint8_t*>(a.v_codes);
+  auto* vs = static_cast<const uint16_t*>(a.v_scales);
+#define KVQ_Q_CASE(NRBV)                                                                                         \
+  case NRBV:                                                                                                     \
+    hipLaunchKernelGGL((decode_kernel<D, KB, NRBV>), grid, block, 0, s, kc, ks, vc, vs, a.seq_lens, a.seq_len,   \
+                       a.kv_heads, a.q_heads, a.capacity, p.head_tile, p.head_tiles, p.chunk, p.n_chunks,        \
+                       p.max_chunks, qdig, qsig, pml, pacc);                                                     \
+    break;
+  switch ((p.head_tile + 3) / 4) {
+    KVQ_Q_CASE(1)
+    KVQ_Q_CASE(2)
+    KVQ_Q_CASE(3)
+    KVQ_Q_CASE(4)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef KVQ_Q_CASE
+  // code * scale was staged as code * scale / 16 in fp16: acc_scale 16 undoes it
+  hipLaunchKernelGGL((merge_kernel<D, true>), dim3(units), dim3(kThreads), 0, s, pml, pacc, p.n_chunks,
+                     p.max_chunks, p.head_tile, p.head_tiles, a.q_heads, a.kv_heads, 16.0f, a.sign_v, a.sign_bs,
+                     a.lambda_v, a.lambda_bs, a.out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
+  const WsLayout w = ws_layout(a.batch * a.kv_heads * p.head_tiles, p.head_tile, a.head_dim, p.max_chunks);
+  if (a.head_dim == 128) return a.k_bits == 4 ? launch_q<128, 4>(a, p, w, s) : launch_q<128, 8>(a, p, w, s);
+  return a.k_bits == 4 ? launch_q<256, 4>(a, p, w, s) : launch_q<256, 8>(a, p, w, s);
+}
+
+}  // namespace kvq_impl

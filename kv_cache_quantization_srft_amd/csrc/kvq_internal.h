@@ -43,11 +43,11 @@ struct CalibArgs {
 
 // Split of a decode call into work-groups (shared by the quantized and the fp16 kernels).
 struct DecodePlan {
-  int heads_per_tile;  // query heads handled by one work-group
-  int head_tiles;      // G / heads_per_tile
-  int chunk;           // tokens per work-group
-  int n_chunks;        // ceil(seq_len / chunk)
-  int max_chunks;      // chunk count the workspace is sized for
+  int head_tile;   // query heads handled by one work-group (a divisor of G, <= 16)
+  int head_tiles;  // G / head_tile
+  int chunk;       // tokens per work-group
+  int n_chunks;    // ceil(seq_len / chunk)
+  int max_chunks;  // chunk count the workspace layout is laid out for
 };
 
 struct DecodeArgs {
@@ -83,10 +83,8 @@ struct DecodeF16Args {
 };
 
 // Host-side planning (pure host code, no HIP call).
-DecodePlan plan_decode(int batch, int kv_heads, int q_heads, int head_dim, int seq_len,
-                       int max_seq_len);
-size_t decode_workspace_bytes(int batch, int kv_heads, int q_heads, int head_dim,
-                              int max_seq_len);
+DecodePlan plan_decode(int batch, int kv_heads, int q_heads, int head_dim, int seq_len, int max_seq_len, bool f16);
+size_t decode_workspace_bytes(int batch, int kv_heads, int q_heads, int head_dim, int max_seq_len);
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);

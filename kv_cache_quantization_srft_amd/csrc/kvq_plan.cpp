@@ -1,0 +1,53 @@
+// Host-side planning of decode launches: head tiling, chunk size and workspace size.
+// Pure host code (no HIP call), shared by the quantized and the fp16 paths.
+#include <algorithm>
+
+#include "kvq_decode_common.h"
+
+namespace kvq_impl {
+namespace {
+
+constexpr long kTargetWorkgroups = 512;
+
+int token_align(bool f16) { return f16 ? 4 * 32 : 4 * 64; }  // 4 waves x superblock
+
+}  // namespace
+
+DecodePlan plan_decode(int batch, int kv_heads, int q_heads, int head_dim, int seq_len, int max_seq_len, bool f16) {
+  DecodePlan p{};
+  const int G = q_heads / kv_heads;
+  const int max_tile = head_dim == 128 ? 16 : 8;  // epilogue LDS holds 4 x tile x d floats
+  int tile = 1;
+  for (int t = std::min(G, max_tile); t >= 1; --t)
+    if (G % t == 0) {
+      tile = t;
+      break;
+    }
+  p.head_tile = tile;
+  p.head_tiles = G / tile;
+  const long units = long(batch) * kv_heads * p.head_tiles;
+  const long cap_chunks = std::max(1L, (kTargetWorkgroups + units - 1) / units);
+  const int align = token_align(f16);
+  auto chunk_for = [&](int len) {
+    long per = (std::max(len, 1) + cap_chunks - 1) / cap_chunks;
+    per = ((per + align - 1) / align) * align;
+    return int(std::max<long>(align, per));
+  };
+  p.chunk = chunk_for(seq_len);
+  p.n_chunks = (std::max(seq_len, 1) + p.chunk - 1) / p.chunk;
+  const int mc = chunk_for(max_seq_len);
+  p.max_chunks = std::max(p.n_chunks, (std::max(max_seq_len, 1) + mc - 1) / mc);
+  return p;
+}
+
+size_t decode_workspace_bytes(int batch, int kv_heads, int q_heads, int head_dim, int max_seq_len) {
+  size_t need = 0;
+  for (bool f16 : {false, true}) {
+    const DecodePlan p = plan_decode(batch, kv_heads, q_heads, head_dim, max_seq_len, max_seq_len, f16);
+    const dec::WsLayout w = dec::ws_layout(batch * kv_heads * p.head_tiles, p.head_tile, head_dim, p.max_chunks);
+    need = std::max(need, w.total);
+  }
+  return need;
+}
+
+}  // namespace kvq_impl
