@@ -30,31 +30,6 @@ typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 fp16x4_t;
 typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4_t;
 
 // ------------------------------------------------------------------------------------------
-// workspace
-// ------------------------------------------------------------------------------------------
-struct WsLayout {
-  size_t qdig;     // int8 query digits in MFMA A-operand order (quantized path)
-  size_t qsig;     // per-head score multiplier (quantized path)
-  size_t pml;      // per (unit, head, chunk): m, l
-  size_t pacc;     // per (unit, head, chunk): acc[d]
-  size_t total;
-};
-
-__host__ __device__ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
-
-__host__ __device__ inline WsLayout ws_layout(int units, int head_tile, int head_dim, int max_chunks) {
-  const int nrb = (head_tile + 3) / 4;
-  const int ns = head_dim / 64;
-  WsLayout w;
-  w.qdig = 0;
-  w.qsig = align256(size_t(units) * nrb * ns * 2 * 64 * 16);
-  w.pml = w.qsig + align256(size_t(units) * 16 * sizeof(float));
-  w.pacc = w.pml + align256(size_t(units) * head_tile * max_chunks * 2 * sizeof(float));
-  w.total = w.pacc + align256(size_t(units) * head_tile * max_chunks * size_t(head_dim) * sizeof(float));
-  return w;
-}
-
-// ------------------------------------------------------------------------------------------
 // twiddles: cos/sin(2 pi m / N), m < N, exact to float rounding (compile-time)
 // ------------------------------------------------------------------------------------------
 template <int N>
@@ -89,12 +64,12 @@ struct TwConst<256> {
 //   fwd[cb][s][lane][j] = 16 Q[16 cb + lane%16][32 s + 8 (lane/16) + j]   (q_hat = Q (s*q))
 //   inv[nb][s][lane][j] = 16 Q[32 s + 8 (lane/16) + j][16 nb + lane%16]   (x = Q^T y)
 // so one 16-byte load per lane fetches the operand of one MFMA.
-constexpr double q_entry(int c, int n, int D, const CosSin* tw) {
-  const double inv = 1.0 / csqrt(double(D));
+// inv = 1/sqrt(D), r2 = sqrt(2/D), tw[m] = (cos, sin)(2 pi m / D)
+constexpr double q_entry(int c, int n, int D, const CosSin* tw, double inv, double r2) {
   if (c == 0) return inv;
   if (c == 1) return (n & 1) ? -inv : inv;
   const CosSin w = tw[((c >> 1) * n) % D];
-  return (c & 1) ? -csqrt(2.0 / double(D)) * w.s : csqrt(2.0 / double(D)) * w.c;
+  return (c & 1) ? -r2 * w.s : r2 * w.c;
 }
 
 template <int D>
@@ -107,13 +82,14 @@ struct MfmaQTable {
   constexpr MfmaQTable() : fwd_hi(), fwd_lo(), inv_hi(), inv_lo() {
     CosSin tw[D] = {};
     for (int m = 0; m < D; ++m) tw[m] = cos_sin_turn(m, D);
+    const double inv = 1.0 / csqrt(double(D)), r2 = csqrt(2.0 / double(D));
     for (int b = 0; b < NB; ++b)
       for (int s = 0; s < NSTEP; ++s)
         for (int l = 0; l < 64; ++l)
           for (int j = 0; j < 8; ++j) {
             const int col = 16 * b + (l & 15), k = 32 * s + 8 * (l >> 4) + j;
             for (int which = 0; which < 2; ++which) {
-              const double v = 16.0 * (which == 0 ? q_entry(col, k, D, tw) : q_entry(k, col, D, tw));
+              const double v = 16.0 * (which == 0 ? q_entry(col, k, D, tw, inv, r2) : q_entry(k, col, D, tw, inv, r2));
               const float vf = float(v);
               const _Float16 hi = static_cast<_Float16>(vf);
               const _Float16 lo = static_cast<_Float16>(float(v - double(static_cast<float>(hi))));
@@ -280,6 +256,23 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict
   const int GT = head_tile;
   const int64_t orow0 = int64_t(b) * q_heads + kvh * G + ht * head_tile;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int NB = D / 16, NSTEP = D / 32, NBW = NB / kWaves;
+  // the inverse-rotation operands do not depend on the partials: load them first
+  constexpr bool kPre = ROT && D == 128;
+  uint4 pbh[kPre ? NBW : 1][NSTEP], pbl[kPre ? NBW : 1][NSTEP];
+  float psg[kPre ? NBW : 1];
+  if constexpr (kPre) {
+    const MfmaQTable<D>& T0 = mqtable<D>();
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s) {
+        pbh[j][s] = ld4(T0.inv_hi[w + kWaves * j][s][lane]);
+        pbl[j][s] = ld4(T0.inv_lo[w + kWaves * j][s][lane]);
+      }
+      psg[j] = sign[b * sign_bs + 16 * (w + kWaves * j) + (lane & 15)];
+    }
+  }
   // per-head chunk weights exp2(m_i - M) and 1/l, one wave per head
   for (int h = w; h < GT; h += kWaves) {
     const float* ml = pml + (int64_t(unit) * GT + h) * max_chunks * 2;
@@ -326,7 +319,6 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict
   }
   if constexpr (ROT) {
     __syncthreads();
-    constexpr int NB = D / 16, NSTEP = D / 32;
     const int n16 = lane & 15, r4 = lane >> 4;
     const MfmaQTable<D>& T = mqtable<D>();
     // A operands: y[head n16][32 s + 8 r4 + (0..7)] split into hi + lo
@@ -343,12 +335,19 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict
       ahi[s] = as_v8h(h4[0], h4[1], h4[2], h4[3]);
       alo[s] = as_v8h(l4[0], l4[1], l4[2], l4[3]);
     }
-    for (int nb = w; nb < NB; nb += kWaves) {
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      const int nb = w + kWaves * j;
       uint4 bh[NSTEP], bl[NSTEP];
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s) {
-        bh[s] = ld4(T.inv_hi[nb][s][lane]);
-        bl[s] = ld4(T.inv_lo[nb][s][lane]);
+        if constexpr (kPre) {
+          bh[s] = pbh[j][s];
+          bl[s] = pbl[j][s];
+        } else {
+          bh[s] = ld4(T.inv_hi[nb][s][lane]);
+          bl[s] = ld4(T.inv_lo[nb][s][lane]);
+        }
       }
       v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -360,7 +359,12 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[s], bhi, acc, 0, 0, 0);
       }
       const int n = 16 * nb + n16;
-      const float sg = (sign[b * sign_bs + n] < 0.0f ? -1.0f : 1.0f) * 0.0625f;
+      float sgn;
+      if constexpr (kPre)
+        sgn = psg[j];
+      else
+        sgn = sign[b * sign_bs + n];
+      const float sg = (sgn < 0.0f ? -1.0f : 1.0f) * 0.0625f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int h = 4 * r4 + i;

@@ -57,7 +57,6 @@ __global__ __launch_bounds__(kThreads) void qprep_kernel(const uint16_t* __restr
   constexpr int NS = D / 64;
   constexpr int NB = D / 16, NSTEP = D / 32;
   __shared__ float qh[16][D];  // rotated, scaled query
-  __shared__ __align__(16) uint32_t smask[D / 2];
   __shared__ float sig[16];
   const int unit = blockIdx.x;
   const int ht = unit % head_tiles;
@@ -68,50 +67,57 @@ __global__ __launch_bounds__(kThreads) void qprep_kernel(const uint16_t* __restr
   const int h0 = kvh * G + ht * head_tile;
   const int GT = head_tile;
   const int nrb = (GT + 3) / 4;
-  for (int i = threadIdx.x; i < D / 2; i += kThreads) {
-    const float* s = sign + b * sign_bs;
-    smask[i] = (s[2 * i] < 0.0f ? 0x8000u : 0u) | (s[2 * i + 1] < 0.0f ? 0x80000000u : 0u);
-  }
-  __syncthreads();
   // q_hat[h][c] = sum_n Q[c][n] s_n q[h][n] * lambda_c * scale as MFMAs: A = the fp16 query
   // (exact, signs flipped in the fp16 bits), B = the forward table (16 Q as fp16 hi + lo).
+  // Every global load of the wave is issued before the first MFMA.
   {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int n16 = lane & 15, r4 = lane >> 4;
+    constexpr int NBW = NB / kWaves;  // channel blocks per wave
+    const MfmaQTable<D>& T = mqtable<D>();
+    uint4 bh[NBW][NSTEP], bl[NBW][NSTEP];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s) {
+        bh[j][s] = ld4(T.fwd_hi[w + kWaves * j][s][lane]);
+        bl[j][s] = ld4(T.fwd_lo[w + kWaves * j][s][lane]);
+      }
+    float lam[NBW];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+      lam[j] = (lambda ? lambda[b * lambda_bs + int64_t(kvh) * D + 16 * (w + kWaves * j) + n16] : 1.0f) * scale *
+               0.0625f;
     v8h aq[NSTEP];
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
       if (n16 < GT) {
         v = *reinterpret_cast<const uint4*>(q + (int64_t(b) * q_heads + h0 + n16) * D + 32 * s + 8 * r4);
-        const uint4 m = *reinterpret_cast<const uint4*>(smask + (32 * s + 8 * r4) / 2);
-        v.x ^= m.x;
-        v.y ^= m.y;
-        v.z ^= m.z;
-        v.w ^= m.w;
+        const float4 s0 = *reinterpret_cast<const float4*>(sign + b * sign_bs + 32 * s + 8 * r4);
+        const float4 s1 = *reinterpret_cast<const float4*>(sign + b * sign_bs + 32 * s + 8 * r4 + 4);
+        v.x ^= (s0.x < 0.0f ? 0x8000u : 0u) | (s0.y < 0.0f ? 0x80000000u : 0u);
+        v.y ^= (s0.z < 0.0f ? 0x8000u : 0u) | (s0.w < 0.0f ? 0x80000000u : 0u);
+        v.z ^= (s1.x < 0.0f ? 0x8000u : 0u) | (s1.y < 0.0f ? 0x80000000u : 0u);
+        v.w ^= (s1.z < 0.0f ? 0x8000u : 0u) | (s1.w < 0.0f ? 0x80000000u : 0u);
       }
       aq[s] = as_v8h(v.x, v.y, v.z, v.w);
     }
-    const MfmaQTable<D>& T = mqtable<D>();
-    for (int cb = w; cb < NB; cb += kWaves) {
-      uint4 bh[NSTEP], bl[NSTEP];
 #pragma unroll
-      for (int s = 0; s < NSTEP; ++s) {
-        bh[s] = ld4(T.fwd_hi[cb][s][lane]);
-        bl[s] = ld4(T.fwd_lo[cb][s][lane]);
-      }
+    for (int j = 0; j < NBW; ++j) {
       v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], as_v8h(bh[s].x, bh[s].y, bh[s].z, bh[s].w), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], as_v8h(bl[s].x, bl[s].y, bl[s].z, bl[s].w), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], as_v8h(bh[j][s].x, bh[j][s].y, bh[j][s].z, bh[j][s].w),
+                                                     acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], as_v8h(bl[j][s].x, bl[j][s].y, bl[j][s].z, bl[j][s].w),
+                                                     acc, 0, 0, 0);
       }
-      const int c = 16 * cb + n16;
-      const float lam = (lambda ? lambda[b * lambda_bs + int64_t(kvh) * D + c] : 1.0f) * scale * 0.0625f;
+      const int c = 16 * (w + kWaves * j) + n16;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int h = 4 * r4 + i;
-        if (h < GT) qh[h][c] = acc[i] * lam;
+        if (h < GT) qh[h][c] = acc[i] * lam[j];
       }
     }
   }
@@ -276,11 +282,14 @@ __device__ __forceinline__ void wave_sync_lds() {
 
 // Everything one wave does with one superblock already in registers.
 template <int D, int KB, int NRB>
-__device__ __forceinline__ void process_superblock(const SBRegs<D, KB>& r, int base, int t_end, int lane,
+__device__ __forceinline__ void process_superblock(SBRegs<D, KB>& r, int base, int t_end, int lane,
                                                    const v4i (&aop)[NRB][D / 64][2], const float (&sig)[NRB],
                                                    float (&m_run)[NRB], float (&l_run)[NRB], v4f (&acc)[D / 16],
                                                    uint8_t* vtile, uint16_t* stile, uint16_t* ktile, float* ptile,
-                                                   float* atile) {
+                                                   float* atile, const uint8_t* __restrict__ kc,
+                                                   const uint16_t* __restrict__ ks, const uint8_t* __restrict__ vc,
+                                                   const uint16_t* __restrict__ vs, int64_t rowbase, int next_base,
+                                                   int last_tok) {
   using Gm = QGeom<D, KB>;
   constexpr int NS = Gm::NS, NG = Gm::NG;
   const int n16 = lane & 15, r4 = lane >> 4;
@@ -352,6 +361,9 @@ __device__ __forceinline__ void process_superblock(const SBRegs<D, KB>& r, int b
       sc[sb][rb] = valid ? s_acc * sig[rb] : -INFINITY;
     }
   }
+
+  // the registers of this superblock are consumed: the next one loads during softmax + values
+  if (next_base < t_end) load_superblock<D, KB>(r, kc, ks, vc, vs, rowbase, next_base, last_tok, lane);
 
   // ---------------- online softmax per head (16-lane rows) ----------------
   bool rescale = false;
@@ -508,9 +520,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
 
   while (base < t_end) {
     process_superblock<D, KB, NRB>(ra, base, t_end, lane, aop, sig, m_run, l_run, acc, vtile, stile, ktile, ptile,
-                                   atile);
+                                   atile, kc, ks, vc, vs, rowbase, base + kStride, last_tok);
     base += kStride;
-    if (base < t_end) load_superblock<D, KB>(ra, kc, ks, vc, vs, rowbase, base, last_tok, lane);
   }
 
   PartialArgs e;

@@ -2,7 +2,7 @@
 // Pure host code (no HIP call), shared by the quantized and the fp16 paths.
 #include <algorithm>
 
-#include "kvq_decode_common.h"
+#include "kvq_internal.h"
 
 namespace kvq_impl {
 namespace {
@@ -44,7 +44,7 @@ size_t decode_workspace_bytes(int batch, int kv_heads, int q_heads, int head_dim
   size_t need = 0;
   for (bool f16 : {false, true}) {
     const DecodePlan p = plan_decode(batch, kv_heads, q_heads, head_dim, max_seq_len, max_seq_len, f16);
-    const dec::WsLayout w = dec::ws_layout(batch * kv_heads * p.head_tiles, p.head_tile, head_dim, p.max_chunks);
+    const WsLayout w = ws_layout(batch * kv_heads * p.head_tiles, p.head_tile, head_dim, p.max_chunks);
     need = std::max(need, w.total);
   }
   return need;
