@@ -194,7 +194,7 @@ def main():
     torch.cuda.synchronize()
     log(f"cache copies: {n_q} quantized x {q_bytes / 1e6:.1f} MB, {n_f} fp16 x {f16_bytes / 1e6:.1f} MB")
 
-    ws = torch.empty(kvq.kvq_decode_attn_workspace_bytes(lay, S), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(kvq.kvq_decode_attn_workspace_bytes(lay, S), dtype=torch.uint8, device="cuda")
     out = torch.empty(LB * Hq * d, dtype=torch.float32, device="cuda")
     out16 = torch.empty_like(out)
     # the step's new token: the last cache position of every layer, re-quantized in place

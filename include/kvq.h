@@ -151,8 +151,14 @@ size_t kvq_decode_attn_workspace_bytes(const kvq_layout* layout, int32_t max_seq
  *   sign_k/v     : float [*, head_dim] +-1, row stride sign_batch_stride (0 = shared)
  *   lambda_k/v   : float [*, kv_heads, head_dim] or NULL (= 1), row stride lambda_batch_stride
  *   sm_scale     : softmax scale; <= 0 selects 1/sqrt(head_dim)
- *   workspace    : >= kvq_decode_attn_workspace_bytes(layout, seq_len) bytes, 256-byte aligned,
- *                  contents irrelevant on entry; in use until the work on `stream` completes
+ *   workspace    : >= kvq_decode_attn_workspace_bytes(layout, seq_len) bytes, 256-byte aligned.
+ *                  Its first 65536 bytes are completion counters: zero them once after
+ *                  allocating the workspace; every call leaves them zero.  The rest is scratch.
+ *                  One workspace serves one call at a time (calls in flight on different
+ *                  streams need their own); in use until the work on `stream` completes.
+ *                  batch * kv_heads * (G / head tile) must not exceed 16384, where the head
+ *                  tile is the largest divisor of G = q_heads / kv_heads that is at most 16
+ *                  (head_dim 128) or 8 (head_dim 256); KVQ_ERR_UNSUPPORTED otherwise.
  *   out          : float [batch, q_heads, head_dim]
  */
 kvq_status kvq_decode_attn(const kvq_layout* layout, const void* q_f16, const void* k_codes,

@@ -5,7 +5,8 @@
 Every source is compiled with hipcc for gfx950 only, in parallel, then linked into
 kv_cache_quantization_srft_amd/libkvq.so.  Packed-FP32 VALU instructions are disabled for the
 device code (-packed-fp32-ops); hipcc's host pass prints that it does not know that feature,
-which is harmless.
+which is harmless.  MFMA instructions write their results to ordinary VGPRs
+(-amdgpu-mfma-vgpr-form), which saves the copies out of accumulator registers.
 """
 from __future__ import annotations
 
@@ -27,6 +28,8 @@ COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fconstexpr-steps=100000000", "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include"),
+    # MFMA results in VGPRs (gfx950 has one register file): no accumulator-register copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

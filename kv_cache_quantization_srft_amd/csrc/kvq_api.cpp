@@ -7,7 +7,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/kvq.h"
+#include "kvq.h"
 #include "kvq_internal.h"
 
 namespace {
@@ -102,6 +102,14 @@ kvq_status check_decode_common(const kvq_layout* L, const void* q, int32_t seq_l
   KVQ_TRY(check_ptr(q, 16, fn, "q"));
   KVQ_TRY(check_ptr(out, 16, fn, "out"));
   KVQ_TRY(check_opt_ptr(seq_lens, 4, fn, "seq_lens"));
+  {
+    const kvq_impl::DecodePlan pl =
+        kvq_impl::plan_decode(L->batch, L->kv_heads, L->q_heads, L->head_dim, seq_len, seq_len, false);
+    const long units = long(L->batch) * L->kv_heads * pl.head_tiles;
+    if (units > kvq_impl::kMaxDecodeUnits)
+      return fail(KVQ_ERR_UNSUPPORTED, "%s: batch x kv_heads x head tiles = %ld exceeds %d", fn, units,
+                  kvq_impl::kMaxDecodeUnits);
+  }
   KVQ_TRY(check_ptr(workspace, 256, fn, "workspace"));
   const size_t need = kvq_impl::decode_workspace_bytes(L->batch, L->kv_heads, L->q_heads, L->head_dim, seq_len);
   if (workspace_bytes < need)

@@ -1,7 +1,7 @@
-// Shared pieces of the decode-attention kernels (gfx950): workspace layout, 16-lane DPP row
-// reductions, the online-softmax bookkeeping of one wave, and the epilogue that merges the
-// per-chunk partials of one (sequence, kv head, head tile) in the last work-group to finish
-// and applies the single inverse rotation.
+// Shared pieces of the decode-attention kernels (gfx950): the SRFT entry table and the MFMA
+// operands generated from it, 16-lane DPP row reductions, the end of a chunk (work-group partial
+// of the online softmax) and the merge of the chunk partials of one (sequence, kv head, head
+// tile) with the single inverse rotation, done by the last work-group of the unit to finish.
 //
 // Partial results follow the tiled attention with online softmax of the hotdry blog
 // ("Flash Attention 与 Metal 内核融合"): every chunk keeps (m, l, acc) with scores in log2
@@ -114,6 +114,91 @@ __device__ __forceinline__ const MfmaQTable<D>& mqtable() {
     return kMQ256;
 }
 
+// ------------------------------------------------------------------------------------------
+// SRFT entries generated in registers.  16 Q[c][n] depends on (c, n) only through the row
+// kind (c = 0, c = 1, even c, odd c) and the angle m = (c/2) n mod D, so a table of 2D fp16
+// (hi | lo << 16) pairs, interleaved per angle, gives every entry with one LDS read:
+//   e[2m]     = 16 sqrt(2/D) cos(2 pi m / D)     (rows c = 2k, k >= 1)
+//   e[2m + 1] = -16 sqrt(2/D) sin(2 pi m / D)    (rows c = 2k + 1, k >= 1)
+//   rows 0 and 1: 16/sqrt(D) and (-1)^n 16/sqrt(D).
+// The split is the one of the full table above (double -> float -> fp16 hi, residual -> lo).
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ v8h as_v8h(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  v4i t = {int(a), int(b), int(c), int(d)};
+  return __builtin_bit_cast(v8h, t);
+}
+
+constexpr uint32_t split16(double v) {
+  const float vf = float(v);
+  const _Float16 hi = static_cast<_Float16>(vf);
+  const _Float16 lo = static_cast<_Float16>(float(v - double(static_cast<float>(hi))));
+  return uint32_t(__builtin_bit_cast(uint16_t, hi)) | (uint32_t(__builtin_bit_cast(uint16_t, lo)) << 16);
+}
+
+template <int D>
+struct SrftPairs {
+  uint32_t e[2 * D];
+  constexpr SrftPairs() : e() {
+    const double r2 = csqrt(2.0 / double(D));
+    for (int m = 0; m < D; ++m) {
+      const CosSin w = cos_sin_turn(m, D);
+      e[2 * m] = split16(16.0 * (r2 * w.c));
+      e[2 * m + 1] = split16(16.0 * (-(r2 * w.s)));
+    }
+  }
+};
+
+template <int D>
+struct SrftRow0 {
+  static constexpr uint32_t pos = split16(16.0 * (1.0 / csqrt(double(D))));
+  static constexpr uint32_t neg = split16(16.0 * (-(1.0 / csqrt(double(D)))));
+};
+
+__device__ const SrftPairs<128> kSP128 = SrftPairs<128>();
+__device__ const SrftPairs<256> kSP256 = SrftPairs<256>();
+
+// Copy the pair table to LDS (2D words), all threads of the work-group: fetch into registers,
+// then store (so the caller can issue other loads in between).
+template <int D>
+__device__ __forceinline__ void srft_pairs_fetch(uint32_t (&v)[2 * D / kThreads]) {
+  const uint32_t* src = D == 128 ? kSP128.e : kSP256.e;
+#pragma unroll
+  for (int i = 0; i < 2 * D / kThreads; ++i) v[i] = src[threadIdx.x + i * kThreads];
+}
+template <int D>
+__device__ __forceinline__ void srft_pairs_store(uint32_t* tw, const uint32_t (&v)[2 * D / kThreads]) {
+#pragma unroll
+  for (int i = 0; i < 2 * D / kThreads; ++i) tw[threadIdx.x + i * kThreads] = v[i];
+}
+
+// 16 Q[c][n] as an fp16 (hi | lo << 16) pair.
+template <int D>
+__device__ __forceinline__ uint32_t q_pair(const uint32_t* tw, int c, int n) {
+  const uint32_t v = tw[2 * (((c >> 1) * n) & (D - 1)) + (c & 1)];
+  return c >= 2 ? v : ((c & n & 1) ? SrftRow0<D>::neg : SrftRow0<D>::pos);
+}
+
+// B operand (hi and lo halves) of v_mfma_f32_16x16x32_f16 for step s and column block blk.
+// Lane l holds k = 8 (l / 16) + j (j = 0..7) of column l % 16:
+//   forward (q_hat = Q x):   B[k][col] = 16 Q[16 blk + col][32 s + k]
+//   inverse (x = Q^T y):     B[k][col] = 16 Q[32 s + k][16 blk + col]
+template <int D, bool INV>
+__device__ __forceinline__ void srft_operand(const uint32_t* tw, int blk, int s, int lane, v8h& hi, v8h& lo) {
+  const int fixed = 16 * blk + (lane & 15);
+  const int k0 = 32 * s + 8 * (lane >> 4);
+  uint32_t e[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) e[j] = INV ? q_pair<D>(tw, k0 + j, fixed) : q_pair<D>(tw, fixed, k0 + j);
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = (e[2 * i] & 0xffffu) | (e[2 * i + 1] << 16);
+    l[i] = (e[2 * i] >> 16) | (e[2 * i + 1] & 0xffff0000u);
+  }
+  hi = as_v8h(h[0], h[1], h[2], h[3]);
+  lo = as_v8h(l[0], l[1], l[2], l[3]);
+}
+
 __device__ __forceinline__ uint4 ld4(const uint32_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // ------------------------------------------------------------------------------------------
@@ -160,10 +245,6 @@ __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint3
   lo = uint32_t(__builtin_bit_cast(uint16_t, la)) | (uint32_t(__builtin_bit_cast(uint16_t, lb)) << 16);
 }
 
-__device__ __forceinline__ v8h as_v8h(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  v4i t = {int(a), int(b), int(c), int(d)};
-  return __builtin_bit_cast(v8h, t);
-}
 
 // ------------------------------------------------------------------------------------------
 // End of a chunk.  Every wave holds, for the heads of its slots, m (uniform in each 16-lane
@@ -171,6 +252,18 @@ __device__ __forceinline__ v8h as_v8h(uint32_t a, uint32_t b, uint32_t c, uint32
 // r4 = lane / 16) holds acc[g][i] for head 4*r4 + i, channel 16*g + c.  The work-group combines
 // its 4 waves in LDS and stores one partial (m, l, acc[d]) per head of the unit.
 // ------------------------------------------------------------------------------------------
+// Chunk partials travel between work-groups that may sit on different XCDs (separate L2s).
+// They are written and read as device-scope relaxed atomics (global_store / global_load with
+// the sc1 scope bit), which the memory model keeps coherent at device scope without an L2
+// writeback or invalidate; ordering against the completion counter comes from waiting for the
+// stores to complete before the counter is incremented (arrive_last).
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 struct PartialArgs {
   int head_tile;
   int max_chunks, chunk_index;
@@ -221,106 +314,156 @@ __device__ __forceinline__ void store_partial(float (&m_run)[NSLOT], float (&l_r
       ll += wml[(ww * 16 + h) * 2 + 1] * f;
     }
     const int64_t prow = (e.unit * GT + h) * e.max_chunks + e.chunk_index;
-    e.pacc[prow * D + c] = a;
+    st_dev(&e.pacc[prow * D + c], a);
     if (c == 0) {
-      e.pml[2 * prow] = mm;
-      e.pml[2 * prow + 1] = ll;
+      st_dev(&e.pml[2 * prow], mm);
+      st_dev(&e.pml[2 * prow + 1], ll);
     }
   }
 }
 
 // ------------------------------------------------------------------------------------------
-// Merge: one work-group of 4 waves per unit (sequence, kv head, head tile).  Every (head,
-// channel) combines its chunks, y = acc_scale * acc / l; with ROT, y is scaled by lambda_V and
-// inverse-rotated with MFMAs against the inverse table (A = y split into fp16 hi + lo):
-//   x[h][n] = s_n sum_c y[h][c] Q[c][n]
+// Completion count of a unit.  Every wave of the work-group waits until its device-scope
+// partial stores have completed (s_waitcnt vmcnt(0)), the work-group synchronizes, and thread 0
+// adds 1 to the unit's counter (a device-scope atomic).  The work-group that brings the count to
+// n_chunks resets the counter to 0 for the next call and merges the unit; its device-scope
+// loads are issued after the increment has returned, so they see every chunk's partial.
 // ------------------------------------------------------------------------------------------
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, int n_chunks, int* flag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev + 1u == uint32_t(n_chunks);
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last ? 1 : 0;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
+// ------------------------------------------------------------------------------------------
+// Merge of one unit (sequence, kv head, head tile) by one work-group of 4 waves.  Every
+// (head, channel) combines its chunks, y = acc_scale * acc / l; with ROT, y is scaled by
+// lambda_V and inverse-rotated with MFMAs against generated operands (A = y split into fp16
+// hi + lo):  x[h][n] = s_n sum_c y[h][c] Q[c][n].
+// ------------------------------------------------------------------------------------------
+struct MergeArgs {
+  const float* pml;
+  const float* pacc;
+  int n_chunks, max_chunks, head_tile, head_tiles, q_heads, kv_heads;
+  float acc_scale;
+  const float* sign;
+  int64_t sign_bs;
+  const float* lambda;
+  int64_t lambda_bs;
+  float* out;
+};
+
+template <int D>
+constexpr int merge_lds_floats() {
+  return 16 * D + 16 * 32 + 32;
+}
+
 template <int D, bool ROT>
-__global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict__ pml, const float* __restrict__ pacc,
-                                                        int n_chunks, int max_chunks, int head_tile, int head_tiles,
-                                                        int q_heads, int kv_heads, float acc_scale,
-                                                        const float* __restrict__ sign, int64_t sign_bs,
-                                                        const float* __restrict__ lambda, int64_t lambda_bs,
-                                                        float* __restrict__ out) {
+__device__ __forceinline__ void merge_unit(const MergeArgs& a, int unit, float* smem, const uint32_t* tw) {
   constexpr int MAXC = 32;  // chunks whose weights are staged in LDS at once
-  __shared__ __align__(16) float y[16][D];
-  __shared__ float wgt[16][MAXC];
-  __shared__ float linv[16];
-  __shared__ float mmax[16];
-  const int unit = blockIdx.x;
-  const int ht = unit % head_tiles;
-  const int bk = unit / head_tiles;
-  const int kvh = bk % kv_heads;
-  const int b = bk / kv_heads;
-  const int G = q_heads / kv_heads;
-  const int GT = head_tile;
-  const int64_t orow0 = int64_t(b) * q_heads + kvh * G + ht * head_tile;
+  constexpr int NP = 16 * D / kThreads;  // (head, channel) pairs per thread, at most
+  constexpr int CR = 8 * 128 / D;        // chunks of each pair prefetched into registers
+  float(*y)[D] = reinterpret_cast<float(*)[D]>(smem);
+  float(*wgt)[MAXC] = reinterpret_cast<float(*)[MAXC]>(smem + 16 * D);
+  float* linv = smem + 16 * D + 16 * MAXC;
+  float* mmax = linv + 16;
+  const int ht = unit % a.head_tiles;
+  const int bk = unit / a.head_tiles;
+  const int kvh = bk % a.kv_heads;
+  const int b = bk / a.kv_heads;
+  const int G = a.q_heads / a.kv_heads;
+  const int GT = a.head_tile;
+  const int n_chunks = a.n_chunks, max_chunks = a.max_chunks;
+  const int64_t orow0 = int64_t(b) * a.q_heads + kvh * G + ht * GT;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   constexpr int NB = D / 16, NSTEP = D / 32, NBW = NB / kWaves;
-  // the inverse-rotation operands do not depend on the partials: load them first
-  constexpr bool kPre = ROT && D == 128;
-  uint4 pbh[kPre ? NBW : 1][NSTEP], pbl[kPre ? NBW : 1][NSTEP];
-  float psg[kPre ? NBW : 1];
-  if constexpr (kPre) {
-    const MfmaQTable<D>& T0 = mqtable<D>();
+  // every load that does not depend on another goes out first: the first CR chunks of this
+  // thread's (head, channel) pairs, lambda and the output signs, then the (m, l) pairs
+  float pre[NP][CR];
+  float lamv[NP];
 #pragma unroll
-    for (int j = 0; j < NBW; ++j) {
+  for (int k = 0; k < NP; ++k) {
+    const int idx = threadIdx.x + k * kThreads;
+    const int h = idx / D, c = idx - h * D;
+    lamv[k] = 1.0f;
 #pragma unroll
-      for (int s = 0; s < NSTEP; ++s) {
-        pbh[j][s] = ld4(T0.inv_hi[w + kWaves * j][s][lane]);
-        pbl[j][s] = ld4(T0.inv_lo[w + kWaves * j][s][lane]);
-      }
-      psg[j] = sign[b * sign_bs + 16 * (w + kWaves * j) + (lane & 15)];
+    for (int i = 0; i < CR; ++i) pre[k][i] = 0.0f;
+    if (h < GT) {
+      const float* pa = a.pacc + (int64_t(unit) * GT + h) * max_chunks * D + c;
+#pragma unroll
+      for (int i = 0; i < CR; ++i)
+        if (i < n_chunks) pre[k][i] = ld_dev(&pa[int64_t(i) * D]);
+      if (ROT && a.lambda) lamv[k] = a.lambda[b * a.lambda_bs + int64_t(kvh) * D + c];
     }
+  }
+  float psg[ROT ? NBW : 1];
+  if constexpr (ROT) {
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) psg[j] = a.sign[b * a.sign_bs + 16 * (w + kWaves * j) + (lane & 15)];
   }
   // per-head chunk weights exp2(m_i - M) and 1/l, one wave per head
   for (int h = w; h < GT; h += kWaves) {
-    const float* ml = pml + (int64_t(unit) * GT + h) * max_chunks * 2;
-    float mm = -INFINITY;
-    for (int i = lane; i < n_chunks; i += 64) mm = fmaxf(mm, ml[2 * i]);
+    const float* ml = a.pml + (int64_t(unit) * GT + h) * max_chunks * 2;
+    float mv[2], lv[2];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = lane + 64 * r;
+      mv[r] = i < n_chunks ? ld_dev(&ml[2 * i]) : -INFINITY;
+      lv[r] = i < n_chunks ? ld_dev(&ml[2 * i + 1]) : 0.0f;
+    }
+    float mm = fmaxf(mv[0], mv[1]);
+    for (int i = lane + 128; i < n_chunks; i += 64) mm = fmaxf(mm, ld_dev(&ml[2 * i]));
     for (int off = 32; off > 0; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off));
     float ll = 0.0f;
-    for (int i = lane; i < n_chunks; i += 64) {
-      const float f = exp2_guard(ml[2 * i], mm);
-      ll += ml[2 * i + 1] * f;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = lane + 64 * r;
+      const float f = exp2_guard(mv[r], mm);
+      ll += lv[r] * f;
       if (i < MAXC) wgt[h][i] = f;
     }
+    for (int i = lane + 128; i < n_chunks; i += 64) ll += ld_dev(&ml[2 * i + 1]) * exp2_guard(ld_dev(&ml[2 * i]), mm);
     for (int off = 32; off > 0; off >>= 1) ll += __shfl_xor(ll, off);
     if (lane == 0) {
-      linv[h] = ll > 0.0f ? acc_scale / ll : 0.0f;
+      linv[h] = ll > 0.0f ? a.acc_scale / ll : 0.0f;
       mmax[h] = mm;
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < 16 * D; idx += kThreads) {
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    const int idx = threadIdx.x + k * kThreads;
     const int h = idx / D, c = idx - h * D;
     float v = 0.0f;
     if (h < GT) {
-      const float* pa = pacc + (int64_t(unit) * GT + h) * max_chunks * D + c;
-      const float* ml = pml + (int64_t(unit) * GT + h) * max_chunks * 2;
-      float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      int i = 0;
-      for (; i + 4 <= n_chunks && i + 4 <= MAXC; i += 4) {
+      const float* pa = a.pacc + (int64_t(unit) * GT + h) * max_chunks * D + c;
+      const float* ml = a.pml + (int64_t(unit) * GT + h) * max_chunks * 2;
+      float acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) a[j] = fmaf(pa[int64_t(i + j) * D], wgt[h][i + j], a[j]);
+      for (int i = 0; i < CR; ++i)
+        if (i < n_chunks) acc4[i & 3] = fmaf(pre[k][i], wgt[h][i], acc4[i & 3]);
+      for (int i = CR; i < n_chunks; ++i) {
+        const float f = i < MAXC ? wgt[h][i] : exp2_guard(ld_dev(&ml[2 * i]), mmax[h]);
+        acc4[i & 3] = fmaf(ld_dev(&pa[int64_t(i) * D]), f, acc4[i & 3]);
       }
-      for (; i < n_chunks; ++i) {
-        const float f = i < MAXC ? wgt[h][i] : exp2_guard(ml[2 * i], mmax[h]);
-        a[0] = fmaf(pa[int64_t(i) * D], f, a[0]);
-      }
-      v = ((a[0] + a[1]) + (a[2] + a[3])) * linv[h];
-      if constexpr (!ROT) {
-        out[(orow0 + h) * D + c] = v;
-      } else {
-        if (lambda) v *= lambda[b * lambda_bs + int64_t(kvh) * D + c];
-      }
+      v = ((acc4[0] + acc4[1]) + (acc4[2] + acc4[3])) * linv[h];
+      if constexpr (!ROT)
+        a.out[(orow0 + h) * D + c] = v;
+      else
+        v *= lamv[k];
     }
     y[h][c] = v;
   }
   if constexpr (ROT) {
     __syncthreads();
     const int n16 = lane & 15, r4 = lane >> 4;
-    const MfmaQTable<D>& T = mqtable<D>();
     // A operands: y[head n16][32 s + 8 r4 + (0..7)] split into hi + lo
     v8h ahi[NSTEP], alo[NSTEP];
 #pragma unroll
@@ -338,37 +481,21 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(const float* __restrict
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       const int nb = w + kWaves * j;
-      uint4 bh[NSTEP], bl[NSTEP];
-#pragma unroll
-      for (int s = 0; s < NSTEP; ++s) {
-        if constexpr (kPre) {
-          bh[s] = pbh[j][s];
-          bl[s] = pbl[j][s];
-        } else {
-          bh[s] = ld4(T.inv_hi[nb][s][lane]);
-          bl[s] = ld4(T.inv_lo[nb][s][lane]);
-        }
-      }
       v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s) {
-        const v8h bhi = as_v8h(bh[s].x, bh[s].y, bh[s].z, bh[s].w);
-        const v8h blo = as_v8h(bl[s].x, bl[s].y, bl[s].z, bl[s].w);
+        v8h bhi, blo;
+        srft_operand<D, true>(tw, nb, s, lane, bhi, blo);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[s], bhi, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[s], blo, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[s], bhi, acc, 0, 0, 0);
       }
       const int n = 16 * nb + n16;
-      float sgn;
-      if constexpr (kPre)
-        sgn = psg[j];
-      else
-        sgn = sign[b * sign_bs + n];
-      const float sg = (sgn < 0.0f ? -1.0f : 1.0f) * 0.0625f;
+      const float sg = (psg[j] < 0.0f ? -1.0f : 1.0f) * 0.0625f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int h = 4 * r4 + i;
-        if (h < GT) out[(orow0 + h) * D + n] = acc[i] * sg;
+        if (h < GT) a.out[(orow0 + h) * D + n] = acc[i] * sg;
       }
     }
   }

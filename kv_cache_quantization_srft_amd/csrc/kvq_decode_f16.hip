@@ -7,7 +7,8 @@
 //     softmax: online per head over 16-lane DPP rows;
 //     values : v_mfma_f32_16x16x32_f16 with A = p split into fp16 hi + lo and B = the fp16
 //              values read transposed from LDS with ds_read_b64_tr_b16;
-//   merge_kernel        : the same chunk merge as the quantized path, without rotation.
+//     epilogue: the same chunk partials and last-work-group merge as the quantized path,
+//              without rotation.
 #include <algorithm>
 
 #include "kvq_decode_common.h"
@@ -29,7 +30,9 @@ struct FGeom {
   static constexpr int LDS_P = 16 * kSB16 * 4;
   static constexpr int LDS_WAVE = LDS_V + LDS_P + 16 * 4;
   static constexpr int LDS_EPI = (kWaves * 16 * 2 + kWaves * (D == 128 ? 16 : 8) * D) * 4;
-  static constexpr int LDS = (kWaves * LDS_WAVE > LDS_EPI ? kWaves * LDS_WAVE : LDS_EPI);
+  static constexpr int LDS_M = merge_lds_floats<D>() * 4;
+  static constexpr int LDS_A = kWaves * LDS_WAVE > LDS_EPI ? kWaves * LDS_WAVE : LDS_EPI;
+  static constexpr int LDS = LDS_A > LDS_M ? LDS_A : LDS_M;
 };
 
 template <int D>
@@ -37,10 +40,11 @@ __global__ __launch_bounds__(kThreads) void decode_f16_kernel(
     const uint16_t* __restrict__ kx, const uint16_t* __restrict__ vx, const uint16_t* __restrict__ q,
     const int32_t* __restrict__ seq_lens, int seq_len, int kv_heads, int q_heads, int capacity, int head_tile,
     int head_tiles, int chunk, int n_chunks, int max_chunks, float qscale, float* __restrict__ pml,
-    float* __restrict__ pacc) {
+    float* __restrict__ pacc, uint32_t* __restrict__ counters, const MergeArgs merge) {
   using Gm = FGeom<D>;
   constexpr int NG = Gm::NG, NSTEP = Gm::NSTEP;
   __shared__ __align__(16) uint8_t smem[Gm::LDS];
+  __shared__ int last_flag;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n16 = lane & 15, r4 = lane >> 4;
   const int ch = blockIdx.x % n_chunks;
@@ -200,6 +204,8 @@ __global__ __launch_bounds__(kThreads) void decode_f16_kernel(
   e.pacc = pacc;
   store_partial<D, 4>(m_run, l_run, acc, [](int k, int rr) { return 4 * rr + k; }, e,
                       reinterpret_cast<float*>(smem));
+  if (!arrive_last(counters + unit, n_chunks, &last_flag)) return;
+  merge_unit<D, false>(merge, int(unit), reinterpret_cast<float*>(smem), nullptr);
 }
 
 template <int D>
@@ -208,13 +214,14 @@ hipError_t launch_f16(const DecodeF16Args& a, const DecodePlan& p, const WsLayou
   auto* pml = reinterpret_cast<float*>(ws + w.pml);
   auto* pacc = reinterpret_cast<float*>(ws + w.pacc);
   const int units = a.batch * a.kv_heads * p.head_tiles;
+  auto* counters = reinterpret_cast<uint32_t*>(ws + w.counters);
+  const MergeArgs m{pml,       pacc,       p.n_chunks, p.max_chunks, p.head_tile, p.head_tiles, a.q_heads,
+                    a.kv_heads, 1.0f,      nullptr,    0,            nullptr,     0,            a.out};
   hipLaunchKernelGGL((decode_f16_kernel<D>), dim3(units * p.n_chunks), dim3(kThreads), 0, s,
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.q), a.seq_lens, a.seq_len, a.kv_heads, a.q_heads, a.capacity,
-                     p.head_tile, p.head_tiles, p.chunk, p.n_chunks, p.max_chunks, a.sm_scale * kLog2e, pml, pacc);
-  hipLaunchKernelGGL((merge_kernel<D, false>), dim3(units), dim3(kThreads), 0, s, pml, pacc, p.n_chunks,
-                     p.max_chunks, p.head_tile, p.head_tiles, a.q_heads, a.kv_heads, 1.0f, nullptr, 0, nullptr, 0,
-                     a.out);
+                     p.head_tile, p.head_tiles, p.chunk, p.n_chunks, p.max_chunks, a.sm_scale * kLog2e, pml, pacc,
+                     counters, m);
   return hipGetLastError();
 }
 

@@ -5,13 +5,14 @@
 //   score_t = (SRFT_sK(q) * lambda_K * sm_scale * log2 e) . (code_K,t * scale_K,t)      [log2 units]
 //   out     = s_V * SRFT^-1( lambda_V * sum_t p_t code_V,t * scale_V,t / sum_t p_t )
 //
-// Three launches per call:
-//   qprep_kernel : one work-group per (sequence, kv head, head tile).  Rotates the query heads
-//                  (O(d^2) with an LDS twiddle table), splits every rotated channel into a
-//                  16-bit integer (two int8 digits, per-head step sigma) laid out exactly as the
-//                  A operand of the score MFMA.
-//   decode_kernel: one work-group of 4 waves per (unit, chunk of tokens).  Each wave walks
-//                  64-token superblocks:
+// One launch per call: a work-group of 4 waves per (sequence, kv head, head tile, chunk of
+// tokens).
+//   prologue: the first superblock's loads go out, then the work-group rotates its query heads
+//             (v_mfma_f32_16x16x32_f16, A = the sign-flipped fp16 query, B = 16 Q split into
+//             fp16 hi + lo, generated from an LDS table of 2d entries) and splits every rotated
+//             channel into a 16-bit integer (two int8 digits, per-head step sigma) laid out as
+//             the A operand of the score MFMA.
+//   main loop: each wave walks 64-token superblocks:
 //     scores : v_mfma_i32_16x16x64_i8.  A rows are (head, group) pairs holding the query digits
 //              of one group of 16 channels (block diagonal); B is the packed K codes widened to
 //              bytes (x16 for int4: one shift and one mask per 8 codes, no unpacking).  The exact
@@ -21,11 +22,9 @@
 //              are staged in LDS and read with ds_read_b64_tr_b4 so that every lane holds 16
 //              tokens of one channel; B = code * scale split exactly into fp16 hi + lo,
 //              A = p split into fp16 hi + lo (three products per tile, fp32 accumulation).
-//   The work-group merges its waves and writes a chunk partial.
-//   merge_kernel : one work-group per (unit, head) merges the chunks, applies lambda_V and the
-//                  inverse rotation, and writes the output.  (Merging inside the main kernel
-//                  would need device-scope release/acquire fences per work-group, which on this
-//                  chip write back and invalidate the whole L2 of the XCD.)
+//   epilogue: the work-group merges its waves and stores a chunk partial; the last work-group
+//             of the unit to finish merges the chunks, applies lambda_V and the inverse rotation
+//             and writes the output.
 #include <algorithm>
 
 #include "kvq_decode_common.h"
@@ -37,9 +36,6 @@ using namespace dec;
 
 constexpr int kSB = 64;  // tokens per wave superblock
 
-// ------------------------------------------------------------------------------------------
-// Prologue: query digits.
-// ------------------------------------------------------------------------------------------
 // Channel held by byte b (0..15) of the widened K codes of one group.
 template <int KB>
 __host__ __device__ constexpr int kbyte_channel(int b) {
@@ -47,131 +43,11 @@ __host__ __device__ constexpr int kbyte_channel(int b) {
   return KB == 8 ? b : ((b >> 2) & 2 ? 8 : 0) + 2 * (b & 3) + ((b >> 2) & 1);
 }
 
-template <int D, int KB>
-__global__ __launch_bounds__(kThreads) void qprep_kernel(const uint16_t* __restrict__ q, int q_heads, int kv_heads,
-                                                         int head_tile, int head_tiles,
-                                                         const float* __restrict__ sign, int64_t sign_bs,
-                                                         const float* __restrict__ lambda, int64_t lambda_bs,
-                                                         float scale, uint4* __restrict__ qdig,
-                                                         float* __restrict__ qsig) {
-  constexpr int NS = D / 64;
-  constexpr int NB = D / 16, NSTEP = D / 32;
-  __shared__ float qh[16][D];  // rotated, scaled query
-  __shared__ float sig[16];
-  const int unit = blockIdx.x;
-  const int ht = unit % head_tiles;
-  const int bk = unit / head_tiles;
-  const int kvh = bk % kv_heads;
-  const int b = bk / kv_heads;
-  const int G = q_heads / kv_heads;
-  const int h0 = kvh * G + ht * head_tile;
-  const int GT = head_tile;
-  const int nrb = (GT + 3) / 4;
-  // q_hat[h][c] = sum_n Q[c][n] s_n q[h][n] * lambda_c * scale as MFMAs: A = the fp16 query
-  // (exact, signs flipped in the fp16 bits), B = the forward table (16 Q as fp16 hi + lo).
-  // Every global load of the wave is issued before the first MFMA.
-  {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int n16 = lane & 15, r4 = lane >> 4;
-    constexpr int NBW = NB / kWaves;  // channel blocks per wave
-    const MfmaQTable<D>& T = mqtable<D>();
-    uint4 bh[NBW][NSTEP], bl[NBW][NSTEP];
-#pragma unroll
-    for (int j = 0; j < NBW; ++j)
-#pragma unroll
-      for (int s = 0; s < NSTEP; ++s) {
-        bh[j][s] = ld4(T.fwd_hi[w + kWaves * j][s][lane]);
-        bl[j][s] = ld4(T.fwd_lo[w + kWaves * j][s][lane]);
-      }
-    float lam[NBW];
-#pragma unroll
-    for (int j = 0; j < NBW; ++j)
-      lam[j] = (lambda ? lambda[b * lambda_bs + int64_t(kvh) * D + 16 * (w + kWaves * j) + n16] : 1.0f) * scale *
-               0.0625f;
-    v8h aq[NSTEP];
-#pragma unroll
-    for (int s = 0; s < NSTEP; ++s) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (n16 < GT) {
-        v = *reinterpret_cast<const uint4*>(q + (int64_t(b) * q_heads + h0 + n16) * D + 32 * s + 8 * r4);
-        const float4 s0 = *reinterpret_cast<const float4*>(sign + b * sign_bs + 32 * s + 8 * r4);
-        const float4 s1 = *reinterpret_cast<const float4*>(sign + b * sign_bs + 32 * s + 8 * r4 + 4);
-        v.x ^= (s0.x < 0.0f ? 0x8000u : 0u) | (s0.y < 0.0f ? 0x80000000u : 0u);
-        v.y ^= (s0.z < 0.0f ? 0x8000u : 0u) | (s0.w < 0.0f ? 0x80000000u : 0u);
-        v.z ^= (s1.x < 0.0f ? 0x8000u : 0u) | (s1.y < 0.0f ? 0x80000000u : 0u);
-        v.w ^= (s1.z < 0.0f ? 0x8000u : 0u) | (s1.w < 0.0f ? 0x80000000u : 0u);
-      }
-      aq[s] = as_v8h(v.x, v.y, v.z, v.w);
-    }
-#pragma unroll
-    for (int j = 0; j < NBW; ++j) {
-      v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int s = 0; s < NSTEP; ++s) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], as_v8h(bh[j][s].x, bh[j][s].y, bh[j][s].z, bh[j][s].w),
-                                                     acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], as_v8h(bl[j][s].x, bl[j][s].y, bl[j][s].z, bl[j][s].w),
-                                                     acc, 0, 0, 0);
-      }
-      const int c = 16 * (w + kWaves * j) + n16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = 4 * r4 + i;
-        if (h < GT) qh[h][c] = acc[i] * lam[j];
-      }
-    }
-  }
-  __syncthreads();
-  // per-head step: the largest |q_hat| maps to 32639 so both digits fit int8 (wave h%4 reduces)
-  {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    for (int h = wv; h < 16; h += kWaves) {
-      float mx = 0.0f;
-      if (h < GT)
-        for (int c = lane; c < D; c += 64) mx = fmaxf(mx, fabsf(qh[h][c]));
-      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-      if (lane == 0) {
-        sig[h] = mx > 0.0f ? mx / 32639.0f : 1.0f;
-        // score multiplier: step, times 1/16 for int4 codes widened as 16*code
-        qsig[int64_t(unit) * 16 + h] = (h < GT ? sig[h] : 0.0f) * (KB == 4 ? 0.0625f : 1.0f);
-      }
-    }
-  }
-  __syncthreads();
-  // A operand of the score MFMA for (row block rb, step s, digit dg): lane l holds row
-  // r = l%16 = (head 4rb + r/4, slot j = r%4) and k bytes of lane group l/16; it is non-zero
-  // only when l/16 == j, where the 16 bytes are the digits of group g = j*NS + s.
-  const int total = nrb * NS * 2 * 64;
-  for (int i = threadIdx.x; i < total; i += kThreads) {
-    const int lane = i & 63;
-    const int blk = i >> 6;  // (rb * NS + s) * 2 + dg
-    const int dg = blk & 1;
-    const int s = (blk >> 1) % NS;
-    const int rb = (blk >> 1) / NS;
-    const int r = lane & 15, kg = lane >> 4;
-    const int h = 4 * rb + (r >> 2), j = r & 3;
-    uint32_t wv[4] = {0u, 0u, 0u, 0u};
-    if (kg == j && h < GT) {
-      const int g = j * NS + s;
-      const float inv = 1.0f / sig[h];
-#pragma unroll
-      for (int bt = 0; bt < 16; ++bt) {
-        const int c = 16 * g + kbyte_channel<KB>(bt);
-        int Q = static_cast<int>(rintf(qh[h][c] * inv));
-        Q = min(max(Q, -32639), 32639);
-        const int hi = (Q + 128) >> 8;
-        const int lo = Q - 256 * hi;
-        const int v = dg == 0 ? hi : lo;
-        wv[bt >> 2] |= (uint32_t(v) & 0xffu) << (8 * (bt & 3));
-      }
-    }
-    qdig[(int64_t(unit) * (total >> 6) + blk) * 64 + lane] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-  }
-}
-
 // ------------------------------------------------------------------------------------------
 // Main kernel.
 // ------------------------------------------------------------------------------------------
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
 template <int D, int KB>
 struct QGeom {
   static constexpr int NS = D / 64;             // score MFMA steps (64 channels each)
@@ -189,7 +65,9 @@ struct QGeom {
   static constexpr int LDS_P = 16 * kSB * 4;
   static constexpr int LDS_WAVE = LDS_V + LDS_S + LDS_K + LDS_P + 16 * 4;
   static constexpr int LDS_EPI = (kWaves * 16 * 2 + kWaves * (D == 128 ? 16 : 8) * D) * 4;
-  static constexpr int LDS = (kWaves * LDS_WAVE > LDS_EPI ? kWaves * LDS_WAVE : LDS_EPI);
+  static constexpr int LDS_Q = 16 * D * 4;  // rotated query of the prologue
+  static constexpr int LDS_M = merge_lds_floats<D>() * 4;
+  static constexpr int LDS = cmax(cmax(kWaves * LDS_WAVE, LDS_EPI), cmax(LDS_Q, LDS_M));
 };
 
 // Widen the int4 codes of one group (2 dwords, 16 codes) to the 16 int8 bytes 16*code.
@@ -199,13 +77,14 @@ __device__ __forceinline__ v4i widen_int4(uint32_t w0, uint32_t w1) {
 }
 
 // 8 nibbles (tokens r = 0..7 of one channel) -> 4 fp16 pairs of code values,
-// pairs hold tokens (0,4), (1,5), (2,6), (3,7).
-__device__ __forceinline__ void nibbles_to_half_pairs(uint32_t x, uint32_t (&p)[4]) {
+// pairs hold tokens (0,4), (1,5), (2,6), (3,7).  mask = 0x000f000f and magic = 0x64006400 come
+// in VGPRs so that the extraction is one v_and_or_b32 per pair (VOP3 takes no literals here).
+__device__ __forceinline__ void nibbles_to_half_pairs(uint32_t x, uint32_t mask, uint32_t magic, uint32_t (&p)[4]) {
   x ^= 0x88888888u;  // offset binary: nibble = code + 8
   const v2h off = {static_cast<_Float16>(-1032.0f), static_cast<_Float16>(-1032.0f)};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t t = ((x >> (4 * i)) & 0x000f000fu) | 0x64006400u;  // halves 1024 + code + 8
+    const uint32_t t = ((x >> (4 * i)) & mask) | magic;  // halves 1024 + code + 8
     const v2h c = __builtin_bit_cast(v2h, t) + off;
     p[i] = __builtin_bit_cast(uint32_t, c);
   }
@@ -417,6 +296,8 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB>& r, int base, i
                        as_v8h(alo[1][0], alo[1][1], alo[1][2], alo[1][3])};
 
   // ---------------- values (fp16 MFMA over LDS-transposed codes) ----------------
+  uint32_t nmask = 0x000f000fu, nmagic = 0x64006400u;
+  asm volatile("" : "+v"(nmask), "+v"(nmagic));
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     // lane r of each 16-lane group points at token 16*r4 + r, group g
@@ -428,7 +309,7 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB>& r, int base, i
 #pragma unroll
     for (int hblk = 0; hblk < 2; ++hblk) {
       uint32_t cp[4];
-      nibbles_to_half_pairs(uint32_t(hblk == 0 ? tr.x : tr.y), cp);
+      nibbles_to_half_pairs(uint32_t(hblk == 0 ? tr.x : tr.y), nmask, nmagic, cp);
       uint32_t bh[4], bl[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -450,37 +331,161 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB>& r, int base, i
   wave_sync_lds();
 }
 
+struct QDecodeParams {
+  const uint8_t* kc;
+  const uint16_t* ks;
+  const uint8_t* vc;
+  const uint16_t* vs;
+  const int32_t* seq_lens;
+  int seq_len, kv_heads, q_heads, capacity;
+  int head_tile, head_tiles, chunk, n_chunks, max_chunks;
+  const uint16_t* q;
+  const float* sign_k;
+  const float* lambda_k;
+  int64_t sign_bs, lambda_bs;
+  float score_scale;  // sm_scale * log2 e
+  uint32_t* counters;
+  float* pml;
+  float* pacc;
+  MergeArgs merge;
+};
+
 template <int D, int KB, int NRB>
-__global__ __launch_bounds__(kThreads) void decode_kernel(
-    const uint8_t* __restrict__ kc, const uint16_t* __restrict__ ks, const uint8_t* __restrict__ vc,
-    const uint16_t* __restrict__ vs, const int32_t* __restrict__ seq_lens, int seq_len, int kv_heads, int q_heads,
-    int capacity, int head_tile, int head_tiles, int chunk, int n_chunks, int max_chunks,
-    const uint4* __restrict__ qdig, const float* __restrict__ qsig, float* __restrict__ pml,
-    float* __restrict__ pacc) {
+__global__ __launch_bounds__(kThreads) void decode_kernel(const QDecodeParams P) {
   using Gm = QGeom<D, KB>;
   constexpr int NS = Gm::NS, NG = Gm::NG;
+  constexpr int NSTEP = D / 32, NBW = D / 16 / kWaves;
   __shared__ __align__(16) uint8_t smem[Gm::LDS];
+  __shared__ uint32_t tw[2 * D];
+  __shared__ float sig_s[16], msc_s[16];
+  __shared__ int last_flag;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int r4 = lane >> 4;
-  const int ch = blockIdx.x % n_chunks;
-  const int64_t unit = blockIdx.x / n_chunks;
-  const int ht = int(unit % head_tiles);
-  const int bk = int(unit / head_tiles);
-  const int kvh = bk % kv_heads;
-  const int b = bk / kv_heads;
-  (void)ht;
-  int L = seq_len;
-  if (seq_lens) L = min(max(seq_lens[b], 0), seq_len);
-  const int t_begin = ch * chunk;
-  const int t_end = min(L, t_begin + chunk);
-  const int64_t rowbase = (int64_t(b) * kv_heads + kvh) * capacity;
+  const int n16 = lane & 15, r4 = lane >> 4;
+  const int ch = blockIdx.x % P.n_chunks;
+  const int unit = blockIdx.x / P.n_chunks;
+  const int ht = unit % P.head_tiles;
+  const int bk = unit / P.head_tiles;
+  const int kvh = bk % P.kv_heads;
+  const int b = bk / P.kv_heads;
+  const int GT = P.head_tile;
+  const int h0 = kvh * (P.q_heads / P.kv_heads) + ht * GT;
+  int L = P.seq_len;
+  if (P.seq_lens) L = min(max(P.seq_lens[b], 0), P.seq_len);
+  const int t_begin = ch * P.chunk;
+  const int t_end = min(L, t_begin + P.chunk);
+  const int64_t rowbase = (int64_t(b) * P.kv_heads + kvh) * P.capacity;
   const int last_tok = max(L - 1, 0);
+  const uint8_t* __restrict__ kc = P.kc;
+  const uint16_t* __restrict__ ks = P.ks;
+  const uint8_t* __restrict__ vc = P.vc;
+  const uint16_t* __restrict__ vs = P.vs;
   constexpr int kStride = kWaves * kSB;
 
-  // first superblock's loads go out before anything else
+  // ---------------- prologue: rotated query -> int8 digit operands ----------------
+  // Its few loads go out first (loads complete in issue order), then the first superblock's.
+  uint32_t twv[2 * D / kThreads];
+  srft_pairs_fetch<D>(twv);
+  float lam[NBW];
+#pragma unroll
+  for (int j = 0; j < NBW; ++j)
+    lam[j] = (P.lambda_k ? P.lambda_k[b * P.lambda_bs + int64_t(kvh) * D + 16 * (w + kWaves * j) + n16] : 1.0f) *
+             P.score_scale * 0.0625f;
+  // A = the fp16 query of head row n16, signs flipped in the fp16 bits (exact)
+  uint4 qv[NSTEP];
+  float4 sv0[NSTEP], sv1[NSTEP];
+#pragma unroll
+  for (int s = 0; s < NSTEP; ++s) {
+    qv[s] = make_uint4(0u, 0u, 0u, 0u);
+    sv0[s] = sv1[s] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+    if (n16 < GT) {
+      qv[s] = *reinterpret_cast<const uint4*>(P.q + (int64_t(b) * P.q_heads + h0 + n16) * D + 32 * s + 8 * r4);
+      sv0[s] = *reinterpret_cast<const float4*>(P.sign_k + b * P.sign_bs + 32 * s + 8 * r4);
+      sv1[s] = *reinterpret_cast<const float4*>(P.sign_k + b * P.sign_bs + 32 * s + 8 * r4 + 4);
+    }
+  }
+
   SBRegs<D, KB> ra;
   int base = t_begin + w * kSB;
   if (base < t_end) load_superblock<D, KB>(ra, kc, ks, vc, vs, rowbase, base, last_tok, lane);
+
+  srft_pairs_store<D>(tw, twv);
+  v8h aq[NSTEP];
+#pragma unroll
+  for (int s = 0; s < NSTEP; ++s) {
+    uint4 v = qv[s];
+    const float4 s0 = sv0[s], s1 = sv1[s];
+    v.x ^= (s0.x < 0.0f ? 0x8000u : 0u) | (s0.y < 0.0f ? 0x80000000u : 0u);
+    v.y ^= (s0.z < 0.0f ? 0x8000u : 0u) | (s0.w < 0.0f ? 0x80000000u : 0u);
+    v.z ^= (s1.x < 0.0f ? 0x8000u : 0u) | (s1.y < 0.0f ? 0x80000000u : 0u);
+    v.w ^= (s1.z < 0.0f ? 0x8000u : 0u) | (s1.w < 0.0f ? 0x80000000u : 0u);
+    aq[s] = as_v8h(v.x, v.y, v.z, v.w);
+  }
+  __syncthreads();
+  // q_hat[h][c] * lambda_c * score_scale: wave w owns channel blocks w, w + 4, ...
+  float(*qh)[D] = reinterpret_cast<float(*)[D]>(smem);
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) {
+    v4f qa = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      v8h bh, bl;
+      srft_operand<D, false>(tw, w + kWaves * j, s, lane, bh, bl);
+      qa = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], bh, qa, 0, 0, 0);
+      qa = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], bl, qa, 0, 0, 0);
+    }
+    const int c = 16 * (w + kWaves * j) + n16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * r4 + i;
+      if (h < GT) qh[h][c] = qa[i] * lam[j];
+    }
+  }
+  __syncthreads();
+  // per-head step: the largest |q_hat| maps to 32639 so both digits fit int8
+  for (int h = w; h < 16; h += kWaves) {
+    float mx = 0.0f;
+    if (h < GT)
+      for (int c = lane; c < D; c += 64) mx = fmaxf(mx, fabsf(qh[h][c]));
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    if (lane == 0) {
+      const float sg = mx > 0.0f ? mx / 32639.0f : 1.0f;
+      sig_s[h] = sg;
+      // score multiplier: step, times 1/16 for int4 codes widened as 16*code
+      msc_s[h] = (h < GT ? sg : 0.0f) * (KB == 4 ? 0.0625f : 1.0f);
+    }
+  }
+  __syncthreads();
+  // A operand of the score MFMA for (row block rb, step s, digit): lane l holds row
+  // r = l%16 = (head 4rb + r/4, slot j = r%4) and the k bytes of lane group l/16; it is
+  // non-zero only when l/16 == j, where the 16 bytes are the digits of group g = j*NS + s.
+  v4i aop[NRB][NS][2];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int h = 4 * rb + (n16 >> 2), j = n16 & 3;
+      uint32_t wh[4] = {0u, 0u, 0u, 0u}, wl[4] = {0u, 0u, 0u, 0u};
+      if (r4 == j && h < GT) {
+        const int g = j * NS + s;
+        const float inv = 1.0f / sig_s[h];
+#pragma unroll
+        for (int bt = 0; bt < 16; ++bt) {
+          const int c = 16 * g + kbyte_channel<KB>(bt);
+          int Q = static_cast<int>(rintf(qh[h][c] * inv));
+          Q = min(max(Q, -32639), 32639);
+          const int hi = (Q + 128) >> 8;
+          const int lo = Q - 256 * hi;
+          wh[bt >> 2] |= (uint32_t(hi) & 0xffu) << (8 * (bt & 3));
+          wl[bt >> 2] |= (uint32_t(lo) & 0xffu) << (8 * (bt & 3));
+        }
+      }
+      aop[rb][s][0] = v4i{int(wh[0]), int(wh[1]), int(wh[2]), int(wh[3])};
+      aop[rb][s][1] = v4i{int(wl[0]), int(wl[1]), int(wl[2]), int(wl[3])};
+    }
+  float sig[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) sig[rb] = msc_s[4 * rb + r4];
+  __syncthreads();  // the main loop's tiles overwrite qh
 
   uint8_t* wbase = smem + w * Gm::LDS_WAVE;
   uint8_t* vtile = wbase;
@@ -488,21 +493,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   uint16_t* ktile = reinterpret_cast<uint16_t*>(wbase + Gm::LDS_V + Gm::LDS_S);
   float* ptile = reinterpret_cast<float*>(wbase + Gm::LDS_V + Gm::LDS_S + Gm::LDS_K);
   float* atile = reinterpret_cast<float*>(wbase + Gm::LDS_V + Gm::LDS_S + Gm::LDS_K + Gm::LDS_P);
-
-  // query digits (A operands) and per-head multipliers
-  v4i aop[NRB][NS][2];
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int dg = 0; dg < 2; ++dg) {
-        const uint4 v = qdig[(unit * (NRB * NS * 2) + (rb * NS + s) * 2 + dg) * 64 + lane];
-        aop[rb][s][dg] = v4i{int(v.x), int(v.y), int(v.z), int(v.w)};
-      }
-  float sig[NRB];
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) sig[rb] = qsig[unit * 16 + 4 * rb + r4];
 
   // P rows never produced by a score row block and alpha of such heads stay neutral
   for (int i = lane; i < 16 * kSB; i += 64) ptile[i] = 0.0f;
@@ -525,51 +515,67 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(
   }
 
   PartialArgs e;
-  e.head_tile = head_tile;
-  e.max_chunks = max_chunks;
+  e.head_tile = GT;
+  e.max_chunks = P.max_chunks;
   e.chunk_index = ch;
   e.unit = unit;
-  e.pml = pml;
-  e.pacc = pacc;
+  e.pml = P.pml;
+  e.pacc = P.pacc;
   store_partial<D, NRB>(m_run, l_run, acc, [](int k, int rr) { return 4 * k + rr; }, e,
                         reinterpret_cast<float*>(smem));
+  if (!arrive_last(P.counters + unit, P.n_chunks, &last_flag)) return;
+  merge_unit<D, true>(P.merge, unit, reinterpret_cast<float*>(smem), tw);
 }
 
 template <int D, int KB>
 hipError_t launch_q(const DecodeArgs& a, const DecodePlan& p, const WsLayout& w, hipStream_t s) {
   char* ws = static_cast<char*>(a.workspace);
-  auto* qdig = reinterpret_cast<uint4*>(ws + w.qdig);
-  auto* qsig = reinterpret_cast<float*>(ws + w.qsig);
-  auto* pml = reinterpret_cast<float*>(ws + w.pml);
-  auto* pacc = reinterpret_cast<float*>(ws + w.pacc);
   const int units = a.batch * a.kv_heads * p.head_tiles;
-  hipLaunchKernelGGL((qprep_kernel<D, KB>), dim3(units), dim3(kThreads), 0, s, static_cast<const uint16_t*>(a.q),
-                     a.q_heads, a.kv_heads, p.head_tile, p.head_tiles, a.sign_k, a.sign_bs, a.lambda_k, a.lambda_bs,
-                     a.sm_scale * kLog2e, qdig, qsig);
+  QDecodeParams P;
+  P.kc = static_cast<const uint8_t*>(a.k_codes);
+  P.ks = static_cast<const uint16_t*>(a.k_scales);
+  P.vc = static_cast<const uint8_t*>(a.v_codes);
+  P.vs = static_cast<const uint16_t*>(a.v_scales);
+  P.seq_lens = a.seq_lens;
+  P.seq_len = a.seq_len;
+  P.kv_heads = a.kv_heads;
+  P.q_heads = a.q_heads;
+  P.capacity = a.capacity;
+  P.head_tile = p.head_tile;
+  P.head_tiles = p.head_tiles;
+  P.chunk = p.chunk;
+  P.n_chunks = p.n_chunks;
+  P.max_chunks = p.max_chunks;
+  P.q = static_cast<const uint16_t*>(a.q);
+  P.sign_k = a.sign_k;
+  P.lambda_k = a.lambda_k;
+  P.sign_bs = a.sign_bs;
+  P.lambda_bs = a.lambda_bs;
+  P.score_scale = a.sm_scale * kLog2e;
+  P.counters = reinterpret_cast<uint32_t*>(ws + w.counters);
+  P.pml = reinterpret_cast<float*>(ws + w.pml);
+  P.pacc = reinterpret_cast<float*>(ws + w.pacc);
+  // code * scale was staged as code * scale / 16 in fp16: acc_scale 16 undoes it
+  P.merge = MergeArgs{P.pml,      P.pacc,     p.n_chunks, p.max_chunks, p.head_tile, p.head_tiles,
+                      a.q_heads,  a.kv_heads, 16.0f,      a.sign_v,     a.sign_bs,   a.lambda_v,
+                      a.lambda_bs, a.out};
   const dim3 grid(units * p.n_chunks), block(kThreads);
-  auto* kc = static_cast<const uint8_t*>(a.k_codes);
-  auto* ks = static_cast<const uint16_t*>(a.k_scales);
-  auto* vc = static_cast<const uint8_t*>(a.v_codes);
-  auto* vs = static_cast<const uint16_t*>(a.v_scales);
-#define KVQ_Q_CASE(NRBV)                                                                                         \
-  case NRBV:                                                                                                     \
-    hipLaunchKernelGGL((decode_kernel<D, KB, NRBV>), grid, block, 0, s, kc, ks, vc, vs, a.seq_lens, a.seq_len,   \
-                       a.kv_heads, a.q_heads, a.capacity, p.head_tile, p.head_tiles, p.chunk, p.n_chunks,        \
-                       p.max_chunks, qdig, qsig, pml, pacc);                                                     \
-    break;
   switch ((p.head_tile + 3) / 4) {
-    KVQ_Q_CASE(1)
-    KVQ_Q_CASE(2)
-    KVQ_Q_CASE(3)
-    KVQ_Q_CASE(4)
+    case 1:
+      hipLaunchKernelGGL((decode_kernel<D, KB, 1>), grid, block, 0, s, P);
+      break;
+    case 2:
+      hipLaunchKernelGGL((decode_kernel<D, KB, 2>), grid, block, 0, s, P);
+      break;
+    case 3:
+      hipLaunchKernelGGL((decode_kernel<D, KB, 3>), grid, block, 0, s, P);
+      break;
+    case 4:
+      hipLaunchKernelGGL((decode_kernel<D, KB, 4>), grid, block, 0, s, P);
+      break;
     default:
       return hipErrorInvalidValue;
   }
-#undef KVQ_Q_CASE
-  // code * scale was staged as code * scale / 16 in fp16: acc_scale 16 undoes it
-  hipLaunchKernelGGL((merge_kernel<D, true>), dim3(units), dim3(kThreads), 0, s, pml, pacc, p.n_chunks,
-                     p.max_chunks, p.head_tile, p.head_tiles, a.q_heads, a.kv_heads, 16.0f, a.sign_v, a.sign_bs,
-                     a.lambda_v, a.lambda_bs, a.out);
   return hipGetLastError();
 }
 

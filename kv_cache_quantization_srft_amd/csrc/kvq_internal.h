@@ -82,24 +82,25 @@ struct DecodeF16Args {
   float* out;
 };
 
-// Decode workspace: byte offsets of its regions.
+// Decode workspace.  The first kDecodeCounterBytes hold one completion counter per unit
+// (sequence, kv head, head tile); they must be zero before the first call and every call
+// leaves them zero.  Then the per-chunk partials (m, l) and acc[d].
+constexpr int kMaxDecodeUnits = 16384;
+constexpr size_t kDecodeCounterBytes = size_t(kMaxDecodeUnits) * sizeof(uint32_t);
+
 struct WsLayout {
-  size_t qdig;     // int8 query digits in MFMA A-operand order (quantized path)
-  size_t qsig;     // per-head score multiplier (quantized path)
-  size_t pml;      // per (unit, head, chunk): m, l
-  size_t pacc;     // per (unit, head, chunk): acc[d]
+  size_t counters;  // uint32 per unit
+  size_t pml;       // per (unit, head, chunk): m, l
+  size_t pacc;      // per (unit, head, chunk): acc[d]
   size_t total;
 };
 
 __host__ __device__ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 __host__ __device__ inline WsLayout ws_layout(int units, int head_tile, int head_dim, int max_chunks) {
-  const int nrb = (head_tile + 3) / 4;
-  const int ns = head_dim / 64;
   WsLayout w;
-  w.qdig = 0;
-  w.qsig = align256(size_t(units) * nrb * ns * 2 * 64 * 16);
-  w.pml = w.qsig + align256(size_t(units) * 16 * sizeof(float));
+  w.counters = 0;
+  w.pml = kDecodeCounterBytes;
   w.pacc = w.pml + align256(size_t(units) * head_tile * max_chunks * 2 * sizeof(float));
   w.total = w.pacc + align256(size_t(units) * head_tile * max_chunks * size_t(head_dim) * sizeof(float));
   return w;

@@ -104,7 +104,7 @@ def oracle_planes(x16, s, lam, bits):
 
 
 def gpu_decode(q16, kc8, ks16, vc8, vs16, k_bits, s_k, s_v, lam_k, lam_v, seq_len, seq_lens=None, sm_scale=0.0,
-               capacity=None, sign_bs=0, lambda_bs=0):
+               capacity=None, sign_bs=0, lambda_bs=0, ws=None):
     """Run kvq_decode_attn on given unpacked int8 codes (packed here by the oracle's packing)."""
     B, Hkv, S, d = kc8.shape
     Hq = q16.shape[1]
@@ -112,7 +112,8 @@ def gpu_decode(q16, kc8, ks16, vc8, vs16, k_bits, s_k, s_v, lam_k, lam_v, seq_le
     lay = kvq.make_layout(B, Hkv, Hq, d, cap, k_bits=k_bits, v_bits=4)
     kb = O.pack_codes(kc8, k_bits)
     vb = O.pack_codes(vc8, 4)
-    ws = torch.empty(kvq.kvq_decode_attn_workspace_bytes(lay, seq_len), dtype=torch.uint8, device="cuda")
+    if ws is None:
+        ws = torch.zeros(kvq.kvq_decode_attn_workspace_bytes(lay, seq_len), dtype=torch.uint8, device="cuda")
     out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
     lk = None if lam_k is None else dev(np.asarray(lam_k, np.float32))
     lv = None if lam_v is None else dev(np.asarray(lam_v, np.float32))
@@ -124,11 +125,12 @@ def gpu_decode(q16, kc8, ks16, vc8, vs16, k_bits, s_k, s_v, lam_k, lam_v, seq_le
     return out.cpu().numpy().astype(np.float64)
 
 
-def gpu_decode_fp16(q16, k16, v16, seq_len, seq_lens=None, sm_scale=0.0):
+def gpu_decode_fp16(q16, k16, v16, seq_len, seq_lens=None, sm_scale=0.0, ws=None):
     B, Hkv, S, d = k16.shape
     Hq = q16.shape[1]
     lay = kvq.make_layout(B, Hkv, Hq, d, S)
-    ws = torch.empty(kvq.kvq_decode_attn_workspace_bytes(lay, seq_len), dtype=torch.uint8, device="cuda")
+    if ws is None:
+        ws = torch.zeros(kvq.kvq_decode_attn_workspace_bytes(lay, seq_len), dtype=torch.uint8, device="cuda")
     out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
     sl = None if seq_lens is None else dev(np.asarray(seq_lens, np.int32))
     kvq.kvq_decode_attn_fp16(lay, dev(q16), dev(k16), dev(v16), seq_len, sl, sm_scale, ws, out)

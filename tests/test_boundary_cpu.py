@@ -143,6 +143,8 @@ def decode(L, lay, q=GOOD, seq_len=16, seq_lens=NULL, sm=0.0, ws=GOOD, ws_bytes=
     (dict(sm=float("nan")), 1, "sm_scale"),
     (dict(kc=MIS), 3, "k_codes"),
     (dict(seq_lens=P((1 << 20) + 2)), 3, "seq_lens"),
+    (dict(lay=dict(batch=16385)), 2, "exceeds 16384"),
+    (dict(lay=dict(batch=2049, kv_heads=2, q_heads=16 * 2 * 4)), 2, "exceeds 16384"),
 ])
 def test_decode_validation(L, kw, status, needle):
     lay = layout(**kw.pop("lay", {}))

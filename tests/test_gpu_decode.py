@@ -127,3 +127,30 @@ def test_fp16_decode(d, G):
     got = gpu_decode_fp16(q, k, v, S, seq_lens=[S, 17])
     ref = O.decode_attention(q, k, v, [S, 17])
     assert np.abs(got - ref).max() <= ATTN_ATOL
+
+
+def test_shared_workspace_across_shapes():
+    """One workspace, zeroed once, serves a sequence of quantized and fp16 calls of different
+    shapes (unit and chunk counts change between calls); every call matches the oracle and the
+    completion counters are back at zero afterwards (the workspace contract of the C ABI)."""
+    import torch
+    from kv_cache_quantization_srft_amd import kvq
+
+    rng = np.random.default_rng(31)
+    lay_big = kvq.make_layout(6, 4, 24, 256, 3000, k_bits=8, v_bits=4)
+    ws = torch.zeros(kvq.kvq_decode_attn_workspace_bytes(lay_big, 3000), dtype=torch.uint8, device="cuda")
+    shapes = [(2, 2, 6, 1200, 128, 4), (6, 4, 3, 3000, 128, 4), (1, 1, 4, 700, 256, 8), (2, 2, 6, 1200, 128, 4),
+              (5, 3, 2, 2100, 128, 8)]
+    for i, (B, Hkv, G, S, d, kb) in enumerate(shapes):
+        q, k, v, sk, sv, lk, lv = _case(rng, B, Hkv, G, S, d, kb)
+        kc, ks = O.quantize(k, sk, lk[:, :, None, :], kb)
+        vc, vs = O.quantize(v, sv, lv[:, :, None, :], 4)
+        say("shared workspace", i, (B, Hkv, G, S, d, kb))
+        got = gpu_decode(q, kc, ks, vc, vs, kb, sk, sv, lk, lv, S, lambda_bs=Hkv * d, ws=ws)
+        ref = O.decode_attention_quantized(q, kc, ks, vc, vs, sk, sv, lk[:, :, None, :], lv[:, :, None, :], S)
+        assert np.abs(got - ref).max() <= ATTN_ATOL, f"call {i}"
+        assert int(ws[:65536].count_nonzero()) == 0, f"counters not reset after call {i}"
+        if i % 2 == 0:
+            got16 = gpu_decode_fp16(q, k, v, S, ws=ws)
+            assert np.abs(got16 - O.decode_attention(q, k, v, S)).max() <= ATTN_ATOL, f"fp16 call {i}"
+            assert int(ws[:65536].count_nonzero()) == 0, f"counters not reset after fp16 call {i}"
