@@ -43,6 +43,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=0, help="timed steps (default: 4 x the cache copies)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--seq", type=int, default=0, help="override the workload's sequence length (a sweep point)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     return ap.parse_args()
@@ -146,6 +147,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = synth.WORKLOADS[args.workload]
+    if args.seq > 0:
+        import dataclasses
+        w = dataclasses.replace(w, seq_len=args.seq)
     L, B, H, Hq, d, S = w.layers, w.batch, w.kv_heads, w.q_heads, w.head_dim, w.seq_len
     LB = L * B
     log(f"workload {w.name}: layers {L} batch {B} kv {H} q {Hq} d {d} seq {S} K{w.k_bits}V{w.v_bits}")

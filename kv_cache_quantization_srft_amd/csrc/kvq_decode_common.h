@@ -225,9 +225,28 @@ __device__ __forceinline__ float row_sum16(float v) {
   return v;
 }
 
+// max / sum over the whole wave: 16-lane rows by DPP, then the four row results by readlane
+// (wave-uniform result)
+__device__ __forceinline__ float wave_max(float v) {
+  v = row_max16(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum16(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 __device__ __forceinline__ float exp2_guard(float a, float m) {
-  // exp2(a - m) with the empty case (a = -inf) mapped to 0
-  return a == -INFINITY ? 0.0f : exp2f(a - m);
+  // exp2(a - m) (v_exp_f32) with the empty case (a = -inf) mapped to 0
+  return a == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(a - m);
 }
 
 // Position of token r (0..15) of a 16-token lane group inside the k order used by the value
@@ -236,13 +255,14 @@ __host__ __device__ constexpr int kpos16(int r) {
   return (r < 8 ? 0 : 8) + ((r & 7) < 4 ? 2 * (r & 7) : 2 * ((r & 7) - 4) + 1);
 }
 
-// fp32 -> fp16 hi + lo, packed in pairs: x ~= hi + lo to ~2^-22 relative.
+// fp32 -> fp16 hi + lo, packed in pairs: x ~= hi + lo to ~2^-21 relative (while lo stays a
+// normal fp16).  Both halves are truncations (v_cvt_pkrtz_f16_f32, two values per
+// instruction); the residual x - hi is exact in fp32.
 __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
-  const _Float16 ha = static_cast<_Float16>(a), hb = static_cast<_Float16>(b);
-  const _Float16 la = static_cast<_Float16>(a - static_cast<float>(ha));
-  const _Float16 lb = static_cast<_Float16>(b - static_cast<float>(hb));
-  hi = uint32_t(__builtin_bit_cast(uint16_t, ha)) | (uint32_t(__builtin_bit_cast(uint16_t, hb)) << 16);
-  lo = uint32_t(__builtin_bit_cast(uint16_t, la)) | (uint32_t(__builtin_bit_cast(uint16_t, lb)) << 16);
+  const auto h = __builtin_amdgcn_cvt_pkrtz(a, b);
+  const auto l = __builtin_amdgcn_cvt_pkrtz(a - static_cast<float>(h[0]), b - static_cast<float>(h[1]));
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
 }
 
 
@@ -279,9 +299,11 @@ __device__ __forceinline__ void store_partial(float (&m_run)[NSLOT], float (&l_r
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n16 = lane & 15, r4 = lane >> 4;
   const int GT = e.head_tile;
-  // smem: wml[4][16][2] | wacc[4][GT][D]  (aliases the main-loop tiles)
+  // smem: wml[4][16][2] | fw[16][4] | hml[16][2] | wacc[4][GT][D]  (aliases the main-loop tiles)
   float* wml = smem;
-  float* wacc = smem + kWaves * 16 * 2;
+  float* fw = smem + kWaves * 16 * 2;
+  float* hml = fw + 16 * kWaves;
+  float* wacc = hml + 16 * 2;
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < NSLOT; ++k) {
@@ -301,23 +323,46 @@ __device__ __forceinline__ void store_partial(float (&m_run)[NSLOT], float (&l_r
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < GT * D; idx += kThreads) {
-    const int h = idx / D, c = idx - h * D;
+  // per head: the work-group max M, the wave weights exp2(m_w - M) and l = sum_w l_w weight_w
+  if (threadIdx.x < 16) {
+    const int h = threadIdx.x;
     float mm = -INFINITY;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) mm = fmaxf(mm, wml[(ww * 16 + h) * 2]);
-    float a = 0.0f, ll = 0.0f;
+    float ll = 0.0f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
       const float f = exp2_guard(wml[(ww * 16 + h) * 2], mm);
-      a += wacc[(ww * GT + h) * D + c] * f;
+      fw[h * kWaves + ww] = f;
       ll += wml[(ww * 16 + h) * 2 + 1] * f;
     }
+    hml[2 * h] = mm;
+    hml[2 * h + 1] = ll;
+  }
+  __syncthreads();
+  // four consecutive channels of one head per thread
+  for (int q = threadIdx.x; q < GT * D / 4; q += kThreads) {
+    const int h = (4 * q) / D, c = 4 * q - h * D;
+    const float4 f = *reinterpret_cast<const float4*>(fw + h * kWaves);
+    const float fv[4] = {f.x, f.y, f.z, f.w};
+    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float4 v = *reinterpret_cast<const float4*>(wacc + (ww * GT + h) * D + c);
+      a.x = fmaf(v.x, fv[ww], a.x);
+      a.y = fmaf(v.y, fv[ww], a.y);
+      a.z = fmaf(v.z, fv[ww], a.z);
+      a.w = fmaf(v.w, fv[ww], a.w);
+    }
     const int64_t prow = (e.unit * GT + h) * e.max_chunks + e.chunk_index;
-    st_dev(&e.pacc[prow * D + c], a);
+    float* dst = e.pacc + prow * D + c;
+    st_dev(dst, a.x);
+    st_dev(dst + 1, a.y);
+    st_dev(dst + 2, a.z);
+    st_dev(dst + 3, a.w);
     if (c == 0) {
-      st_dev(&e.pml[2 * prow], mm);
-      st_dev(&e.pml[2 * prow + 1], ll);
+      st_dev(&e.pml[2 * prow], hml[2 * h]);
+      st_dev(&e.pml[2 * prow + 1], hml[2 * h + 1]);
     }
   }
 }
@@ -404,9 +449,22 @@ __device__ __forceinline__ void merge_unit(const MergeArgs& a, int unit, float* 
     }
   }
   float psg[ROT ? NBW : 1];
+  // d = 128: the inverse-rotation operands come from the global table (d = 256: generated)
+  constexpr bool kTab = ROT && D == 128;
+  uint4 pbh[kTab ? NBW : 1][NSTEP], pbl[kTab ? NBW : 1][NSTEP];
   if constexpr (ROT) {
 #pragma unroll
     for (int j = 0; j < NBW; ++j) psg[j] = a.sign[b * a.sign_bs + 16 * (w + kWaves * j) + (lane & 15)];
+  }
+  if constexpr (kTab) {
+    const MfmaQTable<D>& T = mqtable<D>();
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s) {
+        pbh[j][s] = ld4(T.inv_hi[w + kWaves * j][s][lane]);
+        pbl[j][s] = ld4(T.inv_lo[w + kWaves * j][s][lane]);
+      }
   }
   // per-head chunk weights exp2(m_i - M) and 1/l, one wave per head
   for (int h = w; h < GT; h += kWaves) {
@@ -420,7 +478,7 @@ __device__ __forceinline__ void merge_unit(const MergeArgs& a, int unit, float* 
     }
     float mm = fmaxf(mv[0], mv[1]);
     for (int i = lane + 128; i < n_chunks; i += 64) mm = fmaxf(mm, ld_dev(&ml[2 * i]));
-    for (int off = 32; off > 0; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off));
+    mm = wave_max(mm);
     float ll = 0.0f;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
@@ -430,7 +488,7 @@ __device__ __forceinline__ void merge_unit(const MergeArgs& a, int unit, float* 
       if (i < MAXC) wgt[h][i] = f;
     }
     for (int i = lane + 128; i < n_chunks; i += 64) ll += ld_dev(&ml[2 * i + 1]) * exp2_guard(ld_dev(&ml[2 * i]), mm);
-    for (int off = 32; off > 0; off >>= 1) ll += __shfl_xor(ll, off);
+    ll = wave_sum(ll);
     if (lane == 0) {
       linv[h] = ll > 0.0f ? a.acc_scale / ll : 0.0f;
       mmax[h] = mm;
@@ -485,7 +543,12 @@ __device__ __forceinline__ void merge_unit(const MergeArgs& a, int unit, float* 
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s) {
         v8h bhi, blo;
-        srft_operand<D, true>(tw, nb, s, lane, bhi, blo);
+        if constexpr (kTab) {
+          bhi = as_v8h(pbh[j][s].x, pbh[j][s].y, pbh[j][s].z, pbh[j][s].w);
+          blo = as_v8h(pbl[j][s].x, pbl[j][s].y, pbl[j][s].z, pbl[j][s].w);
+        } else {
+          srft_operand<D, true>(tw, nb, s, lane, bhi, blo);
+        }
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[s], bhi, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[s], blo, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[s], bhi, acc, 0, 0, 0);

@@ -29,7 +29,7 @@ struct FGeom {
   static constexpr int LDS_V = kSB16 * ROWB;
   static constexpr int LDS_P = 16 * kSB16 * 4;
   static constexpr int LDS_WAVE = LDS_V + LDS_P + 16 * 4;
-  static constexpr int LDS_EPI = (kWaves * 16 * 2 + kWaves * (D == 128 ? 16 : 8) * D) * 4;
+  static constexpr int LDS_EPI = (kWaves * 16 * 2 + 16 * kWaves + 32 + kWaves * (D == 128 ? 16 : 8) * D) * 4;
   static constexpr int LDS_M = merge_lds_floats<D>() * 4;
   static constexpr int LDS_A = kWaves * LDS_WAVE > LDS_EPI ? kWaves * LDS_WAVE : LDS_EPI;
   static constexpr int LDS = LDS_A > LDS_M ? LDS_A : LDS_M;

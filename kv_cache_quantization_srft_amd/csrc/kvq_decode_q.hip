@@ -64,8 +64,8 @@ struct QGeom {
   static constexpr int LDS_K = kSB * NG * 2;
   static constexpr int LDS_P = 16 * kSB * 4;
   static constexpr int LDS_WAVE = LDS_V + LDS_S + LDS_K + LDS_P + 16 * 4;
-  static constexpr int LDS_EPI = (kWaves * 16 * 2 + kWaves * (D == 128 ? 16 : 8) * D) * 4;
-  static constexpr int LDS_Q = 16 * D * 4;  // rotated query of the prologue
+  static constexpr int LDS_EPI = (kWaves * 16 * 2 + 16 * kWaves + 32 + kWaves * (D == 128 ? 16 : 8) * D) * 4;
+  static constexpr int LDS_Q = 4 * NS * 2 * 1024 + 256;  // prologue: digit operands + head maxima
   static constexpr int LDS_M = merge_lds_floats<D>() * 4;
   static constexpr int LDS = cmax(cmax(kWaves * LDS_WAVE, LDS_EPI), cmax(LDS_Q, LDS_M));
 };
@@ -100,56 +100,61 @@ struct SBRegs {
   uint32_t vsw[Gm::SLW];    // V scales of token base + lane
 };
 
+// Buffer resource over the bytes [p, p + n) (raw buffer, stride 0): loads at offsets >= n
+// return 0, so tokens past the sequence end need no clamping.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, int off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Loads of the superblock starting at token `base` (wave-uniform) of one (sequence, kv head)
+// row; L = the row's token count.  The resources start at the superblock, so every lane offset
+// is a constant and the address arithmetic is scalar.
 template <int D, int KB>
 __device__ __forceinline__ void load_superblock(SBRegs<D, KB>& r, const uint8_t* __restrict__ kc,
                                                 const uint16_t* __restrict__ ks, const uint8_t* __restrict__ vc,
-                                                const uint16_t* __restrict__ vs, int64_t rowbase, int base,
-                                                int last_tok, int lane) {
+                                                const uint16_t* __restrict__ vs, int64_t rowbase, int base, int L,
+                                                int lane) {
   using Gm = QGeom<D, KB>;
   const int n16 = lane & 15, r4 = lane >> 4;
+  const int nrem = L - base;
+  const int64_t t0 = rowbase + base;
+  const __amdgpu_buffer_rsrc_t rk = row_rsrc(kc + t0 * Gm::KRB, nrem * Gm::KRB);
+  const __amdgpu_buffer_rsrc_t rks = row_rsrc(ks + t0 * Gm::NG, nrem * Gm::NG * 2);
+  const __amdgpu_buffer_rsrc_t rv = row_rsrc(vc + t0 * Gm::VRB, nrem * Gm::VRB);
+  const __amdgpu_buffer_rsrc_t rvs = row_rsrc(vs + t0 * Gm::NG, nrem * Gm::NG * 2);
 #pragma unroll
   for (int sb = 0; sb < 4; ++sb) {
-    const int t = min(base + 16 * sb + n16, last_tok);
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(kc + (rowbase + t) * Gm::KRB + r4 * Gm::KLB);
 #pragma unroll
     for (int i = 0; i < Gm::KLW; i += 4) {
-      const uint4 v = *reinterpret_cast<const uint4*>(src + i);
+      const uint4 v = buf_ld16(rk, (16 * sb + n16) * Gm::KRB + r4 * Gm::KLB + 4 * i);
       r.kw[sb][i] = v.x;
       r.kw[sb][i + 1] = v.y;
       r.kw[sb][i + 2] = v.z;
       r.kw[sb][i + 3] = v.w;
     }
   }
-  const int tl = min(base + lane, last_tok);
-  {
-    const uint32_t* s = reinterpret_cast<const uint32_t*>(ks + (rowbase + tl) * Gm::NG);
 #pragma unroll
-    for (int i = 0; i < Gm::SLW; i += 4) {
-      const uint4 v = *reinterpret_cast<const uint4*>(s + i);
-      r.ksw[i] = v.x;
-      r.ksw[i + 1] = v.y;
-      r.ksw[i + 2] = v.z;
-      r.ksw[i + 3] = v.w;
-    }
+  for (int i = 0; i < Gm::SLW; i += 4) {
+    const uint4 v = buf_ld16(rks, lane * Gm::NG * 2 + 4 * i);
+    r.ksw[i] = v.x;
+    r.ksw[i + 1] = v.y;
+    r.ksw[i + 2] = v.z;
+    r.ksw[i + 3] = v.w;
   }
 #pragma unroll
-  for (int i = 0; i < Gm::VLU; ++i) {
-    const int f = i * 64 + lane;  // 16-byte unit index in the superblock
-    const int tk = f / (Gm::VRB / 16);
-    const int piece = f - tk * (Gm::VRB / 16);
-    const int t = min(base + tk, last_tok);
-    r.vw[i] = *reinterpret_cast<const uint4*>(vc + (rowbase + t) * Gm::VRB + piece * 16);
-  }
-  {
-    const uint32_t* s = reinterpret_cast<const uint32_t*>(vs + (rowbase + tl) * Gm::NG);
+  for (int i = 0; i < Gm::VLU; ++i) r.vw[i] = buf_ld16(rv, (i * 64 + lane) * 16);  // token-major, contiguous
 #pragma unroll
-    for (int i = 0; i < Gm::SLW; i += 4) {
-      const uint4 v = *reinterpret_cast<const uint4*>(s + i);
-      r.vsw[i] = v.x;
-      r.vsw[i + 1] = v.y;
-      r.vsw[i + 2] = v.z;
-      r.vsw[i + 3] = v.w;
-    }
+  for (int i = 0; i < Gm::SLW; i += 4) {
+    const uint4 v = buf_ld16(rvs, lane * Gm::NG * 2 + 4 * i);
+    r.vsw[i] = v.x;
+    r.vsw[i + 1] = v.y;
+    r.vsw[i + 2] = v.z;
+    r.vsw[i + 3] = v.w;
   }
 }
 
@@ -168,7 +173,7 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB>& r, int base, i
                                                    float* atile, const uint8_t* __restrict__ kc,
                                                    const uint16_t* __restrict__ ks, const uint8_t* __restrict__ vc,
                                                    const uint16_t* __restrict__ vs, int64_t rowbase, int next_base,
-                                                   int last_tok) {
+                                                   int L) {
   using Gm = QGeom<D, KB>;
   constexpr int NS = Gm::NS, NG = Gm::NG;
   const int n16 = lane & 15, r4 = lane >> 4;
@@ -218,10 +223,8 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB>& r, int base, i
         kraw[i + 3] = v.w;
       }
     }
-    float ksf[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g)
-      ksf[g] = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t((kraw[g >> 1] >> (16 * (g & 1))) & 0xffffu)));
+    // the fp16 group scales stay packed; the FMA takes them as fp16 operands (v_fma_mix_f32)
+    const v2h* ksp = reinterpret_cast<const v2h*>(kraw);
     const bool valid = base + 16 * sb + n16 < t_end;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
@@ -234,7 +237,7 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB>& r, int base, i
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int dot = chi[i] * 256 + clo[i];
-          s_acc = fmaf(static_cast<float>(dot), ksf[i * NS + s], s_acc);
+          s_acc = fmaf(static_cast<float>(dot), static_cast<float>(ksp[(i * NS + s) >> 1][(i * NS + s) & 1]), s_acc);
         }
       }
       sc[sb][rb] = valid ? s_acc * sig[rb] : -INFINITY;
@@ -242,7 +245,7 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB>& r, int base, i
   }
 
   // the registers of this superblock are consumed: the next one loads during softmax + values
-  if (next_base < t_end) load_superblock<D, KB>(r, kc, ks, vc, vs, rowbase, next_base, last_tok, lane);
+  if (next_base < t_end) load_superblock<D, KB>(r, kc, ks, vc, vs, rowbase, next_base, L, lane);
 
   // ---------------- online softmax per head (16-lane rows) ----------------
   bool rescale = false;
@@ -357,9 +360,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const QDecodeParams P)
   constexpr int NSTEP = D / 32, NBW = D / 16 / kWaves;
   __shared__ __align__(16) uint8_t smem[Gm::LDS];
   __shared__ uint32_t tw[2 * D];
-  __shared__ float sig_s[16], msc_s[16];
   __shared__ int last_flag;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index (uniform)
   const int n16 = lane & 15, r4 = lane >> 4;
   const int ch = blockIdx.x % P.n_chunks;
   const int unit = blockIdx.x / P.n_chunks;
@@ -374,7 +377,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const QDecodeParams P)
   const int t_begin = ch * P.chunk;
   const int t_end = min(L, t_begin + P.chunk);
   const int64_t rowbase = (int64_t(b) * P.kv_heads + kvh) * P.capacity;
-  const int last_tok = max(L - 1, 0);
   const uint8_t* __restrict__ kc = P.kc;
   const uint16_t* __restrict__ ks = P.ks;
   const uint8_t* __restrict__ vc = P.vc;
@@ -383,8 +385,23 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const QDecodeParams P)
 
   // ---------------- prologue: rotated query -> int8 digit operands ----------------
   // Its few loads go out first (loads complete in issue order), then the first superblock's.
-  uint32_t twv[2 * D / kThreads];
-  srft_pairs_fetch<D>(twv);
+  // d = 128: the B operands of this wave's channel blocks come from the global forward table
+  // (16 Q as fp16 hi + lo in operand order); d = 256: they are generated from the LDS pair table.
+  constexpr bool kTab = D == 128;
+  uint4 tbh[kTab ? NBW : 1][NSTEP], tbl[kTab ? NBW : 1][NSTEP];
+  uint32_t twv[kTab ? 1 : 2 * D / kThreads];
+  if constexpr (kTab) {
+    const MfmaQTable<D>& T = mqtable<D>();
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s) {
+        tbh[j][s] = ld4(T.fwd_hi[w + kWaves * j][s][lane]);
+        tbl[j][s] = ld4(T.fwd_lo[w + kWaves * j][s][lane]);
+      }
+  } else {
+    srft_pairs_fetch<D>(twv);
+  }
   float lam[NBW];
 #pragma unroll
   for (int j = 0; j < NBW; ++j)
@@ -406,9 +423,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const QDecodeParams P)
 
   SBRegs<D, KB> ra;
   int base = t_begin + w * kSB;
-  if (base < t_end) load_superblock<D, KB>(ra, kc, ks, vc, vs, rowbase, base, last_tok, lane);
+  if (base < t_end) load_superblock<D, KB>(ra, kc, ks, vc, vs, rowbase, base, L, lane);
 
-  srft_pairs_store<D>(tw, twv);
+  // LDS of the prologue (aliases the main-loop tiles): digit operands, per-wave head maxima
+  constexpr int kDigBytes = NRB * NS * 2 * 1024;
+  uint8_t* dig = smem;
+  float* pmax = reinterpret_cast<float*>(smem + kDigBytes);  // [kWaves][16]
+  for (int i = threadIdx.x; i < kDigBytes / 16; i += kThreads)
+    reinterpret_cast<uint4*>(dig)[i] = make_uint4(0u, 0u, 0u, 0u);
+  if constexpr (!kTab) srft_pairs_store<D>(tw, twv);
   v8h aq[NSTEP];
 #pragma unroll
   for (int s = 0; s < NSTEP; ++s) {
@@ -421,71 +444,101 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const QDecodeParams P)
     aq[s] = as_v8h(v.x, v.y, v.z, v.w);
   }
   __syncthreads();
-  // q_hat[h][c] * lambda_c * score_scale: wave w owns channel blocks w, w + 4, ...
-  float(*qh)[D] = reinterpret_cast<float(*)[D]>(smem);
+  // q_hat[h][c] * lambda_c * score_scale for head h = 4 r4 + i and channel c = 16 (w + 4j) + n16
+  float qv_[NBW][4];
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
     v4f qa = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       v8h bh, bl;
-      srft_operand<D, false>(tw, w + kWaves * j, s, lane, bh, bl);
+      if constexpr (kTab) {
+        bh = as_v8h(tbh[j][s].x, tbh[j][s].y, tbh[j][s].z, tbh[j][s].w);
+        bl = as_v8h(tbl[j][s].x, tbl[j][s].y, tbl[j][s].z, tbl[j][s].w);
+      } else {
+        srft_operand<D, false>(tw, w + kWaves * j, s, lane, bh, bl);
+      }
       qa = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], bh, qa, 0, 0, 0);
       qa = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], bl, qa, 0, 0, 0);
     }
-    const int c = 16 * (w + kWaves * j) + n16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * r4 + i;
-      if (h < GT) qh[h][c] = qa[i] * lam[j];
-    }
+    for (int i = 0; i < 4; ++i) qv_[j][i] = qa[i] * lam[j];
+  }
+  // per-head maximum of |q_hat| over this wave's channels (16-lane DPP rows), then over waves
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) m = fmaxf(m, fabsf(qv_[j][i]));
+    m = row_max16(m);
+    if (n16 == 0) pmax[w * 16 + 4 * r4 + i] = m;
   }
   __syncthreads();
   // per-head step: the largest |q_hat| maps to 32639 so both digits fit int8
-  for (int h = w; h < 16; h += kWaves) {
-    float mx = 0.0f;
-    if (h < GT)
-      for (int c = lane; c < D; c += 64) mx = fmaxf(mx, fabsf(qh[h][c]));
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if (lane == 0) {
-      const float sg = mx > 0.0f ? mx / 32639.0f : 1.0f;
-      sig_s[h] = sg;
-      // score multiplier: step, times 1/16 for int4 codes widened as 16*code
-      msc_s[h] = (h < GT ? sg : 0.0f) * (KB == 4 ? 0.0625f : 1.0f);
+  float sgm[4];
+  {
+    float4 mx = *reinterpret_cast<const float4*>(pmax + 4 * r4);
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) {
+      const float4 o = *reinterpret_cast<const float4*>(pmax + ww * 16 + 4 * r4);
+      mx = make_float4(fmaxf(mx.x, o.x), fmaxf(mx.y, o.y), fmaxf(mx.z, o.z), fmaxf(mx.w, o.w));
+    }
+    const float m4[4] = {mx.x, mx.y, mx.z, mx.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sgm[i] = m4[i] > 0.0f ? m4[i] / 32639.0f : 1.0f;
+  }
+  // score multiplier of the rows this lane's scores belong to: heads 4 rb + r4
+  float sig[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    float mxh = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) mxh = fmaxf(mxh, pmax[ww * 16 + 4 * rb + r4]);
+    const float sg = mxh > 0.0f ? mxh / 32639.0f : 1.0f;
+    // step, times 1/16 for int4 codes widened as 16*code
+    sig[rb] = (4 * rb + r4 < GT ? sg : 0.0f) * (KB == 4 ? 0.0625f : 1.0f);
+  }
+  // the two int8 digits of every channel, scattered into the score MFMA's A operands: for
+  // (row block rb, step s, digit dg) lane l holds row r = l%16 = (head 4rb + r/4, slot r%4) and
+  // the k bytes of lane group l/16; it is non-zero only when l/16 == r%4, where the 16 bytes are
+  // the digits of group g = (r%4) NS + s
+  {
+    int bt_of_c = 0;  // byte of the widened K codes that holds channel n16 of a group
+#pragma unroll
+    for (int bt = 0; bt < 16; ++bt)
+      if (kbyte_channel<KB>(bt) == n16) bt_of_c = bt;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      const int g = w + kWaves * j;
+      const int slot = g / NS, s = g % NS;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = 4 * r4 + i;
+        if (h < GT) {
+          int Q = static_cast<int>(rintf(qv_[j][i] * (1.0f / sgm[i])));
+          Q = min(max(Q, -32639), 32639);
+          const int hi = (Q + 128) >> 8;
+          const int lo = Q - 256 * hi;
+          const int rb = h >> 2, row = (h & 3) * 4 + slot;
+          const int off = ((rb * NS + s) * 2) * 1024 + (row + 16 * slot) * 16 + bt_of_c;
+          dig[off] = uint8_t(hi & 0xff);
+          dig[off + 1024] = uint8_t(lo & 0xff);
+        }
+      }
     }
   }
   __syncthreads();
-  // A operand of the score MFMA for (row block rb, step s, digit): lane l holds row
-  // r = l%16 = (head 4rb + r/4, slot j = r%4) and the k bytes of lane group l/16; it is
-  // non-zero only when l/16 == j, where the 16 bytes are the digits of group g = j*NS + s.
   v4i aop[NRB][NS][2];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const int h = 4 * rb + (n16 >> 2), j = n16 & 3;
-      uint32_t wh[4] = {0u, 0u, 0u, 0u}, wl[4] = {0u, 0u, 0u, 0u};
-      if (r4 == j && h < GT) {
-        const int g = j * NS + s;
-        const float inv = 1.0f / sig_s[h];
+    for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int bt = 0; bt < 16; ++bt) {
-          const int c = 16 * g + kbyte_channel<KB>(bt);
-          int Q = static_cast<int>(rintf(qh[h][c] * inv));
-          Q = min(max(Q, -32639), 32639);
-          const int hi = (Q + 128) >> 8;
-          const int lo = Q - 256 * hi;
-          wh[bt >> 2] |= (uint32_t(hi) & 0xffu) << (8 * (bt & 3));
-          wl[bt >> 2] |= (uint32_t(lo) & 0xffu) << (8 * (bt & 3));
-        }
+      for (int dg = 0; dg < 2; ++dg) {
+        const uint4 v = *reinterpret_cast<const uint4*>(dig + ((rb * NS + s) * 2 + dg) * 1024 + lane * 16);
+        aop[rb][s][dg] = v4i{int(v.x), int(v.y), int(v.z), int(v.w)};
       }
-      aop[rb][s][0] = v4i{int(wh[0]), int(wh[1]), int(wh[2]), int(wh[3])};
-      aop[rb][s][1] = v4i{int(wl[0]), int(wl[1]), int(wl[2]), int(wl[3])};
-    }
-  float sig[NRB];
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) sig[rb] = msc_s[4 * rb + r4];
-  __syncthreads();  // the main loop's tiles overwrite qh
+  __syncthreads();  // the main loop's tiles overwrite the prologue's LDS
 
   uint8_t* wbase = smem + w * Gm::LDS_WAVE;
   uint8_t* vtile = wbase;
@@ -510,7 +563,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const QDecodeParams P)
 
   while (base < t_end) {
     process_superblock<D, KB, NRB>(ra, base, t_end, lane, aop, sig, m_run, l_run, acc, vtile, stile, ktile, ptile,
-                                   atile, kc, ks, vc, vs, rowbase, base + kStride, last_tok);
+                                   atile, kc, ks, vc, vs, rowbase, base + kStride, L);
     base += kStride;
   }
 
