@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 COLD_BYTES = 1 << 30
+MAX_COPIES = 256
 METRIC = "decode-attn effective KV GB/s & % HBM peak; quantize Mvectors/s; vs fp16-KV"
 
 
@@ -191,8 +192,10 @@ def main():
 
     q_bytes = sum(t.numel() * t.element_size() for t in base)
     f16_bytes = 2 * kx.numel() * 2
-    n_q = max(1, -(-COLD_BYTES // q_bytes))
-    n_f = max(1, -(-COLD_BYTES // f16_bytes))
+    # enough copies to span COLD_BYTES, at most MAX_COPIES (tiny caches are latency-bound anyway,
+    # and every copy is a node of the timing graph)
+    n_q = min(MAX_COPIES, max(1, -(-COLD_BYTES // q_bytes)))
+    n_f = min(MAX_COPIES, max(1, -(-COLD_BYTES // f16_bytes)))
     planes = [base] + [tuple(t.clone() for t in base) for _ in range(n_q - 1)]
     kv16 = [(kx, vx)] + [(kx.clone(), vx.clone()) for _ in range(n_f - 1)]
     torch.cuda.synchronize()

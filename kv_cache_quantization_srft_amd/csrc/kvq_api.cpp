@@ -66,9 +66,8 @@ kvq_status check_range(const kvq_layout* L, int32_t pos, int32_t n_tok, const ch
   if (pos < 0 || n_tok < 1 || (long long)pos + n_tok > L->capacity)
     return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: token range [pos=%d, pos+n_tok=%lld) must lie in [0, capacity=%d)", fn,
                 pos, (long long)pos + n_tok, L->capacity);
-  long long tiles = ((long long)n_tok + 255) / 256;
-  if ((long long)L->batch * L->kv_heads * tiles > 0x7fffffffLL)
-    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: too many vectors for one call", fn);
+  if ((long long)L->batch * L->kv_heads * n_tok > 0x7fffffffLL)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: batch x kv_heads x n_tok exceeds 2^31 - 1 vectors", fn);
   return KVQ_OK;
 }
 

@@ -114,89 +114,9 @@ __device__ __forceinline__ const MfmaQTable<D>& mqtable() {
     return kMQ256;
 }
 
-// ------------------------------------------------------------------------------------------
-// SRFT entries generated in registers.  16 Q[c][n] depends on (c, n) only through the row
-// kind (c = 0, c = 1, even c, odd c) and the angle m = (c/2) n mod D, so a table of 2D fp16
-// (hi | lo << 16) pairs, interleaved per angle, gives every entry with one LDS read:
-//   e[2m]     = 16 sqrt(2/D) cos(2 pi m / D)     (rows c = 2k, k >= 1)
-//   e[2m + 1] = -16 sqrt(2/D) sin(2 pi m / D)    (rows c = 2k + 1, k >= 1)
-//   rows 0 and 1: 16/sqrt(D) and (-1)^n 16/sqrt(D).
-// The split is the one of the full table above (double -> float -> fp16 hi, residual -> lo).
-// ------------------------------------------------------------------------------------------
 __device__ __forceinline__ v8h as_v8h(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   v4i t = {int(a), int(b), int(c), int(d)};
   return __builtin_bit_cast(v8h, t);
-}
-
-constexpr uint32_t split16(double v) {
-  const float vf = float(v);
-  const _Float16 hi = static_cast<_Float16>(vf);
-  const _Float16 lo = static_cast<_Float16>(float(v - double(static_cast<float>(hi))));
-  return uint32_t(__builtin_bit_cast(uint16_t, hi)) | (uint32_t(__builtin_bit_cast(uint16_t, lo)) << 16);
-}
-
-template <int D>
-struct SrftPairs {
-  uint32_t e[2 * D];
-  constexpr SrftPairs() : e() {
-    const double r2 = csqrt(2.0 / double(D));
-    for (int m = 0; m < D; ++m) {
-      const CosSin w = cos_sin_turn(m, D);
-      e[2 * m] = split16(16.0 * (r2 * w.c));
-      e[2 * m + 1] = split16(16.0 * (-(r2 * w.s)));
-    }
-  }
-};
-
-template <int D>
-struct SrftRow0 {
-  static constexpr uint32_t pos = split16(16.0 * (1.0 / csqrt(double(D))));
-  static constexpr uint32_t neg = split16(16.0 * (-(1.0 / csqrt(double(D)))));
-};
-
-__device__ const SrftPairs<128> kSP128 = SrftPairs<128>();
-__device__ const SrftPairs<256> kSP256 = SrftPairs<256>();
-
-// Copy the pair table to LDS (2D words), all threads of the work-group: fetch into registers,
-// then store (so the caller can issue other loads in between).
-template <int D>
-__device__ __forceinline__ void srft_pairs_fetch(uint32_t (&v)[2 * D / kThreads]) {
-  const uint32_t* src = D == 128 ? kSP128.e : kSP256.e;
-#pragma unroll
-  for (int i = 0; i < 2 * D / kThreads; ++i) v[i] = src[threadIdx.x + i * kThreads];
-}
-template <int D>
-__device__ __forceinline__ void srft_pairs_store(uint32_t* tw, const uint32_t (&v)[2 * D / kThreads]) {
-#pragma unroll
-  for (int i = 0; i < 2 * D / kThreads; ++i) tw[threadIdx.x + i * kThreads] = v[i];
-}
-
-// 16 Q[c][n] as an fp16 (hi | lo << 16) pair.
-template <int D>
-__device__ __forceinline__ uint32_t q_pair(const uint32_t* tw, int c, int n) {
-  const uint32_t v = tw[2 * (((c >> 1) * n) & (D - 1)) + (c & 1)];
-  return c >= 2 ? v : ((c & n & 1) ? SrftRow0<D>::neg : SrftRow0<D>::pos);
-}
-
-// B operand (hi and lo halves) of v_mfma_f32_16x16x32_f16 for step s and column block blk.
-// Lane l holds k = 8 (l / 16) + j (j = 0..7) of column l % 16:
-//   forward (q_hat = Q x):   B[k][col] = 16 Q[16 blk + col][32 s + k]
-//   inverse (x = Q^T y):     B[k][col] = 16 Q[32 s + k][16 blk + col]
-template <int D, bool INV>
-__device__ __forceinline__ void srft_operand(const uint32_t* tw, int blk, int s, int lane, v8h& hi, v8h& lo) {
-  const int fixed = 16 * blk + (lane & 15);
-  const int k0 = 32 * s + 8 * (lane >> 4);
-  uint32_t e[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) e[j] = INV ? q_pair<D>(tw, k0 + j, fixed) : q_pair<D>(tw, fixed, k0 + j);
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    h[i] = (e[2 * i] & 0xffffu) | (e[2 * i + 1] << 16);
-    l[i] = (e[2 * i] >> 16) | (e[2 * i + 1] & 0xffff0000u);
-  }
-  hi = as_v8h(h[0], h[1], h[2], h[3]);
-  lo = as_v8h(l[0], l[1], l[2], l[3]);
 }
 
 __device__ __forceinline__ uint4 ld4(const uint32_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -410,62 +330,140 @@ constexpr int merge_lds_floats() {
   return 16 * D + 16 * 32 + 32;
 }
 
+// Operands of the inverse rotation of one wave (output blocks w, w + 4, ...) from the global
+// inverse table, all loaded ahead, and the output signs.
+template <int D>
+struct RotOps {
+  static constexpr int NBW = D / 16 / kWaves, NSTEP = D / 32;
+  static constexpr int NPRE = NBW;
+  uint4 bh[NPRE][NSTEP], bl[NPRE][NSTEP];
+  float sg[NBW];
+};
+
+__device__ __forceinline__ void unit_coords(const MergeArgs& a, int unit, int& b, int& kvh, int64_t& orow0) {
+  const int ht = unit % a.head_tiles;
+  const int bk = unit / a.head_tiles;
+  kvh = bk % a.kv_heads;
+  b = bk / a.kv_heads;
+  orow0 = int64_t(b) * a.q_heads + kvh * (a.q_heads / a.kv_heads) + ht * a.head_tile;
+}
+
+template <int D>
+__device__ __forceinline__ void rot_prefetch(RotOps<D>& o, const MergeArgs& a, int unit) {
+  int b, kvh;
+  int64_t orow0;
+  unit_coords(a, unit, b, kvh, orow0);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < RotOps<D>::NBW; ++j) o.sg[j] = a.sign[b * a.sign_bs + 16 * (w + kWaves * j) + (lane & 15)];
+  const MfmaQTable<D>& T = mqtable<D>();
+#pragma unroll
+  for (int j = 0; j < RotOps<D>::NPRE; ++j)
+#pragma unroll
+    for (int s = 0; s < RotOps<D>::NSTEP; ++s) {
+      o.bh[j][s] = ld4(T.inv_hi[w + kWaves * j][s][lane]);
+      o.bl[j][s] = ld4(T.inv_lo[w + kWaves * j][s][lane]);
+    }
+}
+
+// out[h][n] = s_n sum_c y[h][c] Q[c][n] for the heads h < head_tile of the unit, as MFMAs with
+// A = y split into fp16 hi + lo and B = 16 Q (the 1/16 is applied with the sign).
+template <int D>
+__device__ __forceinline__ void rotate_store(const MergeArgs& a, int unit, const float (*y)[D], const RotOps<D>& o) {
+  constexpr int NSTEP = D / 32, NBW = D / 16 / kWaves;
+  int b, kvh;
+  int64_t orow0;
+  unit_coords(a, unit, b, kvh, orow0);
+  const int GT = a.head_tile;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n16 = lane & 15, r4 = lane >> 4;
+  // A operands: y[head n16][32 s + 8 r4 + (0..7)] split into hi + lo
+  v8h ahi[NSTEP], alo[NSTEP];
+#pragma unroll
+  for (int s = 0; s < NSTEP; ++s) {
+    const float4 y0 = *reinterpret_cast<const float4*>(&y[n16][32 * s + 8 * r4]);
+    const float4 y1 = *reinterpret_cast<const float4*>(&y[n16][32 * s + 8 * r4 + 4]);
+    uint32_t h4[4], l4[4];
+    split_pair(y0.x, y0.y, h4[0], l4[0]);
+    split_pair(y0.z, y0.w, h4[1], l4[1]);
+    split_pair(y1.x, y1.y, h4[2], l4[2]);
+    split_pair(y1.z, y1.w, h4[3], l4[3]);
+    ahi[s] = as_v8h(h4[0], h4[1], h4[2], h4[3]);
+    alo[s] = as_v8h(l4[0], l4[1], l4[2], l4[3]);
+  }
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) {
+    const int nb = w + kWaves * j;
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      uint4 ph, pl;
+      if (j < RotOps<D>::NPRE) {
+        ph = o.bh[j < RotOps<D>::NPRE ? j : 0][s];
+        pl = o.bl[j < RotOps<D>::NPRE ? j : 0][s];
+      } else {
+        const MfmaQTable<D>& T = mqtable<D>();
+        ph = ld4(T.inv_hi[nb][s][lane]);
+        pl = ld4(T.inv_lo[nb][s][lane]);
+      }
+      const v8h bhi = as_v8h(ph.x, ph.y, ph.z, ph.w), blo = as_v8h(pl.x, pl.y, pl.z, pl.w);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[s], bhi, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[s], blo, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[s], bhi, acc, 0, 0, 0);
+    }
+    const int n = 16 * nb + n16;
+    const float sg = (o.sg[j] < 0.0f ? -1.0f : 1.0f) * 0.0625f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * r4 + i;
+      if (h < GT) a.out[(orow0 + h) * D + n] = acc[i] * sg;
+    }
+  }
+}
+
+// Merge of the n_chunks partials of one unit from the workspace (the last work-group to
+// finish).  Every (head, channel) combines its chunks, y = acc_scale * acc / l; with ROT, y is
+// scaled by lambda_V and inverse-rotated.  Each thread owns quads of 4 consecutive channels of
+// one head; the first CR chunks of its quads are loaded at once, before the (m, l) pairs.
 template <int D, bool ROT>
-__device__ __forceinline__ void merge_unit(const MergeArgs& a, int unit, float* smem, const uint32_t* tw) {
-  constexpr int MAXC = 32;  // chunks whose weights are staged in LDS at once
-  constexpr int NP = 16 * D / kThreads;  // (head, channel) pairs per thread, at most
-  constexpr int CR = 8 * 128 / D;        // chunks of each pair prefetched into registers
+__device__ __forceinline__ void merge_unit(const MergeArgs& a, int unit, float* smem) {
+  constexpr int MAXC = 32;                    // chunks whose weights are staged in LDS at once
+  constexpr int GTMAX = D == 128 ? 16 : 8;    // largest head tile
+  constexpr int NQ = (GTMAX * D / 4 + kThreads - 1) / kThreads;  // quads per thread, at most
+  constexpr int CR = 8;                       // chunks prefetched into registers
   float(*y)[D] = reinterpret_cast<float(*)[D]>(smem);
   float(*wgt)[MAXC] = reinterpret_cast<float(*)[MAXC]>(smem + 16 * D);
   float* linv = smem + 16 * D + 16 * MAXC;
   float* mmax = linv + 16;
-  const int ht = unit % a.head_tiles;
-  const int bk = unit / a.head_tiles;
-  const int kvh = bk % a.kv_heads;
-  const int b = bk / a.kv_heads;
-  const int G = a.q_heads / a.kv_heads;
+  int b, kvh;
+  int64_t orow0;
+  unit_coords(a, unit, b, kvh, orow0);
   const int GT = a.head_tile;
   const int n_chunks = a.n_chunks, max_chunks = a.max_chunks;
-  const int64_t orow0 = int64_t(b) * a.q_heads + kvh * G + ht * GT;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  constexpr int NB = D / 16, NSTEP = D / 32, NBW = NB / kWaves;
-  // every load that does not depend on another goes out first: the first CR chunks of this
-  // thread's (head, channel) pairs, lambda and the output signs, then the (m, l) pairs
-  float pre[NP][CR];
-  float lamv[NP];
+  float4 pre[NQ][CR];
+  float4 lam4[NQ];
 #pragma unroll
-  for (int k = 0; k < NP; ++k) {
-    const int idx = threadIdx.x + k * kThreads;
-    const int h = idx / D, c = idx - h * D;
-    lamv[k] = 1.0f;
+  for (int k = 0; k < NQ; ++k) {
+    const int q = threadIdx.x + k * kThreads;
+    const int h = (4 * q) / D, c = 4 * q - h * D;
+    lam4[k] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
 #pragma unroll
-    for (int i = 0; i < CR; ++i) pre[k][i] = 0.0f;
+    for (int i = 0; i < CR; ++i) pre[k][i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (h < GT) {
       const float* pa = a.pacc + (int64_t(unit) * GT + h) * max_chunks * D + c;
 #pragma unroll
       for (int i = 0; i < CR; ++i)
-        if (i < n_chunks) pre[k][i] = ld_dev(&pa[int64_t(i) * D]);
-      if (ROT && a.lambda) lamv[k] = a.lambda[b * a.lambda_bs + int64_t(kvh) * D + c];
+        if (i < n_chunks) {
+          const float* p = pa + int64_t(i) * D;
+          pre[k][i] = make_float4(ld_dev(p), ld_dev(p + 1), ld_dev(p + 2), ld_dev(p + 3));
+        }
+      if (ROT && a.lambda)
+        lam4[k] = *reinterpret_cast<const float4*>(a.lambda + b * a.lambda_bs + int64_t(kvh) * D + c);
     }
   }
-  float psg[ROT ? NBW : 1];
-  // d = 128: the inverse-rotation operands come from the global table (d = 256: generated)
-  constexpr bool kTab = ROT && D == 128;
-  uint4 pbh[kTab ? NBW : 1][NSTEP], pbl[kTab ? NBW : 1][NSTEP];
-  if constexpr (ROT) {
-#pragma unroll
-    for (int j = 0; j < NBW; ++j) psg[j] = a.sign[b * a.sign_bs + 16 * (w + kWaves * j) + (lane & 15)];
-  }
-  if constexpr (kTab) {
-    const MfmaQTable<D>& T = mqtable<D>();
-#pragma unroll
-    for (int j = 0; j < NBW; ++j)
-#pragma unroll
-      for (int s = 0; s < NSTEP; ++s) {
-        pbh[j][s] = ld4(T.inv_hi[w + kWaves * j][s][lane]);
-        pbl[j][s] = ld4(T.inv_lo[w + kWaves * j][s][lane]);
-      }
-  }
+  RotOps<D> ro;
+  if constexpr (ROT) rot_prefetch<D>(ro, a, unit);
   // per-head chunk weights exp2(m_i - M) and 1/l, one wave per head
   for (int h = w; h < GT; h += kWaves) {
     const float* ml = a.pml + (int64_t(unit) * GT + h) * max_chunks * 2;
@@ -495,72 +493,146 @@ __device__ __forceinline__ void merge_unit(const MergeArgs& a, int unit, float* 
     }
   }
   __syncthreads();
+  float4 yv[NQ];
 #pragma unroll
-  for (int k = 0; k < NP; ++k) {
-    const int idx = threadIdx.x + k * kThreads;
-    const int h = idx / D, c = idx - h * D;
-    float v = 0.0f;
+  for (int k = 0; k < NQ; ++k) {
+    const int q = threadIdx.x + k * kThreads;
+    const int h = (4 * q) / D, c = 4 * q - h * D;
+    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (h < GT) {
       const float* pa = a.pacc + (int64_t(unit) * GT + h) * max_chunks * D + c;
       const float* ml = a.pml + (int64_t(unit) * GT + h) * max_chunks * 2;
-      float acc4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int i = 0; i < CR; ++i)
-        if (i < n_chunks) acc4[i & 3] = fmaf(pre[k][i], wgt[h][i], acc4[i & 3]);
+        if (i < n_chunks) {
+          const float f = wgt[h][i];
+          v = make_float4(fmaf(pre[k][i].x, f, v.x), fmaf(pre[k][i].y, f, v.y), fmaf(pre[k][i].z, f, v.z),
+                          fmaf(pre[k][i].w, f, v.w));
+        }
       for (int i = CR; i < n_chunks; ++i) {
         const float f = i < MAXC ? wgt[h][i] : exp2_guard(ld_dev(&ml[2 * i]), mmax[h]);
-        acc4[i & 3] = fmaf(ld_dev(&pa[int64_t(i) * D]), f, acc4[i & 3]);
+        const float* p = pa + int64_t(i) * D;
+        v = make_float4(fmaf(ld_dev(p), f, v.x), fmaf(ld_dev(p + 1), f, v.y), fmaf(ld_dev(p + 2), f, v.z),
+                        fmaf(ld_dev(p + 3), f, v.w));
       }
-      v = ((acc4[0] + acc4[1]) + (acc4[2] + acc4[3])) * linv[h];
-      if constexpr (!ROT)
-        a.out[(orow0 + h) * D + c] = v;
-      else
-        v *= lamv[k];
+      const float li = linv[h];
+      v = make_float4(v.x * li * lam4[k].x, v.y * li * lam4[k].y, v.z * li * lam4[k].z, v.w * li * lam4[k].w);
+      if constexpr (!ROT) *reinterpret_cast<float4*>(a.out + (orow0 + h) * D + c) = v;
     }
-    y[h][c] = v;
+    yv[k] = v;
+  }
+  if constexpr (ROT) {
+    // rows of y past the head tile are zero
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+      const int q = threadIdx.x + k * kThreads;
+      if (4 * q < 16 * D) *reinterpret_cast<float4*>(&y[(4 * q) / D][(4 * q) % D]) = yv[k];
+    }
+    for (int q = threadIdx.x + NQ * kThreads; 4 * q < 16 * D; q += kThreads)
+      *reinterpret_cast<float4*>(&y[(4 * q) / D][(4 * q) % D]) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    __syncthreads();
+    rotate_store<D>(a, unit, y, ro);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// A unit covered by one chunk (one work-group) needs no workspace round trip: the work-group
+// combines its waves, normalizes, and (ROT) applies lambda_V and the inverse rotation itself.
+// ------------------------------------------------------------------------------------------
+template <int D, bool ROT, int NSLOT, typename HeadOf>
+__device__ __forceinline__ void finish_direct(float (&m_run)[NSLOT], float (&l_run)[NSLOT], v4f (&acc)[D / 16],
+                                              HeadOf head_of, const MergeArgs& a, int unit, float* smem) {
+  constexpr int NG = D / 16;
+  constexpr int NQ = (16 * D / 4 + kThreads - 1) / kThreads;  // float4 quads per thread, at most
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n16 = lane & 15, r4 = lane >> 4;
+  const int GT = a.head_tile;
+  int b, kvh;
+  int64_t orow0;
+  unit_coords(a, unit, b, kvh, orow0);
+  RotOps<D> ro;
+  if constexpr (ROT) rot_prefetch<D>(ro, a, unit);
+  float4 lam4[NQ];
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) {
+    lam4[k] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+    const int q = threadIdx.x + k * kThreads;
+    const int h = (4 * q) / D, c = 4 * q - h * D;
+    if (ROT && a.lambda && h < GT)
+      lam4[k] = *reinterpret_cast<const float4*>(a.lambda + b * a.lambda_bs + int64_t(kvh) * D + c);
+  }
+  // smem: wml[4][16][2] | fw[16][4] | hml[16][2] | wacc[4][GT][D]; y[16][D] reuses it afterwards
+  float* wml = smem;
+  float* fw = smem + kWaves * 16 * 2;
+  float* hml = fw + 16 * kWaves;
+  float* wacc = hml + 16 * 2;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NSLOT; ++k) {
+    const float lt = row_sum16(l_run[k]);
+    const int h = head_of(k, r4);
+    if (n16 == 0 && h < 16) {
+      wml[(w * 16 + h) * 2] = m_run[k];
+      wml[(w * 16 + h) * 2 + 1] = lt;
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * r4 + i;
+      if (h < GT) wacc[(w * GT + h) * D + 16 * g + n16] = acc[g][i];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    const int h = threadIdx.x;
+    float mm = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) mm = fmaxf(mm, wml[(ww * 16 + h) * 2]);
+    float ll = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float f = exp2_guard(wml[(ww * 16 + h) * 2], mm);
+      fw[h * kWaves + ww] = f;
+      ll += wml[(ww * 16 + h) * 2 + 1] * f;
+    }
+    hml[2 * h] = ll > 0.0f ? a.acc_scale / ll : 0.0f;
+  }
+  __syncthreads();
+  float4 yv[NQ];
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) {
+    const int q = threadIdx.x + k * kThreads;
+    const int h = (4 * q) / D, c = 4 * q - h * D;
+    float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (h < GT) {
+      const float4 f = *reinterpret_cast<const float4*>(fw + h * kWaves);
+      const float fv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float4 v = *reinterpret_cast<const float4*>(wacc + (ww * GT + h) * D + c);
+        s.x = fmaf(v.x, fv[ww], s.x);
+        s.y = fmaf(v.y, fv[ww], s.y);
+        s.z = fmaf(v.z, fv[ww], s.z);
+        s.w = fmaf(v.w, fv[ww], s.w);
+      }
+      const float li = hml[2 * h];
+      s = make_float4(s.x * li * lam4[k].x, s.y * li * lam4[k].y, s.z * li * lam4[k].z, s.w * li * lam4[k].w);
+      if constexpr (!ROT) *reinterpret_cast<float4*>(a.out + (orow0 + h) * D + c) = s;
+    }
+    yv[k] = s;
   }
   if constexpr (ROT) {
     __syncthreads();
-    const int n16 = lane & 15, r4 = lane >> 4;
-    // A operands: y[head n16][32 s + 8 r4 + (0..7)] split into hi + lo
-    v8h ahi[NSTEP], alo[NSTEP];
+    float(*y)[D] = reinterpret_cast<float(*)[D]>(smem);
 #pragma unroll
-    for (int s = 0; s < NSTEP; ++s) {
-      const float4 y0 = *reinterpret_cast<const float4*>(&y[n16][32 * s + 8 * r4]);
-      const float4 y1 = *reinterpret_cast<const float4*>(&y[n16][32 * s + 8 * r4 + 4]);
-      uint32_t h4[4], l4[4];
-      split_pair(y0.x, y0.y, h4[0], l4[0]);
-      split_pair(y0.z, y0.w, h4[1], l4[1]);
-      split_pair(y1.x, y1.y, h4[2], l4[2]);
-      split_pair(y1.z, y1.w, h4[3], l4[3]);
-      ahi[s] = as_v8h(h4[0], h4[1], h4[2], h4[3]);
-      alo[s] = as_v8h(l4[0], l4[1], l4[2], l4[3]);
+    for (int k = 0; k < NQ; ++k) {
+      const int q = threadIdx.x + k * kThreads;
+      if (q < 16 * D / 4) *reinterpret_cast<float4*>(&y[(4 * q) / D][(4 * q) % D]) = yv[k];
     }
-#pragma unroll
-    for (int j = 0; j < NBW; ++j) {
-      const int nb = w + kWaves * j;
-      v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int s = 0; s < NSTEP; ++s) {
-        v8h bhi, blo;
-        if constexpr (kTab) {
-          bhi = as_v8h(pbh[j][s].x, pbh[j][s].y, pbh[j][s].z, pbh[j][s].w);
-          blo = as_v8h(pbl[j][s].x, pbl[j][s].y, pbl[j][s].z, pbl[j][s].w);
-        } else {
-          srft_operand<D, true>(tw, nb, s, lane, bhi, blo);
-        }
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[s], bhi, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[s], blo, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[s], bhi, acc, 0, 0, 0);
-      }
-      const int n = 16 * nb + n16;
-      const float sg = (psg[j] < 0.0f ? -1.0f : 1.0f) * 0.0625f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = 4 * r4 + i;
-        if (h < GT) a.out[(orow0 + h) * D + n] = acc[i] * sg;
-      }
-    }
+    __syncthreads();
+    rotate_store<D>(a, unit, y, ro);
   }
 }
 

@@ -195,6 +195,11 @@ __global__ __launch_bounds__(kThreads) void decode_f16_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
+  if (n_chunks == 1) {
+    finish_direct<D, false, 4>(m_run, l_run, acc, [](int k, int rr) { return 4 * rr + k; }, merge, int(unit),
+                               reinterpret_cast<float*>(smem));
+    return;
+  }
   PartialArgs e;
   e.head_tile = head_tile;
   e.max_chunks = max_chunks;
@@ -205,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void decode_f16_kernel(
   store_partial<D, 4>(m_run, l_run, acc, [](int k, int rr) { return 4 * rr + k; }, e,
                       reinterpret_cast<float*>(smem));
   if (!arrive_last(counters + unit, n_chunks, &last_flag)) return;
-  merge_unit<D, false>(merge, int(unit), reinterpret_cast<float*>(smem), nullptr);
+  merge_unit<D, false>(merge, int(unit), reinterpret_cast<float*>(smem));
 }
 
 template <int D>

@@ -9,7 +9,7 @@
 // tokens).
 //   prologue: the first superblock's loads go out, then the work-group rotates its query heads
 //             (v_mfma_f32_16x16x32_f16, A = the sign-flipped fp16 query, B = 16 Q split into
-//             fp16 hi + lo, generated from an LDS table of 2d entries) and splits every rotated
+//             fp16 hi + lo from a constant table in operand order) and splits every rotated
 //             channel into a 16-bit integer (two int8 digits, per-head step sigma) laid out as
 //             the A operand of the score MFMA.
 //   main loop: each wave walks 64-token superblocks:
@@ -24,7 +24,7 @@
 //              A = p split into fp16 hi + lo (three products per tile, fp32 accumulation).
 //   epilogue: the work-group merges its waves and stores a chunk partial; the last work-group
 //             of the unit to finish merges the chunks, applies lambda_V and the inverse rotation
-//             and writes the output.
+//             and writes the output.  A unit covered by a single chunk skips the workspace.
 #include <algorithm>
 
 #include "kvq_decode_common.h"
@@ -359,7 +359,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const QDecodeParams P)
   constexpr int NS = Gm::NS, NG = Gm::NG;
   constexpr int NSTEP = D / 32, NBW = D / 16 / kWaves;
   __shared__ __align__(16) uint8_t smem[Gm::LDS];
-  __shared__ uint32_t tw[2 * D];
   __shared__ int last_flag;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index (uniform)
@@ -385,23 +384,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const QDecodeParams P)
 
   // ---------------- prologue: rotated query -> int8 digit operands ----------------
   // Its few loads go out first (loads complete in issue order), then the first superblock's.
-  // d = 128: the B operands of this wave's channel blocks come from the global forward table
-  // (16 Q as fp16 hi + lo in operand order); d = 256: they are generated from the LDS pair table.
-  constexpr bool kTab = D == 128;
-  uint4 tbh[kTab ? NBW : 1][NSTEP], tbl[kTab ? NBW : 1][NSTEP];
-  uint32_t twv[kTab ? 1 : 2 * D / kThreads];
-  if constexpr (kTab) {
-    const MfmaQTable<D>& T = mqtable<D>();
-#pragma unroll
-    for (int j = 0; j < NBW; ++j)
-#pragma unroll
-      for (int s = 0; s < NSTEP; ++s) {
-        tbh[j][s] = ld4(T.fwd_hi[w + kWaves * j][s][lane]);
-        tbl[j][s] = ld4(T.fwd_lo[w + kWaves * j][s][lane]);
-      }
-  } else {
-    srft_pairs_fetch<D>(twv);
-  }
   float lam[NBW];
 #pragma unroll
   for (int j = 0; j < NBW; ++j)
@@ -421,6 +403,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const QDecodeParams P)
     }
   }
 
+  // The B operands of this wave's channel blocks come from the global forward table (16 Q as
+  // fp16 hi + lo in operand order), all loaded here.
+  constexpr int NPRE = NBW;
+  const MfmaQTable<D>& T = mqtable<D>();
+  uint4 tbh[NPRE][NSTEP], tbl[NPRE][NSTEP];
+#pragma unroll
+  for (int j = 0; j < NPRE; ++j)
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      tbh[j][s] = ld4(T.fwd_hi[w + kWaves * j][s][lane]);
+      tbl[j][s] = ld4(T.fwd_lo[w + kWaves * j][s][lane]);
+    }
+
   SBRegs<D, KB> ra;
   int base = t_begin + w * kSB;
   if (base < t_end) load_superblock<D, KB>(ra, kc, ks, vc, vs, rowbase, base, L, lane);
@@ -431,7 +426,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const QDecodeParams P)
   float* pmax = reinterpret_cast<float*>(smem + kDigBytes);  // [kWaves][16]
   for (int i = threadIdx.x; i < kDigBytes / 16; i += kThreads)
     reinterpret_cast<uint4*>(dig)[i] = make_uint4(0u, 0u, 0u, 0u);
-  if constexpr (!kTab) srft_pairs_store<D>(tw, twv);
   v8h aq[NSTEP];
 #pragma unroll
   for (int s = 0; s < NSTEP; ++s) {
@@ -451,13 +445,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const QDecodeParams P)
     v4f qa = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
-      v8h bh, bl;
-      if constexpr (kTab) {
-        bh = as_v8h(tbh[j][s].x, tbh[j][s].y, tbh[j][s].z, tbh[j][s].w);
-        bl = as_v8h(tbl[j][s].x, tbl[j][s].y, tbl[j][s].z, tbl[j][s].w);
+      uint4 ph, pl;
+      if (j < NPRE) {
+        ph = tbh[j < NPRE ? j : 0][s];
+        pl = tbl[j < NPRE ? j : 0][s];
       } else {
-        srft_operand<D, false>(tw, w + kWaves * j, s, lane, bh, bl);
+        ph = ld4(T.fwd_hi[w + kWaves * j][s][lane]);
+        pl = ld4(T.fwd_lo[w + kWaves * j][s][lane]);
       }
+      const v8h bh = as_v8h(ph.x, ph.y, ph.z, ph.w), bl = as_v8h(pl.x, pl.y, pl.z, pl.w);
       qa = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], bh, qa, 0, 0, 0);
       qa = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], bl, qa, 0, 0, 0);
     }
@@ -567,6 +563,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const QDecodeParams P)
     base += kStride;
   }
 
+  if (P.n_chunks == 1) {
+    finish_direct<D, true, NRB>(m_run, l_run, acc, [](int k, int rr) { return 4 * k + rr; }, P.merge, unit,
+                                reinterpret_cast<float*>(smem));
+    return;
+  }
   PartialArgs e;
   e.head_tile = GT;
   e.max_chunks = P.max_chunks;
@@ -577,7 +578,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const QDecodeParams P)
   store_partial<D, NRB>(m_run, l_run, acc, [](int k, int rr) { return 4 * k + rr; }, e,
                         reinterpret_cast<float*>(smem));
   if (!arrive_last(P.counters + unit, P.n_chunks, &last_flag)) return;
-  merge_unit<D, true>(P.merge, unit, reinterpret_cast<float*>(smem), tw);
+  merge_unit<D, true>(P.merge, unit, reinterpret_cast<float*>(smem));
 }
 
 template <int D, int KB>

@@ -7,7 +7,10 @@
 namespace kvq_impl {
 namespace {
 
-constexpr long kTargetWorkgroups = 512;
+// Work-groups one launch should have: every CU holds two work-groups of the d = 128 kernels
+// at once and one of the d = 256 kernels (register-limited), and the chunk split aims at one
+// full round of resident work-groups.
+long target_workgroups(int head_dim) { return head_dim == 128 ? 512 : 256; }
 
 int token_align(bool f16) { return f16 ? 4 * 32 : 4 * 64; }  // 4 waves x superblock
 
@@ -26,7 +29,7 @@ DecodePlan plan_decode(int batch, int kv_heads, int q_heads, int head_dim, int s
   p.head_tile = tile;
   p.head_tiles = G / tile;
   const long units = long(batch) * kv_heads * p.head_tiles;
-  const long cap_chunks = std::max(1L, (kTargetWorkgroups + units - 1) / units);
+  const long cap_chunks = std::max(1L, (target_workgroups(head_dim) + units - 1) / units);
   const int align = token_align(f16);
   auto chunk_for = [&](int len) {
     long per = (std::max(len, 1) + cap_chunks - 1) / cap_chunks;

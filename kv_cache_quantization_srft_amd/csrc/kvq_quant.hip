@@ -2,16 +2,14 @@
 // + packing ("When Quantization Is Free", technical summary, Methodology 2 and 3), its inverse
 // (dequantize) and per-channel lambda calibration.
 //
-// Two implementations of the same write path:
-//  * d = 128: the rotation of 16 vectors at a time is a 128x128 matrix product on MFMA
-//    (quantize_mfma_kernel, below), which leaves the VALU free for the absmax, rounding and
-//    packing;
-//  * d = 256 (and calibration / dequantize): one lane owns one head vector end to end: it loads
-//    the fp16 vector, flips signs, runs the d/2-point complex FFT and the Hermitian unpack in
-//    registers, scales by norm/lambda, takes the absmax of each group of 16 channels, rounds to
-//    codes and writes packed bytes and fp16 scales.  A work-group covers up to 256 consecutive
-//    tokens of one (sequence, kv head) row, so the sign masks and per-channel factors are staged
-//    once in LDS and read as broadcasts.
+//  * Quantize (the hot write path, d = 128 and 256): the rotation of 16 vectors at a time is a
+//    d x d matrix product on MFMA (quantize_mfma_kernel, below), which leaves the VALU free for
+//    the absmax, rounding and packing.
+//  * Dequantize and calibration (off the decode path): one lane owns one head vector end to
+//    end: it loads the fp16 vector (or codes), runs the d/2-point complex FFT and the Hermitian
+//    (un)pack in registers, and scales by lambda.  A work-group covers up to 256 consecutive
+//    tokens of one (sequence, kv head) row, so the sign masks and per-channel factors are
+//    staged once in LDS and read as broadcasts.
 #include <algorithm>
 
 #include "kvq_decode_common.h"
@@ -37,46 +35,6 @@ struct CodeMagic {
   static constexpr uint32_t to_twos = BITS == 4 ? 0x88888888u : 0x80808080u;
 };
 
-// Quantize one group of 16 channels already scaled to u (float32).
-// Returns the fp16 scale bits and writes the packed group (8 bytes int4, 16 bytes int8).
-template <int BITS>
-__device__ __forceinline__ uint32_t quantize_group(const float (&u)[16], uint32_t (&packed)[BITS == 4 ? 2 : 4]) {
-  using CM = CodeMagic<BITS>;
-  float a = 0.0f;
-  static_for<0, 16>([&](auto C) { a = fmaxf(a, fabsf(u[decltype(C)::value])); });
-  // scale = fp16(a / qmax), saturated at 65504; division correctly rounded in float32
-  const float ratio = fminf(a / CM::qmax, 65504.0f);
-  const _Float16 sh = static_cast<_Float16>(ratio);
-  const float sf = static_cast<float>(sh);
-  const float inv = sf > 0.0f ? 1.0f / sf : 0.0f;
-  uint32_t t[16];
-  static_for<0, 16>([&](auto C) {
-    constexpr int c = decltype(C)::value;
-    float v = fmaf(u[c], inv, CM::magic);
-    v = fminf(fmaxf(v, CM::magic - CM::qmax), CM::magic + CM::qmax);
-    t[c] = __float_as_uint(v);
-  });
-  if constexpr (BITS == 4) {
-    static_for<0, 2>([&](auto W) {
-      constexpr int w = decltype(W)::value;
-      uint32_t acc = 0;
-      static_for<0, 4>([&](auto B) {
-        constexpr int b = decltype(B)::value;
-        const uint32_t byte = ((t[8 * w + 2 * b + 1] << 4) | t[8 * w + 2 * b]) & 0xffu;
-        acc |= byte << (8 * b);
-      });
-      packed[w] = acc ^ CM::to_twos;
-    });
-  } else {
-    static_for<0, 4>([&](auto W) {
-      constexpr int w = decltype(W)::value;
-      packed[w] = ((t[4 * w] & 0xffu) | ((t[4 * w + 1] & 0xffu) << 8) | ((t[4 * w + 2] & 0xffu) << 16) |
-                   (t[4 * w + 3] << 24)) ^
-                  CM::to_twos;
-    });
-  }
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, sh));
-}
 
 // Stage the sign flips of row b as fp16 sign-bit masks (one dword = two channels).
 template <int D>
@@ -107,65 +65,6 @@ __device__ __forceinline__ void load_signed_vector(const uint16_t* __restrict__ 
   });
 }
 
-template <int D, int BITS, bool HAS_LAMBDA>
-__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(
-    const uint16_t* __restrict__ x, int n_tok, int kv_heads, int tiles_per_row, int pos, int capacity,
-    const float* __restrict__ sign, int64_t sign_bs, const float* __restrict__ lambda, int64_t lambda_bs,
-    uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
-  __shared__ __align__(16) uint32_t smask[D / 2];
-  __shared__ __align__(16) float gtab[D];
-  const int row = blockIdx.x / tiles_per_row;
-  const int tile = blockIdx.x - row * tiles_per_row;
-  const int b = row / kv_heads;
-  const int h = row - b * kv_heads;
-  stage_sign_masks<D>(smask, sign + b * sign_bs);
-  for (int c = threadIdx.x; c < D; c += blockDim.x) {
-    float g = fwd_norm<D>(c);
-    if constexpr (HAS_LAMBDA) g = g / lambda[b * lambda_bs + int64_t(h) * D + c];
-    gtab[c] = g;
-  }
-  __syncthreads();
-  const int t = tile * kQuantThreads + threadIdx.x;
-  if (t >= n_tok) return;
-
-  float y[D];
-  load_signed_vector<D>(x + (int64_t(row) * n_tok + t) * D, smask, y);
-  float r[D];
-  real_fwd_raw<D>(y, r);
-
-  constexpr int CB = D * BITS / 8;  // code bytes per vector
-  const int64_t slot = int64_t(row) * capacity + pos + t;
-  uint8_t* dst = codes + slot * CB;
-  uint32_t sbits[D / 16];
-  static_for<0, D / 16>([&](auto G) {
-    constexpr int g = decltype(G)::value;
-    float u[16];
-    const float4* gt4 = reinterpret_cast<const float4*>(gtab + 16 * g);
-    static_for<0, 4>([&](auto Q) {
-      constexpr int q = decltype(Q)::value;
-      const float4 f = gt4[q];
-      u[4 * q + 0] = r[16 * g + 4 * q + 0] * f.x;
-      u[4 * q + 1] = r[16 * g + 4 * q + 1] * f.y;
-      u[4 * q + 2] = r[16 * g + 4 * q + 2] * f.z;
-      u[4 * q + 3] = r[16 * g + 4 * q + 3] * f.w;
-    });
-    if constexpr (BITS == 4) {
-      uint32_t p[2];
-      sbits[g] = quantize_group<4>(u, p);
-      *reinterpret_cast<uint2*>(dst + 8 * g) = make_uint2(p[0], p[1]);
-    } else {
-      uint32_t p[4];
-      sbits[g] = quantize_group<8>(u, p);
-      *reinterpret_cast<uint4*>(dst + 16 * g) = make_uint4(p[0], p[1], p[2], p[3]);
-    }
-  });
-  uint4* sdst = reinterpret_cast<uint4*>(scales + slot * (D / 16));
-  static_for<0, D / 128>([&](auto Q) {
-    constexpr int q = decltype(Q)::value;
-    sdst[q] = make_uint4(sbits[8 * q + 0] | (sbits[8 * q + 1] << 16), sbits[8 * q + 2] | (sbits[8 * q + 3] << 16),
-                         sbits[8 * q + 4] | (sbits[8 * q + 5] << 16), sbits[8 * q + 6] | (sbits[8 * q + 7] << 16));
-  });
-}
 
 // Signed code of channel c from a packed plane row.
 template <int BITS>
@@ -255,21 +154,41 @@ __global__ __launch_bounds__(kQuantThreads) void calibrate_kernel(const uint16_t
 }
 
 // ------------------------------------------------------------------------------------------
-// d = 128 write path on MFMA.  u = Q (s * x) / lambda for 16 vectors at a time with
+// Write path on MFMA.  u = Q (s * x) / lambda for 16 vectors at a time with
 // v_mfma_f32_16x16x32_f16: A = the forward table (16 Q as fp16 hi + lo, rows = channels,
 // k = input index n), B = the sign-flipped fp16 input (exact), fp32 accumulation.  Wave w owns
 // channel blocks 2w and 2w+1 (groups 2w, 2w+1) and keeps their A operands in registers; the
 // input tile is shared through LDS.  In the result each lane holds 4 consecutive channels of
 // one vector, so a group of 16 channels spans 4 lanes (lane, lane+16, lane+32, lane+48).
 // ------------------------------------------------------------------------------------------
+// n / d for 32-bit n and a divisor fixed per launch: floor(n / d) = floor(M n / 2^64) with
+// M = ceil(2^64 / d) for every n < 2^32 (Lemire, Kaser and Kurz, "Faster remainder by direct
+// computation", 2019), i.e. one 32x64-bit high product instead of a division.
+struct FastDiv {
+  uint32_t d, mh, ml;  // M = mh 2^32 + ml (unused for d = 1)
+  static FastDiv make(uint32_t d) {
+    FastDiv f{d, 0u, 0u};
+    if (d > 1) {
+      const uint64_t m = ~uint64_t(0) / d + 1;
+      f.mh = uint32_t(m >> 32);
+      f.ml = uint32_t(m);
+    }
+    return f;
+  }
+  __device__ __forceinline__ uint32_t div(uint32_t n) const {
+    if (d == 1) return n;
+    const uint64_t t = uint64_t(mh) * n + __umulhi(ml, n);
+    return uint32_t(t >> 32);
+  }
+};
+
 namespace mq {
 
 using dec::v8h;
 using dec::v4f;
 
-constexpr int kD = 128;
-constexpr int kNStep = kD / 32;    // k steps of 32 inputs
-constexpr int kVecs = 16;          // vectors per block (MFMA columns)
+constexpr int kVecs = 16;  // vectors per block (MFMA columns)
+constexpr int kPF = 2;     // blocks prefetched ahead
 
 template <int BITS>
 __device__ __forceinline__ float scale_of(float a) {
@@ -281,29 +200,53 @@ __device__ __forceinline__ float scale_of(float a) {
   return fminf(fmaf(r, rq, y), 65504.0f);
 }
 
-template <int BITS, bool HAS_LAMBDA>
-__global__ __launch_bounds__(256) void quantize_mfma_kernel(const uint16_t* __restrict__ x, int n_tok,
-                                                           int kv_heads, int pos, int capacity,
-                                                           const float* __restrict__ sign, int64_t sign_bs,
-                                                           const float* __restrict__ lambda, int64_t lambda_bs,
-                                                           uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
-                                                           int64_t n_vec) {
-  constexpr int CB = kD * BITS / 8;  // code bytes per vector
+// max over the four 16-lane rows for every lane position (v_permlane32_swap, v_permlane16_swap)
+__device__ __forceinline__ float rows_max4(float a) {
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  a = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  return fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+}
+
+// XOR mask that flips the fp16 signs of 8 consecutive channels where sign < 0
+__device__ __forceinline__ uint4 sign_mask(float4 s0, float4 s1) {
+  return make_uint4((s0.x < 0.0f ? 0x8000u : 0u) | (s0.y < 0.0f ? 0x80000000u : 0u),
+                    (s0.z < 0.0f ? 0x8000u : 0u) | (s0.w < 0.0f ? 0x80000000u : 0u),
+                    (s1.x < 0.0f ? 0x8000u : 0u) | (s1.y < 0.0f ? 0x80000000u : 0u),
+                    (s1.z < 0.0f ? 0x8000u : 0u) | (s1.w < 0.0f ? 0x80000000u : 0u));
+}
+
+// Write path of D-dim vectors, 16 vectors per block, 2D threads per work-group: every thread
+// stages one 16-byte piece of one vector; wave w rotates channel blocks 2w, 2w + 1 of all 16
+// vectors with MFMAs (A = 16 Q as fp16 hi + lo from the constant table, B = the sign-flipped
+// fp16 inputs), then scales, rounds and packs them.  Blocks are processed in a grid-stride loop
+// with kPF blocks' inputs in flight; LDS tiles are double-buffered.
+template <int D, int BITS, bool HAS_LAMBDA>
+__global__ __launch_bounds__(2 * D) void quantize_mfma_kernel(const uint16_t* __restrict__ x, FastDiv fd_tok,
+                                                              FastDiv fd_heads, int pos, int capacity,
+                                                              const float* __restrict__ sign, int64_t sign_bs,
+                                                              const float* __restrict__ lambda, int64_t lambda_bs,
+                                                              uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
+                                                              uint32_t n_vec) {
+  constexpr int NP = D / 8;         // 16-byte pieces per vector
+  constexpr int NSTEP = D / 32;     // k steps of 32 inputs
+  constexpr int CB = D * BITS / 8;  // code bytes per vector
+  constexpr int NG = D / 16;        // groups (= channel blocks) per vector
   using CM = CodeMagic<BITS>;
-  __shared__ __align__(16) uint4 xt[kVecs][16];          // 16 vectors x 256 B, piece p at p ^ v
-  __shared__ __align__(16) uint8_t ct[kVecs][CB];        // packed codes
-  __shared__ __align__(16) uint16_t st[kVecs][kD / 16];  // scales
+  __shared__ __align__(16) uint4 xt[2][kVecs][NP];        // inputs, piece p of vector v at p ^ v
+  __shared__ __align__(16) uint8_t ct[2][kVecs][CB];      // packed codes
+  __shared__ __align__(16) uint16_t st[2][kVecs][NG];     // scales
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int n16 = lane & 15, r4 = lane >> 4;
 
   // A operands of this wave's two channel blocks (constant for the kernel)
-  const dec::MfmaQTable<kD>& T = dec::mqtable<kD>();
-  v8h ahi[2][kNStep], alo[2][kNStep];
+  const dec::MfmaQTable<D>& T = dec::mqtable<D>();
+  v8h ahi[2][NSTEP], alo[2][NSTEP];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int s = 0; s < kNStep; ++s) {
+    for (int s = 0; s < NSTEP; ++s) {
       const uint4 h = dec::ld4(T.fwd_hi[2 * w + i][s][lane]);
       const uint4 l = dec::ld4(T.fwd_lo[2 * w + i][s][lane]);
       ahi[i][s] = dec::as_v8h(h.x, h.y, h.z, h.w);
@@ -315,68 +258,80 @@ __global__ __launch_bounds__(256) void quantize_mfma_kernel(const uint16_t* __re
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) linv[i][j] = 0.0625f;
-  int64_t lam_row = -1;
-
-  // each thread stages one 16-byte piece of one vector; the next block's piece is loaded while
-  // the current block computes
-  const int sv = tid >> 4, spc = tid & 15;
-  uint4 nd;
-  float4 ns0, ns1;
-  auto load_piece = [&](int64_t blk_) {
-    const int64_t gv = blk_ * kVecs + sv;
-    nd = make_uint4(0u, 0u, 0u, 0u);
-    ns0 = ns1 = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-    if (gv < n_vec) {
-      const int b = int((gv / n_tok) / kv_heads);
-      nd = *reinterpret_cast<const uint4*>(x + gv * kD + spc * 8);
-      ns0 = *reinterpret_cast<const float4*>(sign + b * sign_bs + spc * 8);
-      ns1 = *reinterpret_cast<const float4*>(sign + b * sign_bs + spc * 8 + 4);
-    }
+  uint32_t lam_row = ~0u;
+  // vector gv is token gv - row n_tok of row (sequence b, kv head h) = gv / n_tok
+  auto slot_of = [&](uint32_t gv) {
+    const uint32_t rw = fd_tok.div(gv);
+    return int64_t(rw) * capacity + pos + (gv - rw * fd_tok.d);
   };
-  load_piece(blockIdx.x);
 
-  for (int64_t blk = blockIdx.x; blk * kVecs < n_vec; blk += gridDim.x) {
-    // ---- stage 16 input vectors (sign bits flipped) in LDS ----
-    {
-      uint4 d = nd;
-      d.x ^= (ns0.x < 0.0f ? 0x8000u : 0u) | (ns0.y < 0.0f ? 0x80000000u : 0u);
-      d.y ^= (ns0.z < 0.0f ? 0x8000u : 0u) | (ns0.w < 0.0f ? 0x80000000u : 0u);
-      d.z ^= (ns1.x < 0.0f ? 0x8000u : 0u) | (ns1.y < 0.0f ? 0x80000000u : 0u);
-      d.w ^= (ns1.z < 0.0f ? 0x8000u : 0u) | (ns1.w < 0.0f ? 0x80000000u : 0u);
-      xt[sv][spc ^ sv] = d;
-    }
-    __syncthreads();
-    if ((blk + gridDim.x) * kVecs < n_vec) load_piece(blk + gridDim.x);
-    // ---- transform: lane (vector n16, channels 16 cb + 4 r4 + i) ----
-    v4f acc[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int s = 0; s < kNStep; ++s) {
-      const uint4 bx = xt[n16][(4 * s + r4) ^ n16];
-      const v8h bop = dec::as_v8h(bx.x, bx.y, bx.z, bx.w);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[i][s], bop, acc[i], 0, 0, 0);
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[i][s], bop, acc[i], 0, 0, 0);
+  // this thread's piece: vector sv of the block, channels 8 spc .. 8 spc + 7
+  const int sv = tid / NP, spc = tid % NP;
+  const bool shared_sign = sign_bs == 0;
+  const uint4 smask0 = shared_sign ? sign_mask(*reinterpret_cast<const float4*>(sign + spc * 8),
+                                               *reinterpret_cast<const float4*>(sign + spc * 8 + 4))
+                                   : make_uint4(0u, 0u, 0u, 0u);
+  uint4 pd[kPF], pm[kPF];
+  auto load_piece = [&](uint32_t blk_, uint4& d, uint4& m) {
+    const uint32_t gv = blk_ * kVecs + sv;
+    d = make_uint4(0u, 0u, 0u, 0u);
+    m = smask0;
+    if (gv < n_vec) {
+      d = *reinterpret_cast<const uint4*>(x + int64_t(gv) * D + spc * 8);
+      if (!shared_sign) {
+        const int b = int(fd_heads.div(fd_tok.div(gv)));
+        m = sign_mask(*reinterpret_cast<const float4*>(sign + b * sign_bs + spc * 8),
+                      *reinterpret_cast<const float4*>(sign + b * sign_bs + spc * 8 + 4));
       }
     }
+  };
+#pragma unroll
+  for (int f = 0; f < kPF; ++f) load_piece(blockIdx.x + uint32_t(f) * gridDim.x, pd[f], pm[f]);
+
+  int buf = 0;
+  for (uint32_t blk = blockIdx.x; blk * kVecs < n_vec; blk += gridDim.x, buf ^= 1) {
+    // ---- stage 16 input vectors (sign bits flipped) in LDS; refill the prefetch ring ----
+    xt[buf][sv][spc ^ sv] = make_uint4(pd[0].x ^ pm[0].x, pd[0].y ^ pm[0].y, pd[0].z ^ pm[0].z, pd[0].w ^ pm[0].w);
+#pragma unroll
+    for (int f = 0; f + 1 < kPF; ++f) {
+      pd[f] = pd[f + 1];
+      pm[f] = pm[f + 1];
+    }
+    if ((blk + uint32_t(kPF) * gridDim.x) * kVecs < n_vec)
+      load_piece(blk + uint32_t(kPF) * gridDim.x, pd[kPF - 1], pm[kPF - 1]);
+    __syncthreads();
+    // ---- transform: lane (vector n16, channels 16 cb + 4 r4 + i) ----
+    // four independent accumulation chains (hi and lo operands of both blocks)
+    v4f acc[2], accl[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) acc[i] = accl[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      const uint4 bx = xt[buf][n16][(4 * s + r4) ^ n16];
+      const v8h bop = dec::as_v8h(bx.x, bx.y, bx.z, bx.w);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[i][s], bop, acc[i], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) accl[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[i][s], bop, accl[i], 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) acc[i] += accl[i];
     // ---- per-channel factor 1/(16 lambda) (recomputed when this lane's row changes), the group
     //      absmax, scale, codes ----
-    const int64_t gv = blk * kVecs + n16;
-    const int64_t row = gv < n_vec ? gv / n_tok : 0;
     if constexpr (HAS_LAMBDA) {
+      const uint32_t gv = blk * kVecs + n16;
+      const uint32_t row = gv < n_vec ? fd_tok.div(gv) : 0u;
       if (row != lam_row) {
         lam_row = row;
-        const int b = int(row / kv_heads), h = int(row - int64_t(b) * kv_heads);
+        const uint32_t b = fd_heads.div(row), h = row - b * fd_heads.d;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const float4 lm =
-              *reinterpret_cast<const float4*>(lambda + b * lambda_bs + int64_t(h) * kD + 16 * (2 * w + i) + 4 * r4);
-          linv[i][0] = 1.0f / (16.0f * lm.x);
-          linv[i][1] = 1.0f / (16.0f * lm.y);
-          linv[i][2] = 1.0f / (16.0f * lm.z);
-          linv[i][3] = 1.0f / (16.0f * lm.w);
+          const float4 lm = *reinterpret_cast<const float4*>(lambda + int64_t(b) * lambda_bs + int64_t(h) * D +
+                                                             16 * (2 * w + i) + 4 * r4);
+          linv[i][0] = __builtin_amdgcn_rcpf(16.0f * lm.x);
+          linv[i][1] = __builtin_amdgcn_rcpf(16.0f * lm.y);
+          linv[i][2] = __builtin_amdgcn_rcpf(16.0f * lm.z);
+          linv[i][3] = __builtin_amdgcn_rcpf(16.0f * lm.w);
         }
       }
     }
@@ -386,12 +341,10 @@ __global__ __launch_bounds__(256) void quantize_mfma_kernel(const uint16_t* __re
       float u[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) u[j] = acc[i][j] * linv[i][j];
-      float a = fmaxf(fmaxf(fabsf(u[0]), fabsf(u[1])), fmaxf(fabsf(u[2]), fabsf(u[3])));
-      a = fmaxf(a, __shfl_xor(a, 16));
-      a = fmaxf(a, __shfl_xor(a, 32));
+      const float a = rows_max4(fmaxf(fmaxf(fabsf(u[0]), fabsf(u[1])), fmaxf(fabsf(u[2]), fabsf(u[3]))));
       const _Float16 sh = static_cast<_Float16>(scale_of<BITS>(a));
       const float sf = static_cast<float>(sh);
-      const float inv = sf > 0.0f ? 1.0f / sf : 0.0f;
+      const float inv = sf > 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
       uint32_t tq[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -402,58 +355,39 @@ __global__ __launch_bounds__(256) void quantize_mfma_kernel(const uint16_t* __re
       if constexpr (BITS == 4) {
         const uint32_t byte0 = ((tq[1] << 4) | (tq[0] & 0xfu)) & 0xffu;
         const uint32_t byte1 = ((tq[3] << 4) | (tq[2] & 0xfu)) & 0xffu;
-        *reinterpret_cast<uint16_t*>(&ct[n16][8 * g + 2 * r4]) = uint16_t((byte0 | (byte1 << 8)) ^ 0x8888u);
+        *reinterpret_cast<uint16_t*>(&ct[buf][n16][8 * g + 2 * r4]) = uint16_t((byte0 | (byte1 << 8)) ^ 0x8888u);
       } else {
         const uint32_t word = ((tq[0] & 0xffu) | ((tq[1] & 0xffu) << 8) | ((tq[2] & 0xffu) << 16) | (tq[3] << 24)) ^
                               CM::to_twos;
-        *reinterpret_cast<uint32_t*>(&ct[n16][16 * g + 4 * r4]) = word;
+        *reinterpret_cast<uint32_t*>(&ct[buf][n16][16 * g + 4 * r4]) = word;
       }
-      if (r4 == 0) st[n16][g] = __builtin_bit_cast(uint16_t, sh);
+      if (r4 == 0) st[buf][n16][g] = __builtin_bit_cast(uint16_t, sh);
     }
     __syncthreads();
     // ---- store codes (16 B per thread) and scales ----
     {
       constexpr int UNITS = kVecs * CB / 16;  // 16-byte code units
+      constexpr int SUNITS = kVecs * NG / 8;  // 16-byte scale units
       if (tid < UNITS) {
         const int v = tid / (CB / 16), pc = tid - v * (CB / 16);
-        const int64_t gvs = blk * kVecs + v;
-        if (gvs < n_vec) {
-          const int64_t rw = gvs / n_tok, tk = gvs - rw * n_tok;
-          const int64_t slot = rw * capacity + pos + tk;
-          *reinterpret_cast<uint4*>(codes + slot * CB + pc * 16) = *reinterpret_cast<const uint4*>(&ct[v][pc * 16]);
-        }
-      } else if (tid >= 128 && tid < 128 + kVecs) {
-        const int v = tid - 128;
-        const int64_t gvs = blk * kVecs + v;
-        if (gvs < n_vec) {
-          const int64_t rw = gvs / n_tok, tk = gvs - rw * n_tok;
-          const int64_t slot = rw * capacity + pos + tk;
-          *reinterpret_cast<uint4*>(scales + slot * (kD / 16)) = *reinterpret_cast<const uint4*>(&st[v][0]);
-        }
+        const uint32_t gvs = blk * kVecs + v;
+        if (gvs < n_vec)
+          *reinterpret_cast<uint4*>(codes + slot_of(gvs) * CB + pc * 16) =
+              *reinterpret_cast<const uint4*>(&ct[buf][v][pc * 16]);
+      } else if (tid >= UNITS && tid < UNITS + SUNITS) {
+        const int u = tid - UNITS;
+        const int v = u / (NG / 8), pc = u - v * (NG / 8);
+        const uint32_t gvs = blk * kVecs + v;
+        if (gvs < n_vec)
+          *reinterpret_cast<uint4*>(scales + slot_of(gvs) * NG + pc * 8) =
+              *reinterpret_cast<const uint4*>(&st[buf][v][pc * 8]);
       }
     }
-    __syncthreads();
   }
 }
 
 }  // namespace mq
 
-template <int D, int BITS>
-hipError_t quantize_dispatch_lambda(const QuantArgs& a, hipStream_t s) {
-  const int rows = a.batch * a.kv_heads;
-  const int tiles = (a.n_tok + kQuantThreads - 1) / kQuantThreads;
-  const dim3 grid(rows * tiles), block(kQuantThreads);
-  auto* x = static_cast<const uint16_t*>(a.x);
-  auto* codes = static_cast<uint8_t*>(a.codes);
-  auto* scales = static_cast<uint16_t*>(a.scales);
-  if (a.lambda)
-    hipLaunchKernelGGL((quantize_kernel<D, BITS, true>), grid, block, 0, s, x, a.n_tok, a.kv_heads, tiles, a.pos,
-                       a.capacity, a.sign, a.sign_bs, a.lambda, a.lambda_bs, codes, scales);
-  else
-    hipLaunchKernelGGL((quantize_kernel<D, BITS, false>), grid, block, 0, s, x, a.n_tok, a.kv_heads, tiles, a.pos,
-                       a.capacity, a.sign, a.sign_bs, a.lambda, a.lambda_bs, codes, scales);
-  return hipGetLastError();
-}
 
 template <int D, int BITS>
 hipError_t dequantize_dispatch_lambda(const DequantArgs& a, hipStream_t s) {
@@ -473,26 +407,30 @@ hipError_t dequantize_dispatch_lambda(const DequantArgs& a, hipStream_t s) {
 
 }  // namespace
 
-template <int BITS>
+template <int D, int BITS>
 hipError_t quantize_mfma_dispatch(const QuantArgs& a, hipStream_t s) {
-  const int64_t n_vec = int64_t(a.batch) * a.kv_heads * a.n_tok;
+  const uint32_t n_vec = uint32_t(a.batch) * uint32_t(a.kv_heads) * uint32_t(a.n_tok);  // < 2^31 (validated)
+  const FastDiv fd_tok = FastDiv::make(uint32_t(a.n_tok)), fd_heads = FastDiv::make(uint32_t(a.kv_heads));
   const int64_t blocks = (n_vec + mq::kVecs - 1) / mq::kVecs;
-  const int grid = int(std::min<int64_t>(blocks, 2048));
+  // resident work-groups per CU: 3 (d = 128, 256 threads), 1 (d = 256, 512 threads)
+  const int64_t resident = D == 128 ? 3 * 256 : 256;
+  const int grid = int(std::min<int64_t>(blocks, resident));
   auto* x = static_cast<const uint16_t*>(a.x);
   auto* codes = static_cast<uint8_t*>(a.codes);
   auto* scales = static_cast<uint16_t*>(a.scales);
   if (a.lambda)
-    hipLaunchKernelGGL((mq::quantize_mfma_kernel<BITS, true>), dim3(grid), dim3(256), 0, s, x, a.n_tok, a.kv_heads,
+    hipLaunchKernelGGL((mq::quantize_mfma_kernel<D, BITS, true>), dim3(grid), dim3(2 * D), 0, s, x, fd_tok, fd_heads,
                        a.pos, a.capacity, a.sign, a.sign_bs, a.lambda, a.lambda_bs, codes, scales, n_vec);
   else
-    hipLaunchKernelGGL((mq::quantize_mfma_kernel<BITS, false>), dim3(grid), dim3(256), 0, s, x, a.n_tok, a.kv_heads,
-                       a.pos, a.capacity, a.sign, a.sign_bs, a.lambda, a.lambda_bs, codes, scales, n_vec);
+    hipLaunchKernelGGL((mq::quantize_mfma_kernel<D, BITS, false>), dim3(grid), dim3(2 * D), 0, s, x, fd_tok,
+                       fd_heads, a.pos, a.capacity, a.sign, a.sign_bs, a.lambda, a.lambda_bs, codes, scales, n_vec);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
-  if (a.head_dim == 128) return a.bits == 4 ? quantize_mfma_dispatch<4>(a, s) : quantize_mfma_dispatch<8>(a, s);
-  return a.bits == 4 ? quantize_dispatch_lambda<256, 4>(a, s) : quantize_dispatch_lambda<256, 8>(a, s);
+  if (a.head_dim == 128)
+    return a.bits == 4 ? quantize_mfma_dispatch<128, 4>(a, s) : quantize_mfma_dispatch<128, 8>(a, s);
+  return a.bits == 4 ? quantize_mfma_dispatch<256, 4>(a, s) : quantize_mfma_dispatch<256, 8>(a, s);
 }
 
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t s) {
