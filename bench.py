@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--seq", type=int, default=0, help="override the workload's sequence length (a sweep point)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="eager decode launches plus a plain copy of known size, for rocprofv3 --pmc passes")
     return ap.parse_args()
 
 
@@ -136,6 +138,42 @@ def cpu_baseline(w, budget_s):
     }
 
 
+PMC_COPY_BYTES = 1 << 30  # the plain copy whose counter readings scale the decode's
+
+
+def decode_sources_sha():
+    """sha256 over the decode kernel's sources: the traffic figure of a profile applies only to
+    the kernel it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kv_cache_quantization_srft_amd", "csrc")
+    for name in ("kvq_decode_q.hip", "kvq_decode_common.h", "kvq_internal.h", "kvq_device.h", "kvq_plan.cpp"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(workload_name):
+    """HBM bytes per decode launch from the committed rocprofv3 --pmc summary of this workload
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the same counter's reading for a plain copy of known
+    size), or None when there is none or the decode sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"kvq_decode_traffic_{workload_name}.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- `") and "`: " in line:
+                k, v = line[3:].split("`: ", 1)
+                vals[k] = v.strip()
+    if vals.get("decode_sources_sha") != decode_sources_sha():
+        return None
+    try:
+        return int(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -211,6 +249,22 @@ def main():
     def decode(p):
         kvq.kvq_decode_attn(lay, q, p[0], p[1], p[2], p[3], S, None, s, s, 0, lam_k, lam_v, lbs, 0.0, ws, out)
 
+    if args.pmc_run:
+        # counter passes: 20 eager decode launches over the cache copies, then 4 plain copies of
+        # PMC_COPY_BYTES (device to device) whose counter readings give the scale factor
+        for i in range(20):
+            decode(planes[i % len(planes)])
+        torch.cuda.synchronize()
+        src = torch.empty(PMC_COPY_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_run": w.name, "decode_launches": 20, "copy_bytes": PMC_COPY_BYTES,
+                          "decode_algorithmic_bytes": q_bytes, "decode_sources_sha": decode_sources_sha()}))
+        return
+
     def step(p):
         kvq.kvq_quantize(lay, w.k_bits, k_new, S - 1, 1, s, 0, lam_k, lbs, p[0], p[1])
         kvq.kvq_quantize(lay, w.v_bits, v_new, S - 1, 1, s, 0, lam_v, lbs, p[2], p[3])
@@ -263,10 +317,10 @@ def main():
                           "GBps_moved": round(bq_bytes / (res_bq["ms_mean"] * 1e-3) / 1e9, 2),
                           "frac_hbm_peak": round(bq_bytes / (res_bq["ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                           "vectors": n_vec, "ms": round(res_bq["ms_mean"], 5)},
-        "roofline": {"bound": "hbm", "kernel": "kvq_decode_attn (whole call)",
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel (one launch per kvq_decode_attn call)",
                      "achieved": round(dec_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "algorithmic_bytes_per_launch": dec_bytes},
+                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": profiled_traffic(w.name),
+                     "algorithmic_bytes_per_launch": dec_bytes, "decode_sources_sha": decode_sources_sha()},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")

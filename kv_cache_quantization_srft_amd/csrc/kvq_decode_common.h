@@ -193,15 +193,34 @@ __device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint3
 // its 4 waves in LDS and stores one partial (m, l, acc[d]) per head of the unit.
 // ------------------------------------------------------------------------------------------
 // Chunk partials travel between work-groups that may sit on different XCDs (separate L2s).
-// They are written and read as device-scope relaxed atomics (global_store / global_load with
-// the sc1 scope bit), which the memory model keeps coherent at device scope without an L2
+// They are written and read with device-scope accesses (the sc1 scope bit, as the memory model
+// uses for device-scope relaxed atomics), which stay coherent at device scope without an L2
 // writeback or invalidate; ordering against the completion counter comes from waiting for the
 // stores to complete before the counter is incremented (arrive_last).
-__device__ __forceinline__ void st_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// The accesses go through buffer resources over the unit's partials with the cache policy of
+// device scope (sc1: written through to / read from the device's coherence point), 8 or 16
+// bytes at a time.
+constexpr int kDevScope = 16;  // cache-policy operand of the buffer intrinsics: sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, int64_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, int(n), 0x00020000);
 }
-__device__ __forceinline__ float ld_dev(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void st_dev4(__amdgpu_buffer_rsrc_t r, int off, float4 v) {
+  const v4f x = {v.x, v.y, v.z, v.w};
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, x), r, off, 0, kDevScope);
+}
+__device__ __forceinline__ void st_dev2(__amdgpu_buffer_rsrc_t r, int off, float a, float b) {
+  typedef int v2i __attribute__((ext_vector_type(2)));
+  const v2i x = {__float_as_int(a), __float_as_int(b)};
+  __builtin_amdgcn_raw_buffer_store_b64(x, r, off, 0, kDevScope);
+}
+__device__ __forceinline__ float4 ld_dev4(__amdgpu_buffer_rsrc_t r, int off) {
+  const v4i x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDevScope);
+  return make_float4(__int_as_float(x[0]), __int_as_float(x[1]), __int_as_float(x[2]), __int_as_float(x[3]));
+}
+__device__ __forceinline__ float2 ld_dev2(__amdgpu_buffer_rsrc_t r, int off) {
+  const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kDevScope);
+  return make_float2(__int_as_float(x[0]), __int_as_float(x[1]));
 }
 
 struct PartialArgs {
@@ -260,7 +279,10 @@ __device__ __forceinline__ void store_partial(float (&m_run)[NSLOT], float (&l_r
     hml[2 * h + 1] = ll;
   }
   __syncthreads();
-  // four consecutive channels of one head per thread
+  // four consecutive channels of one head per thread; the unit's partials: pacc rows
+  // (h, chunk) of D floats, pml pairs (m, l) per (h, chunk)
+  const __amdgpu_buffer_rsrc_t racc = buf_rsrc(e.pacc + e.unit * GT * e.max_chunks * D, int64_t(GT) * e.max_chunks * D * 4);
+  const __amdgpu_buffer_rsrc_t rml = buf_rsrc(e.pml + e.unit * GT * e.max_chunks * 2, int64_t(GT) * e.max_chunks * 8);
   for (int q = threadIdx.x; q < GT * D / 4; q += kThreads) {
     const int h = (4 * q) / D, c = 4 * q - h * D;
     const float4 f = *reinterpret_cast<const float4*>(fw + h * kWaves);
@@ -274,16 +296,9 @@ __device__ __forceinline__ void store_partial(float (&m_run)[NSLOT], float (&l_r
       a.z = fmaf(v.z, fv[ww], a.z);
       a.w = fmaf(v.w, fv[ww], a.w);
     }
-    const int64_t prow = (e.unit * GT + h) * e.max_chunks + e.chunk_index;
-    float* dst = e.pacc + prow * D + c;
-    st_dev(dst, a.x);
-    st_dev(dst + 1, a.y);
-    st_dev(dst + 2, a.z);
-    st_dev(dst + 3, a.w);
-    if (c == 0) {
-      st_dev(&e.pml[2 * prow], hml[2 * h]);
-      st_dev(&e.pml[2 * prow + 1], hml[2 * h + 1]);
-    }
+    const int prow = h * e.max_chunks + e.chunk_index;
+    st_dev4(racc, (prow * D + c) * 4, a);
+    if (c == 0) st_dev2(rml, prow * 8, hml[2 * h], hml[2 * h + 1]);
   }
 }
 
@@ -441,6 +456,9 @@ __device__ __forceinline__ void merge_unit(const MergeArgs& a, int unit, float* 
   const int GT = a.head_tile;
   const int n_chunks = a.n_chunks, max_chunks = a.max_chunks;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const __amdgpu_buffer_rsrc_t racc =
+      buf_rsrc(a.pacc + int64_t(unit) * GT * max_chunks * D, int64_t(GT) * max_chunks * D * 4);
+  const __amdgpu_buffer_rsrc_t rml = buf_rsrc(a.pml + int64_t(unit) * GT * max_chunks * 2, int64_t(GT) * max_chunks * 8);
   float4 pre[NQ][CR];
   float4 lam4[NQ];
 #pragma unroll
@@ -451,13 +469,9 @@ __device__ __forceinline__ void merge_unit(const MergeArgs& a, int unit, float* 
 #pragma unroll
     for (int i = 0; i < CR; ++i) pre[k][i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (h < GT) {
-      const float* pa = a.pacc + (int64_t(unit) * GT + h) * max_chunks * D + c;
 #pragma unroll
       for (int i = 0; i < CR; ++i)
-        if (i < n_chunks) {
-          const float* p = pa + int64_t(i) * D;
-          pre[k][i] = make_float4(ld_dev(p), ld_dev(p + 1), ld_dev(p + 2), ld_dev(p + 3));
-        }
+        if (i < n_chunks) pre[k][i] = ld_dev4(racc, ((h * max_chunks + i) * D + c) * 4);
       if (ROT && a.lambda)
         lam4[k] = *reinterpret_cast<const float4*>(a.lambda + b * a.lambda_bs + int64_t(kvh) * D + c);
     }
@@ -466,16 +480,16 @@ __device__ __forceinline__ void merge_unit(const MergeArgs& a, int unit, float* 
   if constexpr (ROT) rot_prefetch<D>(ro, a, unit);
   // per-head chunk weights exp2(m_i - M) and 1/l, one wave per head
   for (int h = w; h < GT; h += kWaves) {
-    const float* ml = a.pml + (int64_t(unit) * GT + h) * max_chunks * 2;
     float mv[2], lv[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int i = lane + 64 * r;
-      mv[r] = i < n_chunks ? ld_dev(&ml[2 * i]) : -INFINITY;
-      lv[r] = i < n_chunks ? ld_dev(&ml[2 * i + 1]) : 0.0f;
+      const float2 v = i < n_chunks ? ld_dev2(rml, (h * max_chunks + i) * 8) : make_float2(-INFINITY, 0.0f);
+      mv[r] = v.x;
+      lv[r] = v.y;
     }
     float mm = fmaxf(mv[0], mv[1]);
-    for (int i = lane + 128; i < n_chunks; i += 64) mm = fmaxf(mm, ld_dev(&ml[2 * i]));
+    for (int i = lane + 128; i < n_chunks; i += 64) mm = fmaxf(mm, ld_dev2(rml, (h * max_chunks + i) * 8).x);
     mm = wave_max(mm);
     float ll = 0.0f;
 #pragma unroll
@@ -485,7 +499,10 @@ __device__ __forceinline__ void merge_unit(const MergeArgs& a, int unit, float* 
       ll += lv[r] * f;
       if (i < MAXC) wgt[h][i] = f;
     }
-    for (int i = lane + 128; i < n_chunks; i += 64) ll += ld_dev(&ml[2 * i + 1]) * exp2_guard(ld_dev(&ml[2 * i]), mm);
+    for (int i = lane + 128; i < n_chunks; i += 64) {
+      const float2 v = ld_dev2(rml, (h * max_chunks + i) * 8);
+      ll += v.y * exp2_guard(v.x, mm);
+    }
     ll = wave_sum(ll);
     if (lane == 0) {
       linv[h] = ll > 0.0f ? a.acc_scale / ll : 0.0f;
@@ -500,8 +517,6 @@ __device__ __forceinline__ void merge_unit(const MergeArgs& a, int unit, float* 
     const int h = (4 * q) / D, c = 4 * q - h * D;
     float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (h < GT) {
-      const float* pa = a.pacc + (int64_t(unit) * GT + h) * max_chunks * D + c;
-      const float* ml = a.pml + (int64_t(unit) * GT + h) * max_chunks * 2;
 #pragma unroll
       for (int i = 0; i < CR; ++i)
         if (i < n_chunks) {
@@ -510,10 +525,9 @@ __device__ __forceinline__ void merge_unit(const MergeArgs& a, int unit, float* 
                           fmaf(pre[k][i].w, f, v.w));
         }
       for (int i = CR; i < n_chunks; ++i) {
-        const float f = i < MAXC ? wgt[h][i] : exp2_guard(ld_dev(&ml[2 * i]), mmax[h]);
-        const float* p = pa + int64_t(i) * D;
-        v = make_float4(fmaf(ld_dev(p), f, v.x), fmaf(ld_dev(p + 1), f, v.y), fmaf(ld_dev(p + 2), f, v.z),
-                        fmaf(ld_dev(p + 3), f, v.w));
+        const float f = i < MAXC ? wgt[h][i] : exp2_guard(ld_dev2(rml, (h * max_chunks + i) * 8).x, mmax[h]);
+        const float4 p = ld_dev4(racc, ((h * max_chunks + i) * D + c) * 4);
+        v = make_float4(fmaf(p.x, f, v.x), fmaf(p.y, f, v.y), fmaf(p.z, f, v.z), fmaf(p.w, f, v.w));
       }
       const float li = linv[h];
       v = make_float4(v.x * li * lam4[k].x, v.y * li * lam4[k].y, v.z * li * lam4[k].z, v.w * li * lam4[k].w);

@@ -354,7 +354,8 @@ struct QDecodeParams {
 };
 
 template <int D, int KB, int NRB>
-__global__ __launch_bounds__(kThreads) void decode_kernel(const QDecodeParams P) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1))) void decode_kernel(
+    const QDecodeParams P) {
   using Gm = QGeom<D, KB>;
   constexpr int NS = Gm::NS, NG = Gm::NG;
   constexpr int NSTEP = D / 32, NBW = D / 16 / kWaves;
