@@ -188,7 +188,6 @@ using dec::v8h;
 using dec::v4f;
 
 constexpr int kVecs = 16;  // vectors per block (MFMA columns)
-constexpr int kPF = 2;     // blocks prefetched ahead
 
 template <int BITS>
 __device__ __forceinline__ float scale_of(float a) {
@@ -201,11 +200,12 @@ __device__ __forceinline__ float scale_of(float a) {
 }
 
 // max over the four 16-lane rows for every lane position (v_permlane32_swap, v_permlane16_swap)
-__device__ __forceinline__ float rows_max4(float a) {
-  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
-  a = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
-  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
-  return fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+// of a non-negative float given as its bit pattern (non-negative floats order like their bits)
+__device__ __forceinline__ uint32_t rows_max4(uint32_t a) {
+  const auto r32 = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+  a = max(uint32_t(r32[0]), uint32_t(r32[1]));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+  return max(uint32_t(r16[0]), uint32_t(r16[1]));
 }
 
 // XOR mask that flips the fp16 signs of 8 consecutive channels where sign < 0
@@ -220,8 +220,10 @@ __device__ __forceinline__ uint4 sign_mask(float4 s0, float4 s1) {
 // stages one 16-byte piece of one vector; wave w rotates channel blocks 2w, 2w + 1 of all 16
 // vectors with MFMAs (A = 16 Q as fp16 hi + lo from the constant table, B = the sign-flipped
 // fp16 inputs), then scales, rounds and packs them.  Blocks are processed in a grid-stride loop
-// with kPF blocks' inputs in flight; LDS tiles are double-buffered.
-template <int D, int BITS, bool HAS_LAMBDA>
+// with kPF blocks' inputs in flight; LDS tiles are double-buffered.  SHARED: every row uses sign
+// row 0 (sign_bs == 0), so the sign mask is fixed per thread and the prefetch ring holds data
+// only, which leaves the registers for a deeper ring.
+template <int D, int BITS, bool HAS_LAMBDA, bool SHARED>
 __global__ __launch_bounds__(2 * D) void quantize_mfma_kernel(const uint16_t* __restrict__ x, FastDiv fd_tok,
                                                               FastDiv fd_heads, int pos, int capacity,
                                                               const float* __restrict__ sign, int64_t sign_bs,
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(2 * D) void quantize_mfma_kernel(const uint16_t* __
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) linv[i][j] = 0.0625f;
-  uint32_t lam_row = ~0u;
+  uint32_t lam_lo = 1u, lam_hi = 0u;  // vectors [lam_lo, lam_hi) share the row whose linv is held
   // vector gv is token gv - row n_tok of row (sequence b, kv head h) = gv / n_tok
   auto slot_of = [&](uint32_t gv) {
     const uint32_t rw = fd_tok.div(gv);
@@ -267,38 +269,40 @@ __global__ __launch_bounds__(2 * D) void quantize_mfma_kernel(const uint16_t* __
 
   // this thread's piece: vector sv of the block, channels 8 spc .. 8 spc + 7
   const int sv = tid / NP, spc = tid % NP;
-  const bool shared_sign = sign_bs == 0;
-  const uint4 smask0 = shared_sign ? sign_mask(*reinterpret_cast<const float4*>(sign + spc * 8),
-                                               *reinterpret_cast<const float4*>(sign + spc * 8 + 4))
-                                   : make_uint4(0u, 0u, 0u, 0u);
-  uint4 pd[kPF], pm[kPF];
-  auto load_piece = [&](uint32_t blk_, uint4& d, uint4& m) {
+  constexpr int kPF = 2;  // blocks prefetched ahead
+  const uint4 smask0 = SHARED ? sign_mask(*reinterpret_cast<const float4*>(sign + spc * 8),
+                                          *reinterpret_cast<const float4*>(sign + spc * 8 + 4))
+                              : make_uint4(0u, 0u, 0u, 0u);
+  uint4 pd[kPF], pm[SHARED ? 1 : kPF];
+  auto load_piece = [&](uint32_t blk_, int f) {
     const uint32_t gv = blk_ * kVecs + sv;
-    d = make_uint4(0u, 0u, 0u, 0u);
-    m = smask0;
+    pd[f] = make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (!SHARED) pm[f] = make_uint4(0u, 0u, 0u, 0u);
     if (gv < n_vec) {
-      d = *reinterpret_cast<const uint4*>(x + int64_t(gv) * D + spc * 8);
-      if (!shared_sign) {
+      pd[f] = *reinterpret_cast<const uint4*>(x + int64_t(gv) * D + spc * 8);
+      if constexpr (!SHARED) {
         const int b = int(fd_heads.div(fd_tok.div(gv)));
-        m = sign_mask(*reinterpret_cast<const float4*>(sign + b * sign_bs + spc * 8),
-                      *reinterpret_cast<const float4*>(sign + b * sign_bs + spc * 8 + 4));
+        pm[f] = sign_mask(*reinterpret_cast<const float4*>(sign + b * sign_bs + spc * 8),
+                          *reinterpret_cast<const float4*>(sign + b * sign_bs + spc * 8 + 4));
       }
     }
   };
 #pragma unroll
-  for (int f = 0; f < kPF; ++f) load_piece(blockIdx.x + uint32_t(f) * gridDim.x, pd[f], pm[f]);
+  for (int f = 0; f < kPF; ++f) load_piece(blockIdx.x + uint32_t(f) * gridDim.x, f);
 
   int buf = 0;
   for (uint32_t blk = blockIdx.x; blk * kVecs < n_vec; blk += gridDim.x, buf ^= 1) {
     // ---- stage 16 input vectors (sign bits flipped) in LDS; refill the prefetch ring ----
-    xt[buf][sv][spc ^ sv] = make_uint4(pd[0].x ^ pm[0].x, pd[0].y ^ pm[0].y, pd[0].z ^ pm[0].z, pd[0].w ^ pm[0].w);
+    {
+      const uint4 m = SHARED ? smask0 : pm[0];
+      xt[buf][sv][spc ^ sv] = make_uint4(pd[0].x ^ m.x, pd[0].y ^ m.y, pd[0].z ^ m.z, pd[0].w ^ m.w);
+    }
 #pragma unroll
     for (int f = 0; f + 1 < kPF; ++f) {
       pd[f] = pd[f + 1];
-      pm[f] = pm[f + 1];
+      if constexpr (!SHARED) pm[f] = pm[f + 1];
     }
-    if ((blk + uint32_t(kPF) * gridDim.x) * kVecs < n_vec)
-      load_piece(blk + uint32_t(kPF) * gridDim.x, pd[kPF - 1], pm[kPF - 1]);
+    if ((blk + uint32_t(kPF) * gridDim.x) * kVecs < n_vec) load_piece(blk + uint32_t(kPF) * gridDim.x, kPF - 1);
     __syncthreads();
     // ---- transform: lane (vector n16, channels 16 cb + 4 r4 + i) ----
     // four independent accumulation chains (hi and lo operands of both blocks)
@@ -319,10 +323,11 @@ __global__ __launch_bounds__(2 * D) void quantize_mfma_kernel(const uint16_t* __
     // ---- per-channel factor 1/(16 lambda) (recomputed when this lane's row changes), the group
     //      absmax, scale, codes ----
     if constexpr (HAS_LAMBDA) {
-      const uint32_t gv = blk * kVecs + n16;
-      const uint32_t row = gv < n_vec ? fd_tok.div(gv) : 0u;
-      if (row != lam_row) {
-        lam_row = row;
+      const uint32_t gv = min(blk * kVecs + n16, n_vec - 1u);
+      if (gv < lam_lo || gv >= lam_hi) {
+        const uint32_t row = fd_tok.div(gv);
+        lam_lo = row * fd_tok.d;
+        lam_hi = lam_lo + fd_tok.d;
         const uint32_t b = fd_heads.div(row), h = row - b * fd_heads.d;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -341,7 +346,9 @@ __global__ __launch_bounds__(2 * D) void quantize_mfma_kernel(const uint16_t* __
       float u[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) u[j] = acc[i][j] * linv[i][j];
-      const float a = rows_max4(fmaxf(fmaxf(fabsf(u[0]), fabsf(u[1])), fmaxf(fabsf(u[2]), fabsf(u[3]))));
+      const uint32_t am = max(max(__float_as_uint(fabsf(u[0])), __float_as_uint(fabsf(u[1]))),
+                              max(__float_as_uint(fabsf(u[2])), __float_as_uint(fabsf(u[3]))));
+      const float a = __uint_as_float(rows_max4(am));
       const _Float16 sh = static_cast<_Float16>(scale_of<BITS>(a));
       const float sf = static_cast<float>(sh);
       const float inv = sf > 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
@@ -418,12 +425,22 @@ hipError_t quantize_mfma_dispatch(const QuantArgs& a, hipStream_t s) {
   auto* x = static_cast<const uint16_t*>(a.x);
   auto* codes = static_cast<uint8_t*>(a.codes);
   auto* scales = static_cast<uint16_t*>(a.scales);
-  if (a.lambda)
-    hipLaunchKernelGGL((mq::quantize_mfma_kernel<D, BITS, true>), dim3(grid), dim3(2 * D), 0, s, x, fd_tok, fd_heads,
-                       a.pos, a.capacity, a.sign, a.sign_bs, a.lambda, a.lambda_bs, codes, scales, n_vec);
-  else
-    hipLaunchKernelGGL((mq::quantize_mfma_kernel<D, BITS, false>), dim3(grid), dim3(2 * D), 0, s, x, fd_tok,
-                       fd_heads, a.pos, a.capacity, a.sign, a.sign_bs, a.lambda, a.lambda_bs, codes, scales, n_vec);
+#define KVQ_QLAUNCH(LAM, SH)                                                                                        \
+  hipLaunchKernelGGL((mq::quantize_mfma_kernel<D, BITS, LAM, SH>), dim3(grid), dim3(2 * D), 0, s, x, fd_tok, fd_heads, \
+                     a.pos, a.capacity, a.sign, a.sign_bs, a.lambda, a.lambda_bs, codes, scales, n_vec)
+  const bool shared = a.sign_bs == 0;
+  if (a.lambda) {
+    if (shared)
+      KVQ_QLAUNCH(true, true);
+    else
+      KVQ_QLAUNCH(true, false);
+  } else {
+    if (shared)
+      KVQ_QLAUNCH(false, true);
+    else
+      KVQ_QLAUNCH(false, false);
+  }
+#undef KVQ_QLAUNCH
   return hipGetLastError();
 }
 
