@@ -37,6 +37,10 @@ Readings taken where the pages are silent (each also listed in the design notes)
       softmax scale defaults to 1/sqrt(d); output is float in the original domain.
   R10 Calibrated lambda = per-channel absmax of SRFT(x) over the first n_cal tokens;
       a zero absmax is replaced by 1.
+  R13 SRHT (the pages' alternative rotation, [QF] Methodology 1 and Key results, SRFT vs
+      SRHT): SRHT(x) = d^-1/2 H_d diag(s) x with H_d the Sylvester-ordered Walsh-Hadamard
+      matrix, H[i][j] = (-1)^popcount(i & j); everything downstream (lambda, quantizer,
+      decode) is unchanged.  Functions take transform="srft" (default) or "srht".
 """
 from __future__ import annotations
 
@@ -112,12 +116,54 @@ def inverse_srft(y: np.ndarray, s: np.ndarray) -> np.ndarray:
     return np.asarray(s, dtype=np.float64) * z.real
 
 
+def hadamard_matrix(d: int) -> np.ndarray:
+    """Sylvester-ordered Walsh-Hadamard matrix, H[i][j] = (-1)^popcount(i & j) (reading R13)."""
+    i = np.arange(d)
+    a = np.bitwise_and(i[:, None], i[None, :])
+    parity = np.zeros_like(a)
+    while a.any():
+        parity ^= a & 1
+        a >>= 1
+    return np.where(parity == 1, -1.0, 1.0)
+
+
+def srht(x: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """SRHT(x) = d^-1/2 H diag(s) x (reading R13)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    return (np.asarray(s, dtype=np.float64) * x) @ hadamard_matrix(d).T / np.sqrt(d)
+
+
+def inverse_srht(y: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """x = diag(s) d^-1/2 H y: H H = d I, so this is the exact inverse of srht."""
+    y = np.asarray(y, dtype=np.float64)
+    d = y.shape[-1]
+    return np.asarray(s, dtype=np.float64) * (y @ hadamard_matrix(d).T / np.sqrt(d))
+
+
+def rotate(x: np.ndarray, s: np.ndarray, transform: str = "srft") -> np.ndarray:
+    """The rotation of the write path: SRFT (readings R1, R2) or SRHT (R13)."""
+    if transform == "srft":
+        return srft(x, s)
+    if transform == "srht":
+        return srht(x, s)
+    raise ValueError(f"unknown transform {transform!r}")
+
+
+def inverse_rotate(y: np.ndarray, s: np.ndarray, transform: str = "srft") -> np.ndarray:
+    if transform == "srft":
+        return inverse_srft(y, s)
+    if transform == "srht":
+        return inverse_srht(y, s)
+    raise ValueError(f"unknown transform {transform!r}")
+
+
 # ----------------------------------------------------------------------------------------
 # Quantizer  [QF] Methodology 2 ("缩放与量化", "半字节打包") and 3 (per-channel + per-group).
 # ----------------------------------------------------------------------------------------
-def rotated_scaled(x16: np.ndarray, s: np.ndarray, lam: np.ndarray) -> np.ndarray:
+def rotated_scaled(x16: np.ndarray, s: np.ndarray, lam: np.ndarray, transform: str = "srft") -> np.ndarray:
     """u = SRFT(x) / lambda in float64 (reading R3).  x16 is taken as stored (fp16 -> f64)."""
-    return srft(np.asarray(x16).astype(np.float64), s) / np.asarray(lam, dtype=np.float64)
+    return rotate(np.asarray(x16).astype(np.float64), s, transform) / np.asarray(lam, dtype=np.float64)
 
 
 def fp16_saturate(v32: np.ndarray) -> np.ndarray:
@@ -146,13 +192,14 @@ def quantize_decision(u: np.ndarray, bits: int, group: int = GROUP):
     return codes.reshape(shape), scale16
 
 
-def quantize(x16: np.ndarray, s: np.ndarray, lam: np.ndarray, bits: int, group: int = GROUP):
+def quantize(x16: np.ndarray, s: np.ndarray, lam: np.ndarray, bits: int, group: int = GROUP,
+             transform: str = "srft"):
     """Full write path for vectors x16 [..., d]: sign -> DFT -> pack -> /lambda -> absmax -> round.
 
     lam broadcasts against x16 (e.g. [Hkv, 1, d] for x16 [Hkv, n, d]).
     Returns (codes int8, scales float16).
     """
-    return quantize_decision(rotated_scaled(x16, s, lam), bits, group)
+    return quantize_decision(rotated_scaled(x16, s, lam, transform), bits, group)
 
 
 def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
@@ -185,20 +232,20 @@ def unpack_codes(packed: np.ndarray, bits: int) -> np.ndarray:
 
 
 def dequantize(codes: np.ndarray, scales16: np.ndarray, s: np.ndarray, lam: np.ndarray,
-               group: int = GROUP) -> np.ndarray:
+               group: int = GROUP, transform: str = "srft") -> np.ndarray:
     """x_hat = diag(s) F^H unpack(lambda * code * scale), float64 (inverse of the write path)."""
     c = np.asarray(codes).astype(np.float64)
     sc = np.repeat(np.asarray(scales16).astype(np.float64), group, axis=-1)
     y = np.asarray(lam, dtype=np.float64) * (c * sc)
-    return inverse_srft(y, s)
+    return inverse_rotate(y, s, transform)
 
 
-def calibrate_lambda(x16: np.ndarray, s: np.ndarray, n_cal: int) -> np.ndarray:
+def calibrate_lambda(x16: np.ndarray, s: np.ndarray, n_cal: int, transform: str = "srft") -> np.ndarray:
     """Per-channel absmax of SRFT(x) over the first n_cal tokens (reading R10).
 
     x16: [..., n, d] -> lambda [..., d] float64.  Zero channels get lambda = 1.
     """
-    y = srft(np.asarray(x16)[..., :n_cal, :].astype(np.float64), s)
+    y = rotate(np.asarray(x16)[..., :n_cal, :].astype(np.float64), s, transform)
     lam = np.abs(y).max(axis=-2)
     return np.where(lam > 0, lam, 1.0)
 
@@ -236,14 +283,14 @@ def decode_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_lens, sm_s
 
 
 def decode_attention_quantized(q16, k_codes, k_scales, v_codes, v_scales, s_k, s_v, lam_k, lam_v,
-                               seq_lens, sm_scale=None):
+                               seq_lens, sm_scale=None, transform: str = "srft"):
     """Decode attention over a quantized cache: dequantize every K/V vector, then attend.
 
     Codes are unpacked int8 codes [B, Hkv, S, d]; scales float16 [B, Hkv, S, d/16];
     lam_k, lam_v broadcast against [B, Hkv, 1, d].
     """
-    k_hat = dequantize(k_codes, k_scales, s_k, lam_k)
-    v_hat = dequantize(v_codes, v_scales, s_v, lam_v)
+    k_hat = dequantize(k_codes, k_scales, s_k, lam_k, transform=transform)
+    v_hat = dequantize(v_codes, v_scales, s_v, lam_v, transform=transform)
     return decode_attention(np.asarray(q16).astype(np.float64), k_hat, v_hat, seq_lens, sm_scale)
 
 
