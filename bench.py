@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--seq", type=int, default=0, help="override the workload's sequence length (a sweep point)")
+    ap.add_argument("--transform", choices=("srft", "srht"), default="srft",
+                    help="the rotation: SRFT (default) or the SRHT variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle sample")
     ap.add_argument("--pmc-run", action="store_true",
@@ -102,7 +104,7 @@ def capture(torch, fn):
     return g
 
 
-def cpu_baseline(w, budget_s):
+def cpu_baseline(w, budget_s, transform="srft"):
     """Time the CPU oracle, as it stands, on a bounded sample of the same workload."""
     from kv_cache_quantization_srft_amd import synth
     from oracle import kvq_oracle as O
@@ -115,13 +117,13 @@ def cpu_baseline(w, budget_s):
         k = synth.kv(w, layer, synth.K_TENSOR)
         v = synth.kv(w, layer, synth.V_TENSOR)
         q = synth.query(w, layer)
-        lk = O.calibrate_lambda(k, s, w.n_cal)[:, :, None, :] if w.calibrate else 1.0
-        lv = O.calibrate_lambda(v, s, w.n_cal)[:, :, None, :] if w.calibrate else 1.0
+        lk = O.calibrate_lambda(k, s, w.n_cal, transform)[:, :, None, :] if w.calibrate else 1.0
+        lv = O.calibrate_lambda(v, s, w.n_cal, transform)[:, :, None, :] if w.calibrate else 1.0
         t0 = time.perf_counter()
-        kc, ks = O.quantize(k, s, lk, w.k_bits)
-        vc, vs = O.quantize(v, s, lv, w.v_bits)
+        kc, ks = O.quantize(k, s, lk, w.k_bits, transform=transform)
+        vc, vs = O.quantize(v, s, lv, w.v_bits, transform=transform)
         t1 = time.perf_counter()
-        O.decode_attention_quantized(q, kc, ks, vc, vs, s, s, lk, lv, w.seq_len)
+        O.decode_attention_quantized(q, kc, ks, vc, vs, s, s, lk, lv, w.seq_len, transform=transform)
         t2 = time.perf_counter()
         t_q += t1 - t0
         t_dec += t2 - t1
@@ -131,7 +133,7 @@ def cpu_baseline(w, budget_s):
     bytes_layer = w.batch * w.kv_heads * w.seq_len * (w.head_dim * (w.k_bits + w.v_bits) // 8 + 2 * 2 * w.head_dim // 16)
     return {
         "value": bytes_layer * layers_done / t_dec / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": (f"{layers_done} of {w.layers} layers: oracle decode (dequantize K,V by O(d^2) DFT + attention "
+        "sample": (f"{layers_done} of {w.layers} layers: oracle decode (dequantize K,V by the O(d^2) inverse {transform.upper()} + attention "
                    f"over {w.seq_len} tokens, {w.q_heads} heads); numpy float64, single thread"),
         "decode_ms_per_layer": 1e3 * t_dec / layers_done,
         "quantize_Mvectors_per_s": vec_q / t_q / 1e6,
@@ -193,7 +195,7 @@ def main():
     LB = L * B
     log(f"workload {w.name}: layers {L} batch {B} kv {H} q {Hq} d {d} seq {S} K{w.k_bits}V{w.v_bits}")
     s = torch.from_numpy(synth.signs(w)).cuda()
-    lay = kvq.make_layout(LB, H, Hq, d, S, k_bits=w.k_bits, v_bits=w.v_bits)
+    lay = kvq.make_layout(LB, H, Hq, d, S, k_bits=w.k_bits, v_bits=w.v_bits, transform=args.transform)
 
     # ---- synthetic cache, resident in HBM (layers folded into the batch) ----
     t0 = time.perf_counter()
@@ -303,6 +305,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "layers": L, "batch": B, "kv_heads": H, "q_heads": Hq, "head_dim": d,
                    "seq_len": S, "k_bits": w.k_bits, "v_bits": w.v_bits, "group": 16,
+                   "rotation": args.transform,
                    "lambda": "calibrated (first 512 tokens)" if w.calibrate else "1",
                    "storage": f"int{w.k_bits} K / int{w.v_bits} V codes + fp16 group scales",
                    "parallelism": "single GPU; layers folded into the batch", "cold_cache_copies": R},
@@ -324,7 +327,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.transform)
     print(json.dumps(result), flush=True)
 
 

@@ -70,7 +70,12 @@ typedef struct {
   int32_t k_bits;     /* 4 or 8                                                                 */
   int32_t v_bits;     /* 4                                                                      */
   int32_t capacity;   /* tokens allocated per (sequence, kv head): the token stride of planes   */
+  int32_t transform;  /* rotation of the write path and of the decode: KVQ_TRANSFORM_SRFT (0,    */
+                      /* [QF] Methodology 1) or KVQ_TRANSFORM_SRHT (1, the pages' alternative:  */
+                      /* d^-1/2 H diag(s) x with the Sylvester-ordered Walsh-Hadamard matrix)   */
 } kvq_layout;
+
+enum { KVQ_TRANSFORM_SRFT = 0, KVQ_TRANSFORM_SRHT = 1 };
 
 /* Library version: major * 10000 + minor * 100 + patch. */
 int32_t kvq_version(void);

@@ -40,6 +40,8 @@ kvq_status check_layout(const kvq_layout* L, const char* fn) {
   if (L->head_dim != 128 && L->head_dim != 256)
     return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 128, 256)", fn, L->head_dim);
   if (L->group_size != 16) return fail(KVQ_ERR_UNSUPPORTED, "%s: group_size %d (supported: 16)", fn, L->group_size);
+  if (L->transform != KVQ_TRANSFORM_SRFT && L->transform != KVQ_TRANSFORM_SRHT)
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: transform %d (supported: 0 = SRFT, 1 = SRHT)", fn, L->transform);
   const long long rows = (long long)L->batch * L->kv_heads;
   if (rows * (long long)L->capacity > (1LL << 40))
     return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: batch*kv_heads*capacity too large", fn);
@@ -167,6 +169,7 @@ kvq_status kvq_quantize(const kvq_layout* L, int32_t bits, const void* x_f16, in
   KVQ_TRY(check_strides(sign_batch_stride, lambda_batch_stride, fn));
   kvq_impl::QuantArgs a{L->batch, L->kv_heads, L->head_dim, bits, L->capacity, pos, n_tok, x_f16, sign,
                         sign_batch_stride, lambda, lambda_batch_stride, codes, scales};
+  a.transform = L->transform;
   return hip_status(kvq_impl::launch_quantize(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -185,6 +188,7 @@ kvq_status kvq_dequantize(const kvq_layout* L, int32_t bits, const void* codes, 
   KVQ_TRY(check_strides(sign_batch_stride, lambda_batch_stride, fn));
   kvq_impl::DequantArgs a{L->batch, L->kv_heads, L->head_dim, bits, L->capacity, pos, n_tok, codes, scales, sign,
                           sign_batch_stride, lambda, lambda_batch_stride, out};
+  a.transform = L->transform;
   return hip_status(kvq_impl::launch_dequantize(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -199,6 +203,7 @@ kvq_status kvq_calibrate_lambda(const kvq_layout* L, const void* x_f16, int32_t 
   KVQ_TRY(check_ptr(lambda, 4, fn, "lambda"));
   KVQ_TRY(check_strides(sign_batch_stride, 0, fn));
   kvq_impl::CalibArgs a{L->batch, L->kv_heads, L->head_dim, n_tok, n_cal, x_f16, sign, sign_batch_stride, lambda};
+  a.transform = L->transform;
   return hip_status(kvq_impl::launch_calibrate(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -234,6 +239,7 @@ kvq_status kvq_decode_attn(const kvq_layout* L, const void* q_f16, const void* k
                          L->capacity, seq_len,    seq_lens,   q_f16,       k_codes,     k_scales,
                          v_codes,    v_scales,    sign_k,     sign_v,      sign_batch_stride, lambda_k,
                          lambda_v,   lambda_batch_stride,     scale,       workspace,   out};
+  a.transform = L->transform;
   return hip_status(kvq_impl::launch_decode(a, p, static_cast<hipStream_t>(stream)), fn);
 }
 

@@ -72,6 +72,10 @@ constexpr double q_entry(int c, int n, int D, const CosSin* tw, double inv, doub
   return (c & 1) ? -r2 * w.s : r2 * w.c;
 }
 
+// The SRHT (Sylvester-ordered Walsh-Hadamard) counterpart, d^-1/2 H[c][n] with
+// H[c][n] = (-1)^popcount(c & n); inv = 1/sqrt(D).
+constexpr double h_entry(int c, int n, double inv) { return (__builtin_popcount(c & n) & 1) ? -inv : inv; }
+
 template <int D>
 struct MfmaQTable {
   static constexpr int NB = D / 16, NSTEP = D / 32;
@@ -79,9 +83,12 @@ struct MfmaQTable {
   uint32_t fwd_lo[NB][NSTEP][64][4];
   uint32_t inv_hi[NB][NSTEP][64][4];
   uint32_t inv_lo[NB][NSTEP][64][4];
-  constexpr MfmaQTable() : fwd_hi(), fwd_lo(), inv_hi(), inv_lo() {
+  // had = false: the SRFT matrix Q; had = true: the SRHT matrix d^-1/2 H (symmetric, so the
+  // forward and inverse operands coincide)
+  constexpr MfmaQTable(bool had = false) : fwd_hi(), fwd_lo(), inv_hi(), inv_lo() {
     CosSin tw[D] = {};
-    for (int m = 0; m < D; ++m) tw[m] = cos_sin_turn(m, D);
+    if (!had)
+      for (int m = 0; m < D; ++m) tw[m] = cos_sin_turn(m, D);
     const double inv = 1.0 / csqrt(double(D)), r2 = csqrt(2.0 / double(D));
     for (int b = 0; b < NB; ++b)
       for (int s = 0; s < NSTEP; ++s)
@@ -89,7 +96,8 @@ struct MfmaQTable {
           for (int j = 0; j < 8; ++j) {
             const int col = 16 * b + (l & 15), k = 32 * s + 8 * (l >> 4) + j;
             for (int which = 0; which < 2; ++which) {
-              const double v = 16.0 * (which == 0 ? q_entry(col, k, D, tw, inv, r2) : q_entry(k, col, D, tw, inv, r2));
+              const int r = which == 0 ? col : k, cl = which == 0 ? k : col;  // Q[r][cl]
+              const double v = 16.0 * (had ? h_entry(r, cl, inv) : q_entry(r, cl, D, tw, inv, r2));
               const float vf = float(v);
               const _Float16 hi = static_cast<_Float16>(vf);
               const _Float16 lo = static_cast<_Float16>(float(v - double(static_cast<float>(hi))));
@@ -103,15 +111,18 @@ struct MfmaQTable {
   }
 };
 
-__device__ const MfmaQTable<128> kMQ128 = MfmaQTable<128>();
-__device__ const MfmaQTable<256> kMQ256 = MfmaQTable<256>();
+__device__ const MfmaQTable<128> kMQ128 = MfmaQTable<128>(false);
+__device__ const MfmaQTable<256> kMQ256 = MfmaQTable<256>(false);
+__device__ const MfmaQTable<128> kMH128 = MfmaQTable<128>(true);
+__device__ const MfmaQTable<256> kMH256 = MfmaQTable<256>(true);
 
+// transform: 0 = SRFT, 1 = SRHT (uniform across the launch)
 template <int D>
-__device__ __forceinline__ const MfmaQTable<D>& mqtable() {
+__device__ __forceinline__ const MfmaQTable<D>& mqtable(int transform) {
   if constexpr (D == 128)
-    return kMQ128;
+    return transform ? kMH128 : kMQ128;
   else
-    return kMQ256;
+    return transform ? kMH256 : kMQ256;
 }
 
 __device__ __forceinline__ v8h as_v8h(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -338,6 +349,7 @@ struct MergeArgs {
   const float* lambda;
   int64_t lambda_bs;
   float* out;
+  int transform;  // rotation to invert: 0 = SRFT, 1 = SRHT
 };
 
 template <int D>
@@ -371,7 +383,7 @@ __device__ __forceinline__ void rot_prefetch(RotOps<D>& o, const MergeArgs& a, i
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int j = 0; j < RotOps<D>::NBW; ++j) o.sg[j] = a.sign[b * a.sign_bs + 16 * (w + kWaves * j) + (lane & 15)];
-  const MfmaQTable<D>& T = mqtable<D>();
+  const MfmaQTable<D>& T = mqtable<D>(a.transform);
 #pragma unroll
   for (int j = 0; j < RotOps<D>::NPRE; ++j)
 #pragma unroll
@@ -417,7 +429,7 @@ __device__ __forceinline__ void rotate_store(const MergeArgs& a, int unit, const
         ph = o.bh[j < RotOps<D>::NPRE ? j : 0][s];
         pl = o.bl[j < RotOps<D>::NPRE ? j : 0][s];
       } else {
-        const MfmaQTable<D>& T = mqtable<D>();
+        const MfmaQTable<D>& T = mqtable<D>(a.transform);
         ph = ld4(T.inv_hi[nb][s][lane]);
         pl = ld4(T.inv_lo[nb][s][lane]);
       }

@@ -221,7 +221,8 @@ hipError_t launch_f16(const DecodeF16Args& a, const DecodePlan& p, const WsLayou
   const int units = a.batch * a.kv_heads * p.head_tiles;
   auto* counters = reinterpret_cast<uint32_t*>(ws + w.counters);
   const MergeArgs m{pml,       pacc,       p.n_chunks, p.max_chunks, p.head_tile, p.head_tiles, a.q_heads,
-                    a.kv_heads, 1.0f,      nullptr,    0,            nullptr,     0,            a.out};
+                    a.kv_heads, 1.0f,      nullptr,    0,            nullptr,     0,            a.out,
+                    0};
   hipLaunchKernelGGL((decode_f16_kernel<D>), dim3(units * p.n_chunks), dim3(kThreads), 0, s,
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.q), a.seq_lens, a.seq_len, a.kv_heads, a.q_heads, a.capacity,

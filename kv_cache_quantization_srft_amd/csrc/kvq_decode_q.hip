@@ -407,7 +407,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   // The B operands of this wave's channel blocks come from the global forward table (16 Q as
   // fp16 hi + lo in operand order), all loaded here.
   constexpr int NPRE = NBW;
-  const MfmaQTable<D>& T = mqtable<D>();
+  const MfmaQTable<D>& T = mqtable<D>(P.merge.transform);
   uint4 tbh[NPRE][NSTEP], tbl[NPRE][NSTEP];
 #pragma unroll
   for (int j = 0; j < NPRE; ++j)
@@ -613,7 +613,7 @@ hipError_t launch_q(const DecodeArgs& a, const DecodePlan& p, const WsLayout& w,
   // code * scale was staged as code * scale / 16 in fp16: acc_scale 16 undoes it
   P.merge = MergeArgs{P.pml,      P.pacc,     p.n_chunks, p.max_chunks, p.head_tile, p.head_tiles,
                       a.q_heads,  a.kv_heads, 16.0f,      a.sign_v,     a.sign_bs,   a.lambda_v,
-                      a.lambda_bs, a.out};
+                      a.lambda_bs, a.out,     a.transform};
   const dim3 grid(units * p.n_chunks), block(kThreads);
   switch ((p.head_tile + 3) / 4) {
     case 1:

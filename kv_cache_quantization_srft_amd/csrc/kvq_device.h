@@ -300,4 +300,28 @@ __device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(f)));
 }
 
+// In-place fast Walsh-Hadamard transform in Sylvester (natural) order, unnormalized:
+// y <- H y with H[i][j] = (-1)^popcount(i & j), log2 N stages of add / subtract butterflies.
+// The SRHT is d^-1/2 H diag(s) x; H is symmetric and H H = N I, so the same routine inverts it.
+template <int N>
+__host__ __device__ __forceinline__ void wht(float (&y)[N]) {
+#pragma unroll
+  for (int h = 1; h < N; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < N; i += 2 * h) {
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        const float a = y[j], b = y[j + h];
+        y[j] = a + b;
+        y[j + h] = a - b;
+      }
+    }
+  }
+}
+
+template <int D>
+__host__ __device__ constexpr float inv_sqrt_d() {
+  return float(1.0 / csqrt(double(D)));
+}
+
 }  // namespace kvqd

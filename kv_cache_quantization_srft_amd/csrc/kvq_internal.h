@@ -18,6 +18,7 @@ struct QuantArgs {
   int64_t lambda_bs;
   void* codes;
   void* scales;
+  int transform;  // 0 = SRFT, 1 = SRHT
 };
 
 struct DequantArgs {
@@ -30,6 +31,7 @@ struct DequantArgs {
   const float* lambda;
   int64_t lambda_bs;
   float* out;
+  int transform;
 };
 
 struct CalibArgs {
@@ -39,6 +41,7 @@ struct CalibArgs {
   const float* sign;
   int64_t sign_bs;
   float* lambda;
+  int transform;
 };
 
 // Split of a decode call into work-groups (shared by the quantized and the fp16 kernels).
@@ -68,6 +71,7 @@ struct DecodeArgs {
   float sm_scale;
   void* workspace;
   float* out;
+  int transform;
 };
 
 struct DecodeF16Args {

@@ -78,7 +78,7 @@ __device__ __forceinline__ float code_at(const uint8_t* __restrict__ row, int c)
   }
 }
 
-template <int D, int BITS, bool HAS_LAMBDA>
+template <int D, int BITS, bool HAS_LAMBDA, bool HAD>
 __global__ __launch_bounds__(kQuantThreads) void dequantize_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int n_tok, int kv_heads,
     int tiles_per_row, int pos, int capacity, const float* __restrict__ sign, int64_t sign_bs,
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kQuantThreads) void dequantize_kernel(
   const int h = row - b * kv_heads;
   for (int c = threadIdx.x; c < D; c += blockDim.x) {
     lam[c] = HAS_LAMBDA ? lambda[b * lambda_bs + int64_t(h) * D + c] : 1.0f;
-    sgn[c] = (sign[b * sign_bs + c] < 0.0f ? -1.0f : 1.0f) * inv_norm<D>();
+    sgn[c] = (sign[b * sign_bs + c] < 0.0f ? -1.0f : 1.0f) * (HAD ? inv_sqrt_d<D>() : inv_norm<D>());
   }
   __syncthreads();
   const int t = tile * kQuantThreads + threadIdx.x;
@@ -109,7 +109,12 @@ __global__ __launch_bounds__(kQuantThreads) void dequantize_kernel(
     });
   });
   float y[D];
-  real_inv_raw<D>(a, y);
+  if constexpr (HAD) {
+    static_for<0, D>([&](auto C) { y[decltype(C)::value] = a[decltype(C)::value]; });
+    wht<D>(y);
+  } else {
+    real_inv_raw<D>(a, y);
+  }
   float4* o4 = reinterpret_cast<float4*>(out + (int64_t(row) * n_tok + t) * D);
   static_for<0, D / 4>([&](auto Q) {
     constexpr int q = decltype(Q)::value;
@@ -119,7 +124,7 @@ __global__ __launch_bounds__(kQuantThreads) void dequantize_kernel(
 }
 
 // lambda[b, h, c] = max over the first n_cal tokens of |SRFT(x)_c|; one work-group per row.
-template <int D>
+template <int D, bool HAD>
 __global__ __launch_bounds__(kQuantThreads) void calibrate_kernel(const uint16_t* __restrict__ x, int n_tok,
                                                                   int n_cal, const float* __restrict__ sign,
                                                                   int64_t sign_bs, int kv_heads,
@@ -137,11 +142,17 @@ __global__ __launch_bounds__(kQuantThreads) void calibrate_kernel(const uint16_t
     float y[D];
     load_signed_vector<D>(x + (int64_t(row) * n_tok + (valid ? t : 0)) * D, smask, y);
     float r[D];
-    real_fwd_raw<D>(y, r);
+    if constexpr (HAD) {
+      static_for<0, D>([&](auto C) { r[decltype(C)::value] = y[decltype(C)::value]; });
+      wht<D>(r);
+    } else {
+      real_fwd_raw<D>(y, r);
+    }
     static_for<0, D>([&](auto C) {
       constexpr int c = decltype(C)::value;
       // non-negative floats order like their bit patterns
-      uint32_t v = valid ? __float_as_uint(fabsf(r[c] * fwd_norm<D>(c))) : 0u;
+      const float nrm = HAD ? inv_sqrt_d<D>() : fwd_norm<D>(c);
+      uint32_t v = valid ? __float_as_uint(fabsf(r[c] * nrm)) : 0u;
       for (int off = 32; off > 0; off >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off)));
       if ((threadIdx.x & 63) == 0) atomicMax(&amax[c], v);
     });
@@ -229,7 +240,7 @@ __global__ __launch_bounds__(2 * D) void quantize_mfma_kernel(const uint16_t* __
                                                               const float* __restrict__ sign, int64_t sign_bs,
                                                               const float* __restrict__ lambda, int64_t lambda_bs,
                                                               uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
-                                                              uint32_t n_vec) {
+                                                              uint32_t n_vec, int transform) {
   constexpr int NP = D / 8;         // 16-byte pieces per vector
   constexpr int NSTEP = D / 32;     // k steps of 32 inputs
   constexpr int CB = D * BITS / 8;  // code bytes per vector
@@ -243,7 +254,7 @@ __global__ __launch_bounds__(2 * D) void quantize_mfma_kernel(const uint16_t* __
   const int n16 = lane & 15, r4 = lane >> 4;
 
   // A operands of this wave's two channel blocks (constant for the kernel)
-  const dec::MfmaQTable<D>& T = dec::mqtable<D>();
+  const dec::MfmaQTable<D>& T = dec::mqtable<D>(transform);
   v8h ahi[2][NSTEP], alo[2][NSTEP];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -396,7 +407,7 @@ __global__ __launch_bounds__(2 * D) void quantize_mfma_kernel(const uint16_t* __
 }  // namespace mq
 
 
-template <int D, int BITS>
+template <int D, int BITS, bool HAD>
 hipError_t dequantize_dispatch_lambda(const DequantArgs& a, hipStream_t s) {
   const int rows = a.batch * a.kv_heads;
   const int tiles = (a.n_tok + kQuantThreads - 1) / kQuantThreads;
@@ -404,11 +415,19 @@ hipError_t dequantize_dispatch_lambda(const DequantArgs& a, hipStream_t s) {
   auto* codes = static_cast<const uint8_t*>(a.codes);
   auto* scales = static_cast<const uint16_t*>(a.scales);
   if (a.lambda)
-    hipLaunchKernelGGL((dequantize_kernel<D, BITS, true>), grid, block, 0, s, codes, scales, a.n_tok, a.kv_heads,
-                       tiles, a.pos, a.capacity, a.sign, a.sign_bs, a.lambda, a.lambda_bs, a.out);
+    hipLaunchKernelGGL((dequantize_kernel<D, BITS, true, HAD>), grid, block, 0, s, codes, scales, a.n_tok,
+                       a.kv_heads, tiles, a.pos, a.capacity, a.sign, a.sign_bs, a.lambda, a.lambda_bs, a.out);
   else
-    hipLaunchKernelGGL((dequantize_kernel<D, BITS, false>), grid, block, 0, s, codes, scales, a.n_tok, a.kv_heads,
-                       tiles, a.pos, a.capacity, a.sign, a.sign_bs, a.lambda, a.lambda_bs, a.out);
+    hipLaunchKernelGGL((dequantize_kernel<D, BITS, false, HAD>), grid, block, 0, s, codes, scales, a.n_tok,
+                       a.kv_heads, tiles, a.pos, a.capacity, a.sign, a.sign_bs, a.lambda, a.lambda_bs, a.out);
+  return hipGetLastError();
+}
+
+template <int D, bool HAD>
+hipError_t calibrate_dispatch(const CalibArgs& a, hipStream_t s) {
+  const dim3 grid(a.batch * a.kv_heads), block(kQuantThreads);
+  hipLaunchKernelGGL((calibrate_kernel<D, HAD>), grid, block, 0, s, static_cast<const uint16_t*>(a.x), a.n_tok,
+                     a.n_cal, a.sign, a.sign_bs, a.kv_heads, a.lambda);
   return hipGetLastError();
 }
 
@@ -427,7 +446,7 @@ hipError_t quantize_mfma_dispatch(const QuantArgs& a, hipStream_t s) {
   auto* scales = static_cast<uint16_t*>(a.scales);
 #define KVQ_QLAUNCH(LAM, SH)                                                                                        \
   hipLaunchKernelGGL((mq::quantize_mfma_kernel<D, BITS, LAM, SH>), dim3(grid), dim3(2 * D), 0, s, x, fd_tok, fd_heads, \
-                     a.pos, a.capacity, a.sign, a.sign_bs, a.lambda, a.lambda_bs, codes, scales, n_vec)
+                     a.pos, a.capacity, a.sign, a.sign_bs, a.lambda, a.lambda_bs, codes, scales, n_vec, a.transform)
   const bool shared = a.sign_bs == 0;
   if (a.lambda) {
     if (shared)
@@ -451,21 +470,21 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t s) {
-  if (a.head_dim == 128)
-    return a.bits == 4 ? dequantize_dispatch_lambda<128, 4>(a, s) : dequantize_dispatch_lambda<128, 8>(a, s);
-  return a.bits == 4 ? dequantize_dispatch_lambda<256, 4>(a, s) : dequantize_dispatch_lambda<256, 8>(a, s);
+  const bool had = a.transform != 0;
+  if (a.head_dim == 128) {
+    if (a.bits == 4)
+      return had ? dequantize_dispatch_lambda<128, 4, true>(a, s) : dequantize_dispatch_lambda<128, 4, false>(a, s);
+    return had ? dequantize_dispatch_lambda<128, 8, true>(a, s) : dequantize_dispatch_lambda<128, 8, false>(a, s);
+  }
+  if (a.bits == 4)
+    return had ? dequantize_dispatch_lambda<256, 4, true>(a, s) : dequantize_dispatch_lambda<256, 4, false>(a, s);
+  return had ? dequantize_dispatch_lambda<256, 8, true>(a, s) : dequantize_dispatch_lambda<256, 8, false>(a, s);
 }
 
 hipError_t launch_calibrate(const CalibArgs& a, hipStream_t s) {
-  const dim3 grid(a.batch * a.kv_heads), block(kQuantThreads);
-  auto* x = static_cast<const uint16_t*>(a.x);
-  if (a.head_dim == 128)
-    hipLaunchKernelGGL((calibrate_kernel<128>), grid, block, 0, s, x, a.n_tok, a.n_cal, a.sign, a.sign_bs,
-                       a.kv_heads, a.lambda);
-  else
-    hipLaunchKernelGGL((calibrate_kernel<256>), grid, block, 0, s, x, a.n_tok, a.n_cal, a.sign, a.sign_bs,
-                       a.kv_heads, a.lambda);
-  return hipGetLastError();
+  const bool had = a.transform != 0;
+  if (a.head_dim == 128) return had ? calibrate_dispatch<128, true>(a, s) : calibrate_dispatch<128, false>(a, s);
+  return had ? calibrate_dispatch<256, true>(a, s) : calibrate_dispatch<256, false>(a, s);
 }
 
 }  // namespace kvq_impl

@@ -32,13 +32,20 @@ class KvqError(RuntimeError):
         self.status = status
 
 
+TRANSFORMS = {"srft": 0, "srht": 1}
+
+
 class kvq_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("batch", "kv_heads", "q_heads", "head_dim", "group_size", "k_bits", "v_bits", "capacity")]
+                ("batch", "kv_heads", "q_heads", "head_dim", "group_size", "k_bits", "v_bits", "capacity",
+                 "transform")]
 
 
-def make_layout(batch, kv_heads, q_heads, head_dim, capacity, k_bits=4, v_bits=4, group_size=16) -> kvq_layout:
-    return kvq_layout(batch, kv_heads, q_heads, head_dim, group_size, k_bits, v_bits, capacity)
+def make_layout(batch, kv_heads, q_heads, head_dim, capacity, k_bits=4, v_bits=4, group_size=16,
+                transform="srft") -> kvq_layout:
+    """transform: "srft" (KVQ_TRANSFORM_SRFT) or "srht" (KVQ_TRANSFORM_SRHT), or the enum value."""
+    tr = TRANSFORMS[transform] if isinstance(transform, str) else int(transform)
+    return kvq_layout(batch, kv_heads, q_heads, head_dim, group_size, k_bits, v_bits, capacity, tr)
 
 
 _lib = None

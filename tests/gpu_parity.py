@@ -45,12 +45,12 @@ def planes(layout, bits, fill=0xAB):
     return codes, scales
 
 
-def gpu_quantize(x16, s, lam, bits, capacity=None, pos=0, sign_bs=0, lambda_bs=None):
+def gpu_quantize(x16, s, lam, bits, capacity=None, pos=0, sign_bs=0, lambda_bs=None, transform="srft"):
     """x16 [B, H, n, d] fp16; lam [B?, H, d] or None.  Returns (codes u8 [B,H,cap,d*bits/8],
     scales f16 [B,H,cap,d/16]) as numpy, plus the layout."""
     B, H, n, d = x16.shape
     cap = capacity or (pos + n)
-    lay = kvq.make_layout(B, H, H, d, cap, k_bits=bits, v_bits=4)
+    lay = kvq.make_layout(B, H, H, d, cap, k_bits=bits, v_bits=4, transform=transform)
     codes, scales = planes(lay, bits)
     lam_t = None if lam is None else dev(np.asarray(lam, np.float32))
     if lambda_bs is None:
@@ -104,12 +104,12 @@ def oracle_planes(x16, s, lam, bits):
 
 
 def gpu_decode(q16, kc8, ks16, vc8, vs16, k_bits, s_k, s_v, lam_k, lam_v, seq_len, seq_lens=None, sm_scale=0.0,
-               capacity=None, sign_bs=0, lambda_bs=0, ws=None):
+               capacity=None, sign_bs=0, lambda_bs=0, ws=None, transform="srft"):
     """Run kvq_decode_attn on given unpacked int8 codes (packed here by the oracle's packing)."""
     B, Hkv, S, d = kc8.shape
     Hq = q16.shape[1]
     cap = capacity or S
-    lay = kvq.make_layout(B, Hkv, Hq, d, cap, k_bits=k_bits, v_bits=4)
+    lay = kvq.make_layout(B, Hkv, Hq, d, cap, k_bits=k_bits, v_bits=4, transform=transform)
     kb = O.pack_codes(kc8, k_bits)
     vb = O.pack_codes(vc8, 4)
     if ws is None:

@@ -111,6 +111,14 @@ def test_group_size_unsupported(L):
     assert quantize(L, lay) == 2 and "group_size" in msg(L)
 
 
+def test_transform_field(L):
+    lay = layout(transform="srht")
+    assert lay.transform == 1 and layout().transform == 0
+    lay.transform = 2
+    assert quantize(L, lay) == 2 and "transform" in msg(L)
+    assert decode(L, lay) == 2 and "transform" in msg(L)
+
+
 def test_dequantize_and_calibrate_validation(L):
     lay = layout()
     st = L.kvq_dequantize(ctypes.byref(lay), 8, GOOD, GOOD, 0, 65, GOOD, 0, NULL, 0, GOOD, NULL)
