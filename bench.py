@@ -268,6 +268,12 @@ def main():
         return
 
     def step(p):
+        # one launch: the new token's K and V go through the write path into position S - 1,
+        # then decode attention over all S positions
+        kvq.kvq_decode_attn_append(lay, q, k_new, v_new, p[0], p[1], p[2], p[3], S, None, s, s, 0, lam_k, lam_v,
+                                   lbs, 0.0, ws, out)
+
+    def step_unfused(p):
         kvq.kvq_quantize(lay, w.k_bits, k_new, S - 1, 1, s, 0, lam_k, lbs, p[0], p[1])
         kvq.kvq_quantize(lay, w.v_bits, v_new, S - 1, 1, s, 0, lam_v, lbs, p[2], p[3])
         decode(p)
@@ -276,6 +282,7 @@ def main():
     R = len(planes)
     steps = args.steps if args.steps > 0 else 4 * R
     res_step = timer.run(lambda i: step(planes[i]), R, steps, args.warmup)
+    res_step3 = timer.run(lambda i: step_unfused(planes[i]), R, steps, args.warmup)
     res_dec = timer.run(lambda i: decode(planes[i]), R, steps, args.warmup)
     Rf = len(kv16)
     res_f16 = timer.run(lambda i: kvq.kvq_decode_attn_fp16(lay, q, kv16[i][0], kv16[i][1], S, None, 0.0, ws, out16),
@@ -309,7 +316,10 @@ def main():
                    "lambda": "calibrated (first 512 tokens)" if w.calibrate else "1",
                    "storage": f"int{w.k_bits} K / int{w.v_bits} V codes + fp16 group scales",
                    "parallelism": "single GPU; layers folded into the batch", "cold_cache_copies": R},
-        "step_breakdown": {"step": res_step, "decode_only": res_dec},
+        "step_breakdown": {"step": res_step, "step_three_launches": res_step3, "decode_only": res_dec,
+                           "calls": {"step": "kvq_decode_attn_append (append + decode, one launch)",
+                                     "step_three_launches": "kvq_quantize K, kvq_quantize V, kvq_decode_attn",
+                                     "decode_only": "kvq_decode_attn"}},
         "decode": {"GBps": round(dec_gbps, 2), "frac_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),
                    "bytes_per_step": dec_bytes, "ms": round(res_dec["ms_mean"], 5)},
         "fp16_decode": {"GBps": round(f16_gbps, 2), "frac_hbm_peak": round(f16_gbps / HBM_PEAK_GBPS, 4),

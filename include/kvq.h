@@ -174,6 +174,31 @@ kvq_status kvq_decode_attn(const kvq_layout* layout, const void* q_f16, const vo
                            void* workspace, size_t workspace_bytes, float* out, void* stream);
 
 /*
+ * kvq_decode_attn_append -- one decode step in one launch: the write path ([QF] Methodology 2,
+ * the steps of the fused kernel) on the step's new K and V vectors, then kvq_decode_attn over
+ * the cache that now holds them ([QF] Key results: one vector written per head and step, the
+ * whole prefix read).  For every sequence b with L = seq_lens ? seq_lens[b] : seq_len
+ * (clamped to [0, seq_len]) and L >= 1, and every kv head j, the vectors k_new[b, j] and
+ * v_new[b, j] are quantized into position L - 1 of the planes as kvq_quantize(pos = L - 1,
+ * n_tok = 1) does with the same signs and lambdas (K with layout->k_bits, V with
+ * layout->v_bits); then out is what kvq_decode_attn returns for that cache.  A sequence with
+ * L = 0 is not written and gets a zero output.
+ *   k_new, v_new : fp16 [batch, kv_heads, head_dim] contiguous, 16-byte aligned
+ *   k_codes, ... : the four planes, read and (at L - 1) written
+ *   other arguments, the workspace rules and the error behaviour as kvq_decode_attn, except
+ *   that the head tile is the largest divisor of G that is at most 14 (head_dim 128) or 8
+ *   (head_dim 256).  Positions other than L - 1 are not written.  The codes agree with
+ *   kvq_quantize's to the write path's parity bar (the two use the same arithmetic).
+ */
+kvq_status kvq_decode_attn_append(const kvq_layout* layout, const void* q_f16, const void* k_new_f16,
+                                  const void* v_new_f16, void* k_codes, void* k_scales, void* v_codes,
+                                  void* v_scales, int32_t seq_len, const int32_t* seq_lens,
+                                  const float* sign_k, const float* sign_v, int64_t sign_batch_stride,
+                                  const float* lambda_k, const float* lambda_v,
+                                  int64_t lambda_batch_stride, float sm_scale, void* workspace,
+                                  size_t workspace_bytes, float* out, void* stream);
+
+/*
  * kvq_decode_attn_fp16 -- the same decode attention over an unquantized fp16 cache (the
  * comparator): k_f16, v_f16 are fp16 [batch, kv_heads, capacity, head_dim]; no rotation, no
  * lambda.  layout->k_bits/v_bits are ignored.  Other arguments as kvq_decode_attn.

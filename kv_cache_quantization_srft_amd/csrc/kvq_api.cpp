@@ -91,7 +91,7 @@ kvq_status hip_status(hipError_t e, const char* fn) {
 
 kvq_status check_decode_common(const kvq_layout* L, const void* q, int32_t seq_len, const int32_t* seq_lens,
                                float sm_scale, void* workspace, size_t workspace_bytes, float* out,
-                               const char* fn) {
+                               const char* fn, bool append = false) {
   if (L->q_heads < 1 || L->q_heads % L->kv_heads != 0)
     return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: q_heads (%d) must be a positive multiple of kv_heads (%d)", fn,
                 L->q_heads, L->kv_heads);
@@ -105,7 +105,7 @@ kvq_status check_decode_common(const kvq_layout* L, const void* q, int32_t seq_l
   KVQ_TRY(check_opt_ptr(seq_lens, 4, fn, "seq_lens"));
   {
     const kvq_impl::DecodePlan pl =
-        kvq_impl::plan_decode(L->batch, L->kv_heads, L->q_heads, L->head_dim, seq_len, seq_len, false);
+        kvq_impl::plan_decode(L->batch, L->kv_heads, L->q_heads, L->head_dim, seq_len, seq_len, false, append);
     const long units = long(L->batch) * L->kv_heads * pl.head_tiles;
     if (units > kvq_impl::kMaxDecodeUnits)
       return fail(KVQ_ERR_UNSUPPORTED, "%s: batch x kv_heads x head tiles = %ld exceeds %d", fn, units,
@@ -240,6 +240,41 @@ kvq_status kvq_decode_attn(const kvq_layout* L, const void* q_f16, const void* k
                          v_codes,    v_scales,    sign_k,     sign_v,      sign_batch_stride, lambda_k,
                          lambda_v,   lambda_batch_stride,     scale,       workspace,   out};
   a.transform = L->transform;
+  return hip_status(kvq_impl::launch_decode(a, p, static_cast<hipStream_t>(stream)), fn);
+}
+
+kvq_status kvq_decode_attn_append(const kvq_layout* L, const void* q_f16, const void* k_new_f16,
+                                  const void* v_new_f16, void* k_codes, void* k_scales, void* v_codes,
+                                  void* v_scales, int32_t seq_len, const int32_t* seq_lens, const float* sign_k,
+                                  const float* sign_v, int64_t sign_batch_stride, const float* lambda_k,
+                                  const float* lambda_v, int64_t lambda_batch_stride, float sm_scale,
+                                  void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  const char* fn = "kvq_decode_attn_append";
+  KVQ_TRY(check_layout(L, fn));
+  KVQ_TRY(check_bits(L->k_bits, fn, "k_bits"));
+  if (L->v_bits != 4) return fail(KVQ_ERR_UNSUPPORTED, "%s: v_bits %d (supported: 4)", fn, L->v_bits);
+  KVQ_TRY(check_decode_common(L, q_f16, seq_len, seq_lens, sm_scale, workspace, workspace_bytes, out, fn, true));
+  KVQ_TRY(check_ptr(k_new_f16, 16, fn, "k_new"));
+  KVQ_TRY(check_ptr(v_new_f16, 16, fn, "v_new"));
+  KVQ_TRY(check_ptr(k_codes, 16, fn, "k_codes"));
+  KVQ_TRY(check_ptr(k_scales, 16, fn, "k_scales"));
+  KVQ_TRY(check_ptr(v_codes, 16, fn, "v_codes"));
+  KVQ_TRY(check_ptr(v_scales, 16, fn, "v_scales"));
+  KVQ_TRY(check_ptr(sign_k, 4, fn, "sign_k"));
+  KVQ_TRY(check_ptr(sign_v, 4, fn, "sign_v"));
+  KVQ_TRY(check_opt_ptr(lambda_k, 4, fn, "lambda_k"));
+  KVQ_TRY(check_opt_ptr(lambda_v, 4, fn, "lambda_v"));
+  KVQ_TRY(check_strides(sign_batch_stride, lambda_batch_stride, fn));
+  const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt(float(L->head_dim));
+  const kvq_impl::DecodePlan p =
+      kvq_impl::plan_decode(L->batch, L->kv_heads, L->q_heads, L->head_dim, seq_len, seq_len, false, true);
+  kvq_impl::DecodeArgs a{L->batch,   L->kv_heads, L->q_heads, L->head_dim, L->k_bits,   L->v_bits,
+                         L->capacity, seq_len,    seq_lens,   q_f16,       k_codes,     k_scales,
+                         v_codes,    v_scales,    sign_k,     sign_v,      sign_batch_stride, lambda_k,
+                         lambda_v,   lambda_batch_stride,     scale,       workspace,   out};
+  a.transform = L->transform;
+  a.k_new = k_new_f16;
+  a.v_new = v_new_f16;
   return hip_status(kvq_impl::launch_decode(a, p, static_cast<hipStream_t>(stream)), fn);
 }
 

@@ -67,6 +67,8 @@ struct QGeom {
   static constexpr int LDS_EPI = (kWaves * 16 * 2 + 16 * kWaves + 32 + kWaves * (D == 128 ? 16 : 8) * D) * 4;
   static constexpr int LDS_Q = 4 * NS * 2 * 1024 + 256;  // prologue: digit operands + head maxima
   static constexpr int LDS_M = merge_lds_floats<D>() * 4;
+  // append staging: K codes, K scales, V codes, V scales of the new token (16-byte aligned parts)
+  static constexpr int APP_KS = KRB, APP_V = KRB + NG * 2, APP_VS = APP_V + VRB, APP = APP_VS + NG * 2;
   static constexpr int LDS = cmax(cmax(kWaves * LDS_WAVE, LDS_EPI), cmax(LDS_Q, LDS_M));
 };
 
@@ -155,6 +157,40 @@ __device__ __forceinline__ void load_superblock(SBRegs<D, KB>& r, const uint8_t*
     r.vsw[i + 1] = v.y;
     r.vsw[i + 2] = v.z;
     r.vsw[i + 3] = v.w;
+  }
+}
+
+// Overwrite, in the registers of a loaded superblock, the token at superblock offset tl
+// (wave-uniform) with the new token staged in LDS (app: K codes, K scales, V codes, V scales).
+// The lanes holding each part follow load_superblock's layout.
+template <int D, int KB>
+__device__ __forceinline__ void patch_superblock(SBRegs<D, KB>& r, int tl, const uint8_t* app, int lane) {
+  using Gm = QGeom<D, KB>;
+  const int n16 = lane & 15, r4 = lane >> 4;
+  const uint32_t* ak = reinterpret_cast<const uint32_t*>(app);
+  const uint32_t* aks = reinterpret_cast<const uint32_t*>(app + Gm::APP_KS);
+  const uint4* av = reinterpret_cast<const uint4*>(app + Gm::APP_V);
+  const uint32_t* avs = reinterpret_cast<const uint32_t*>(app + Gm::APP_VS);
+  uint32_t kn[Gm::KLW];
+#pragma unroll
+  for (int i = 0; i < Gm::KLW; ++i) kn[i] = ak[r4 * Gm::KLW + i];
+  // per-lane selects (a uniform branch per block would index the registers dynamically)
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) {
+    const bool hit = 16 * sb + n16 == tl;
+#pragma unroll
+    for (int i = 0; i < Gm::KLW; ++i) r.kw[sb][i] = hit ? kn[i] : r.kw[sb][i];
+  }
+  const bool sl = lane == tl;
+#pragma unroll
+  for (int i = 0; i < Gm::SLW; ++i) {
+    r.ksw[i] = sl ? aks[i] : r.ksw[i];
+    r.vsw[i] = sl ? avs[i] : r.vsw[i];
+  }
+#pragma unroll
+  for (int i = 0; i < Gm::VLU; ++i) {
+    const int byte = (i * 64 + lane) * 16;
+    if (byte / Gm::VRB == tl) r.vw[i] = av[(byte % Gm::VRB) / 16];
   }
 }
 
@@ -351,6 +387,10 @@ struct QDecodeParams {
   float* pml;
   float* pacc;
   MergeArgs merge;
+  // append (k_new == nullptr: none): the new K and V vectors [batch, kv_heads, D] of every
+  // row, quantized into position L - 1 of the planes by the work-group holding that position
+  const uint16_t* k_new;
+  const uint16_t* v_new;
 };
 
 template <int D, int KB, int NRB>
@@ -361,6 +401,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   constexpr int NSTEP = D / 32, NBW = D / 16 / kWaves;
   __shared__ __align__(16) uint8_t smem[Gm::LDS];
   __shared__ int last_flag;
+  __shared__ __align__(16) uint8_t appbuf[Gm::APP];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index (uniform)
   const int n16 = lane & 15, r4 = lane >> 4;
@@ -377,10 +418,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   const int t_begin = ch * P.chunk;
   const int t_end = min(L, t_begin + P.chunk);
   const int64_t rowbase = (int64_t(b) * P.kv_heads + kvh) * P.capacity;
-  const uint8_t* __restrict__ kc = P.kc;
-  const uint16_t* __restrict__ ks = P.ks;
-  const uint8_t* __restrict__ vc = P.vc;
-  const uint16_t* __restrict__ vs = P.vs;
+  // not restrict: an appending call writes one token of these planes
+  const uint8_t* kc = P.kc;
+  const uint16_t* ks = P.ks;
+  const uint8_t* vc = P.vc;
+  const uint16_t* vs = P.vs;
   constexpr int kStride = kWaves * kSB;
 
   // ---------------- prologue: rotated query -> int8 digit operands ----------------
@@ -391,16 +433,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
     lam[j] = (P.lambda_k ? P.lambda_k[b * P.lambda_bs + int64_t(kvh) * D + 16 * (w + kWaves * j) + n16] : 1.0f) *
              P.score_scale * 0.0625f;
   // A = the fp16 query of head row n16, signs flipped in the fp16 bits (exact)
+  // An appending work-group (the one holding position L - 1 of its row; the head tile is then
+  // at most 14) also rotates the new K vector as row 14 (signs s_K) and the new V vector as
+  // row 15 (signs s_V).
+  const int t_app = L - 1;
+  const bool app = P.k_new != nullptr && t_app >= t_begin && t_app < t_end;  // work-group uniform
   uint4 qv[NSTEP];
   float4 sv0[NSTEP], sv1[NSTEP];
+  const uint16_t* qrow = nullptr;
+  const float* srow = P.sign_k + b * P.sign_bs;
+  if (n16 < GT) {
+    qrow = P.q + (int64_t(b) * P.q_heads + h0 + n16) * D;
+  } else if (app && n16 >= 14) {
+    qrow = (n16 == 14 ? P.k_new : P.v_new) + (int64_t(b) * P.kv_heads + kvh) * D;
+    if (n16 == 15) srow = P.merge.sign + b * P.sign_bs;
+  }
 #pragma unroll
   for (int s = 0; s < NSTEP; ++s) {
     qv[s] = make_uint4(0u, 0u, 0u, 0u);
     sv0[s] = sv1[s] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-    if (n16 < GT) {
-      qv[s] = *reinterpret_cast<const uint4*>(P.q + (int64_t(b) * P.q_heads + h0 + n16) * D + 32 * s + 8 * r4);
-      sv0[s] = *reinterpret_cast<const float4*>(P.sign_k + b * P.sign_bs + 32 * s + 8 * r4);
-      sv1[s] = *reinterpret_cast<const float4*>(P.sign_k + b * P.sign_bs + 32 * s + 8 * r4 + 4);
+    if (qrow) {
+      qv[s] = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * r4);
+      sv0[s] = *reinterpret_cast<const float4*>(srow + 32 * s + 8 * r4);
+      sv1[s] = *reinterpret_cast<const float4*>(srow + 32 * s + 8 * r4 + 4);
+    }
+  }
+  float nlk[NBW], nlv[NBW];  // raw lambda_K, lambda_V of this lane's channels (appending only)
+  if (app) {
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      const int64_t c = int64_t(kvh) * D + 16 * (w + kWaves * j) + n16;
+      nlk[j] = P.lambda_k ? P.lambda_k[b * P.lambda_bs + c] : 1.0f;
+      nlv[j] = P.merge.lambda ? P.merge.lambda[b * P.merge.lambda_bs + c] : 1.0f;
     }
   }
 
@@ -440,10 +504,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   }
   __syncthreads();
   // q_hat[h][c] * lambda_c * score_scale for head h = 4 r4 + i and channel c = 16 (w + 4j) + n16
+  // (hi and lo products in separate chains, added at the end, as the write path does)
   float qv_[NBW][4];
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
-    v4f qa = {0.0f, 0.0f, 0.0f, 0.0f};
+    v4f qa = {0.0f, 0.0f, 0.0f, 0.0f}, ql = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       uint4 ph, pl;
@@ -456,10 +521,39 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
       }
       const v8h bh = as_v8h(ph.x, ph.y, ph.z, ph.w), bl = as_v8h(pl.x, pl.y, pl.z, pl.w);
       qa = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], bh, qa, 0, 0, 0);
-      qa = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], bl, qa, 0, 0, 0);
+      ql = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], bl, ql, 0, 0, 0);
     }
+    qa += ql;
 #pragma unroll
     for (int i = 0; i < 4; ++i) qv_[j][i] = qa[i] * lam[j];
+    if (app) {
+      // the write path on rows 14 (K) and 15 (V), lanes 48..63, channel c = 16 g + n16:
+      // u = 16 SRFT(x)_c / (16 lambda_c), group absmax over the row's 16 lanes, fp16 scale,
+      // rounded codes, packed into the LDS staging of the new token
+      const int g = w + kWaves * j;
+      const float uk = qa[2] * __builtin_amdgcn_rcpf(16.0f * nlk[j]);
+      const float uv = qa[3] * __builtin_amdgcn_rcpf(16.0f * nlv[j]);
+      const _Float16 shk = static_cast<_Float16>(scale_of<KB>(row_max16(fabsf(uk))));
+      const _Float16 shv = static_cast<_Float16>(scale_of<4>(row_max16(fabsf(uv))));
+      const float sfk = static_cast<float>(shk), sfv = static_cast<float>(shv);
+      const uint32_t ck = code_byte<KB>(uk, sfk > 0.0f ? __builtin_amdgcn_rcpf(sfk) : 0.0f);
+      const uint32_t cv = code_byte<4>(uv, sfv > 0.0f ? __builtin_amdgcn_rcpf(sfv) : 0.0f);
+      // int4: two's-complement nibbles, the even channel low (odd partner n16 ^ 1 by DPP)
+      const uint32_t nk = (ck ^ 8u) & 0xfu, nvv = (cv ^ 8u) & 0xfu;
+      const uint32_t pk = uint32_t(__builtin_amdgcn_mov_dpp(int(nk), 0xB1, 0xf, 0xf, false));
+      const uint32_t pv = uint32_t(__builtin_amdgcn_mov_dpp(int(nvv), 0xB1, 0xf, 0xf, false));
+      if (r4 == 3) {
+        if constexpr (KB == 8)
+          appbuf[16 * g + n16] = uint8_t(ck ^ 0x80u);
+        else if ((n16 & 1) == 0)
+          appbuf[8 * g + n16 / 2] = uint8_t(nk | (pk << 4));
+        if ((n16 & 1) == 0) appbuf[Gm::APP_V + 8 * g + n16 / 2] = uint8_t(nvv | (pv << 4));
+        if (n16 == 0) {
+          reinterpret_cast<uint16_t*>(appbuf + Gm::APP_KS)[g] = __builtin_bit_cast(uint16_t, shk);
+          reinterpret_cast<uint16_t*>(appbuf + Gm::APP_VS)[g] = __builtin_bit_cast(uint16_t, shv);
+        }
+      }
+    }
   }
   // per-head maximum of |q_hat| over this wave's channels (16-lane DPP rows), then over waves
 #pragma unroll
@@ -471,6 +565,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
     if (n16 == 0) pmax[w * 16 + 4 * r4 + i] = m;
   }
   __syncthreads();
+  if (app && ht == 0) {
+    // the new token leaves for the planes (every head tile patches its own registers)
+    constexpr int UK = Gm::KRB / 16, US = NG * 2 / 16, UV = Gm::VRB / 16;
+    const int tid = threadIdx.x;
+    const int64_t slot = rowbase + t_app;
+    if (tid < UK) {
+      *reinterpret_cast<uint4*>(const_cast<uint8_t*>(kc) + slot * Gm::KRB + 16 * tid) =
+          *reinterpret_cast<const uint4*>(appbuf + 16 * tid);
+    } else if (tid < UK + US) {
+      const int u = tid - UK;
+      *reinterpret_cast<uint4*>(const_cast<uint16_t*>(ks) + slot * NG + 8 * u) =
+          *reinterpret_cast<const uint4*>(appbuf + Gm::APP_KS + 16 * u);
+    } else if (tid < UK + US + UV) {
+      const int u = tid - UK - US;
+      *reinterpret_cast<uint4*>(const_cast<uint8_t*>(vc) + slot * Gm::VRB + 16 * u) =
+          *reinterpret_cast<const uint4*>(appbuf + Gm::APP_V + 16 * u);
+    } else if (tid < UK + 2 * US + UV) {
+      const int u = tid - UK - US - UV;
+      *reinterpret_cast<uint4*>(const_cast<uint16_t*>(vs) + slot * NG + 8 * u) =
+          *reinterpret_cast<const uint4*>(appbuf + Gm::APP_VS + 16 * u);
+    }
+  }
   // per-head step: the largest |q_hat| maps to 32639 so both digits fit int8
   float sgm[4];
   {
@@ -559,6 +675,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   for (int g = 0; g < NG; ++g) acc[g] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   while (base < t_end) {
+    if (app && t_app >= base && t_app < base + kSB) patch_superblock<D, KB>(ra, t_app - base, appbuf, lane);
     process_superblock<D, KB, NRB>(ra, base, t_end, lane, aop, sig, m_run, l_run, acc, vtile, stile, ktile, ptile,
                                    atile, kc, ks, vc, vs, rowbase, base + kStride, L);
     base += kStride;
@@ -614,6 +731,8 @@ hipError_t launch_q(const DecodeArgs& a, const DecodePlan& p, const WsLayout& w,
   P.merge = MergeArgs{P.pml,      P.pacc,     p.n_chunks, p.max_chunks, p.head_tile, p.head_tiles,
                       a.q_heads,  a.kv_heads, 16.0f,      a.sign_v,     a.sign_bs,   a.lambda_v,
                       a.lambda_bs, a.out,     a.transform};
+  P.k_new = static_cast<const uint16_t*>(a.k_new);
+  P.v_new = static_cast<const uint16_t*>(a.v_new);
   const dim3 grid(units * p.n_chunks), block(kThreads);
   switch ((p.head_tile + 3) / 4) {
     case 1:

@@ -324,4 +324,38 @@ __host__ __device__ constexpr float inv_sqrt_d() {
   return float(1.0 / csqrt(double(D)));
 }
 
+// ---- the code decision of the write path (group absmax -> fp16 scale -> rounded codes) ----
+
+// Rounding by the float32 "magic number": for |v| <= 2^22, fma(u, inv, M) with M = 2^23 + off
+// rounds u*inv to the nearest integer (ties to even, as M + off is even) and leaves
+// off + code in the low mantissa bits.  With off = 8 (int4) / 128 (int8) and codes clamped to
+// [-qmax, qmax], byte 0 of the bit pattern is the offset-binary code and nothing above it
+// within the byte is set.
+template <int BITS>
+struct CodeMagic {
+  static constexpr float qmax = BITS == 4 ? 7.0f : 127.0f;
+  static constexpr float magic = BITS == 4 ? 8388616.0f : 8388736.0f;  // 2^23 + 8 / 2^23 + 128
+  static constexpr uint32_t to_twos = BITS == 4 ? 0x88888888u : 0x80808080u;
+};
+
+// fp32 a / qmax, correctly rounded (reciprocal product plus one exact residual correction),
+// saturated at the fp16 maximum
+template <int BITS>
+__device__ __forceinline__ float scale_of(float a) {
+  constexpr float q = BITS == 4 ? 7.0f : 127.0f;
+  constexpr float rq = 1.0f / q;
+  const float y = a * rq;
+  const float r = fmaf(-y, q, a);
+  return fminf(fmaf(r, rq, y), 65504.0f);
+}
+
+// Offset-binary code byte (code + 8 or code + 128) of u under the reciprocal scale inv.
+template <int BITS>
+__device__ __forceinline__ uint32_t code_byte(float u, float inv) {
+  using CM = CodeMagic<BITS>;
+  float vq = fmaf(u, inv, CM::magic);
+  vq = fminf(fmaxf(vq, CM::magic - CM::qmax), CM::magic + CM::qmax);
+  return __float_as_uint(vq) & 0xffu;
+}
+
 }  // namespace kvqd

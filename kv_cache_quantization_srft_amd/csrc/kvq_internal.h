@@ -72,6 +72,10 @@ struct DecodeArgs {
   void* workspace;
   float* out;
   int transform;
+  // append (nullptr: none): new K and V vectors [batch, kv_heads, head_dim] fp16, quantized into
+  // position L - 1 of every row before it is attended (the planes above are then written)
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
 };
 
 struct DecodeF16Args {
@@ -111,7 +115,8 @@ __host__ __device__ inline WsLayout ws_layout(int units, int head_tile, int head
 }
 
 // Host-side planning (pure host code, no HIP call).
-DecodePlan plan_decode(int batch, int kv_heads, int q_heads, int head_dim, int seq_len, int max_seq_len, bool f16);
+DecodePlan plan_decode(int batch, int kv_heads, int q_heads, int head_dim, int seq_len, int max_seq_len, bool f16,
+                       bool append = false);
 size_t decode_workspace_bytes(int batch, int kv_heads, int q_heads, int head_dim, int max_seq_len);
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);

@@ -16,10 +16,13 @@ int token_align(bool f16) { return f16 ? 4 * 32 : 4 * 64; }  // 4 waves x superb
 
 }  // namespace
 
-DecodePlan plan_decode(int batch, int kv_heads, int q_heads, int head_dim, int seq_len, int max_seq_len, bool f16) {
+DecodePlan plan_decode(int batch, int kv_heads, int q_heads, int head_dim, int seq_len, int max_seq_len, bool f16,
+                       bool append) {
   DecodePlan p{};
   const int G = q_heads / kv_heads;
-  const int max_tile = head_dim == 128 ? 16 : 8;  // epilogue LDS holds 4 x tile x d floats
+  // epilogue LDS holds 4 x tile x d floats; an appending call rotates the new K and V vectors
+  // in rows 14 and 15 of the query rotation
+  const int max_tile = head_dim == 128 ? (append ? 14 : 16) : 8;
   int tile = 1;
   for (int t = std::min(G, max_tile); t >= 1; --t)
     if (G % t == 0) {
@@ -45,8 +48,9 @@ DecodePlan plan_decode(int batch, int kv_heads, int q_heads, int head_dim, int s
 
 size_t decode_workspace_bytes(int batch, int kv_heads, int q_heads, int head_dim, int max_seq_len) {
   size_t need = 0;
-  for (bool f16 : {false, true}) {
-    const DecodePlan p = plan_decode(batch, kv_heads, q_heads, head_dim, max_seq_len, max_seq_len, f16);
+  for (int variant = 0; variant < 3; ++variant) {
+    const DecodePlan p =
+        plan_decode(batch, kv_heads, q_heads, head_dim, max_seq_len, max_seq_len, variant == 1, variant == 2);
     const WsLayout w = ws_layout(batch * kv_heads * p.head_tiles, p.head_tile, head_dim, p.max_chunks);
     need = std::max(need, w.total);
   }

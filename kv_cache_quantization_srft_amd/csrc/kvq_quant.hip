@@ -23,18 +23,6 @@ using namespace kvqd;
 
 constexpr int kQuantThreads = 256;
 
-// Rounding by the float32 "magic number": for |v| <= 2^22, fma(u, inv, M) with M = 2^23 + off
-// rounds u*inv to the nearest integer (ties to even, as M + off is even) and leaves
-// off + code in the low mantissa bits.  With off = 8 (int4) / 128 (int8) and codes clamped to
-// [-qmax, qmax], byte 0 of the bit pattern is the offset-binary code and nothing above it
-// within the byte is set.
-template <int BITS>
-struct CodeMagic {
-  static constexpr float qmax = BITS == 4 ? 7.0f : 127.0f;
-  static constexpr float magic = BITS == 4 ? 8388616.0f : 8388736.0f;  // 2^23 + 8 / 2^23 + 128
-  static constexpr uint32_t to_twos = BITS == 4 ? 0x88888888u : 0x80808080u;
-};
-
 
 // Stage the sign flips of row b as fp16 sign-bit masks (one dword = two channels).
 template <int D>
@@ -199,16 +187,6 @@ using dec::v8h;
 using dec::v4f;
 
 constexpr int kVecs = 16;  // vectors per block (MFMA columns)
-
-template <int BITS>
-__device__ __forceinline__ float scale_of(float a) {
-  // fp32 a / qmax, correctly rounded (reciprocal product plus one exact residual correction)
-  constexpr float q = BITS == 4 ? 7.0f : 127.0f;
-  constexpr float rq = 1.0f / q;
-  const float y = a * rq;
-  const float r = fmaf(-y, q, a);
-  return fminf(fmaf(r, rq, y), 65504.0f);
-}
 
 // max over the four 16-lane rows for every lane position (v_permlane32_swap, v_permlane16_swap)
 // of a non-negative float given as its bit pattern (non-negative floats order like their bits)

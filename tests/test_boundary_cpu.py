@@ -195,3 +195,31 @@ def test_binding_requires_device_tensors(L):
     x = torch.zeros(2 * 2 * 4 * 128, dtype=torch.float16)
     with pytest.raises(ValueError):
         kvq.kvq_quantize(lay, 4, x, 0, 4, x, 0, None, 0, x, x, stream=0)
+
+
+def append(L, lay, q=GOOD, k_new=GOOD, v_new=GOOD, seq_len=16, ws_bytes=1 << 30, kc=GOOD):
+    return L.kvq_decode_attn_append(ctypes.byref(lay), q, k_new, v_new, kc, GOOD, GOOD, GOOD, seq_len, NULL, GOOD,
+                                    GOOD, 0, NULL, NULL, 0, ctypes.c_float(0.0), GOOD, ws_bytes, GOOD, NULL)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(k_new=NULL), 1, "k_new is NULL"),
+    (dict(v_new=MIS), 3, "v_new is not"),
+    (dict(kc=MIS), 3, "k_codes"),
+    (dict(seq_len=65), 1, "seq_len"),
+    (dict(lay=dict(v_bits=8)), 2, "v_bits"),
+    (dict(ws_bytes=16), 4, "workspace has 16 bytes"),
+])
+def test_append_validation(L, kw, status, needle):
+    lay = layout(**kw.pop("lay", {}))
+    assert append(L, lay, **kw) == status
+    assert needle in msg(L)
+
+
+def test_append_head_tile_limit(L):
+    # G = 16 at d = 128: kvq_decode_attn uses one head tile of 16, the appending call two of 8
+    # (rows 14 and 15 of its query rotation carry the new K and V), so its unit count doubles
+    # (both calls fail validation: the first only at the workspace size, after the unit check)
+    lay = layout(batch=8193, kv_heads=1, q_heads=16)
+    assert decode(L, lay, ws_bytes=16) == 4 and "workspace has 16 bytes" in msg(L)
+    assert append(L, lay, ws_bytes=16) == 2 and "exceeds 16384" in msg(L)
