@@ -427,45 +427,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
 
   // ---------------- prologue: rotated query -> int8 digit operands ----------------
   // Its few loads go out first (loads complete in issue order), then the first superblock's.
-  float lam[NBW];
-#pragma unroll
-  for (int j = 0; j < NBW; ++j)
-    lam[j] = (P.lambda_k ? P.lambda_k[b * P.lambda_bs + int64_t(kvh) * D + 16 * (w + kWaves * j) + n16] : 1.0f) *
-             P.score_scale * 0.0625f;
-  // A = the fp16 query of head row n16, signs flipped in the fp16 bits (exact)
-  // An appending work-group (the one holding position L - 1 of its row; the head tile is then
-  // at most 14) also rotates the new K vector as row 14 (signs s_K) and the new V vector as
-  // row 15 (signs s_V).
+  // Every load here is unconditional (absent rows and a null lambda read valid memory whose
+  // value is then discarded), so that all of them are in flight together.
+  // A = the fp16 query of head row n16, signs flipped in the fp16 bits (exact).  An appending
+  // work-group (the one holding position L - 1 of its row; the head tile is then at most 14)
+  // also rotates the new K vector as row 14 (signs s_K) and the new V vector as row 15 (s_V).
   const int t_app = L - 1;
   const bool app = P.k_new != nullptr && t_app >= t_begin && t_app < t_end;  // work-group uniform
+  const bool nrow = app && n16 >= 14;
+  const bool live = n16 < GT || nrow;
+  const float* srow_k = P.sign_k + b * P.sign_bs;
+  const uint16_t* qrow = nrow ? (n16 == 14 ? P.k_new : P.v_new) + (int64_t(b) * P.kv_heads + kvh) * D
+                              : P.q + (int64_t(b) * P.q_heads + h0 + min(n16, GT - 1)) * D;
+  const float* srow = nrow && n16 == 15 ? P.merge.sign + b * P.sign_bs : srow_k;
   uint4 qv[NSTEP];
   float4 sv0[NSTEP], sv1[NSTEP];
-  const uint16_t* qrow = nullptr;
-  const float* srow = P.sign_k + b * P.sign_bs;
-  if (n16 < GT) {
-    qrow = P.q + (int64_t(b) * P.q_heads + h0 + n16) * D;
-  } else if (app && n16 >= 14) {
-    qrow = (n16 == 14 ? P.k_new : P.v_new) + (int64_t(b) * P.kv_heads + kvh) * D;
-    if (n16 == 15) srow = P.merge.sign + b * P.sign_bs;
-  }
 #pragma unroll
   for (int s = 0; s < NSTEP; ++s) {
-    qv[s] = make_uint4(0u, 0u, 0u, 0u);
-    sv0[s] = sv1[s] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-    if (qrow) {
-      qv[s] = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * r4);
-      sv0[s] = *reinterpret_cast<const float4*>(srow + 32 * s + 8 * r4);
-      sv1[s] = *reinterpret_cast<const float4*>(srow + 32 * s + 8 * r4 + 4);
-    }
+    qv[s] = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * r4);
+    sv0[s] = *reinterpret_cast<const float4*>(srow + 32 * s + 8 * r4);
+    sv1[s] = *reinterpret_cast<const float4*>(srow + 32 * s + 8 * r4 + 4);
   }
-  float nlk[NBW], nlv[NBW];  // raw lambda_K, lambda_V of this lane's channels (appending only)
-  if (app) {
+  // lambda_K and lambda_V of this lane's channels c = 16 (w + 4 j) + n16 (1 where absent)
+  const int64_t lofs = b * P.lambda_bs + int64_t(kvh) * D;
+  const float* lkrow = P.lambda_k ? P.lambda_k + lofs : srow_k;
+  const float* lvrow = P.merge.lambda ? P.merge.lambda + lofs : srow_k;
+  float nlk[NBW], nlv[NBW];
 #pragma unroll
-    for (int j = 0; j < NBW; ++j) {
-      const int64_t c = int64_t(kvh) * D + 16 * (w + kWaves * j) + n16;
-      nlk[j] = P.lambda_k ? P.lambda_k[b * P.lambda_bs + c] : 1.0f;
-      nlv[j] = P.merge.lambda ? P.merge.lambda[b * P.merge.lambda_bs + c] : 1.0f;
-    }
+  for (int j = 0; j < NBW; ++j) {
+    nlk[j] = lkrow[16 * (w + kWaves * j) + n16];
+    nlv[j] = lvrow[16 * (w + kWaves * j) + n16];
   }
 
   // The B operands of this wave's channel blocks come from the global forward table (16 Q as
@@ -491,10 +482,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   float* pmax = reinterpret_cast<float*>(smem + kDigBytes);  // [kWaves][16]
   for (int i = threadIdx.x; i < kDigBytes / 16; i += kThreads)
     reinterpret_cast<uint4*>(dig)[i] = make_uint4(0u, 0u, 0u, 0u);
+  float lam[NBW];
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) {
+    nlk[j] = P.lambda_k ? nlk[j] : 1.0f;
+    nlv[j] = P.merge.lambda ? nlv[j] : 1.0f;
+    lam[j] = nlk[j] * P.score_scale * 0.0625f;
+  }
   v8h aq[NSTEP];
 #pragma unroll
   for (int s = 0; s < NSTEP; ++s) {
-    uint4 v = qv[s];
+    uint4 v = live ? qv[s] : make_uint4(0u, 0u, 0u, 0u);
     const float4 s0 = sv0[s], s1 = sv1[s];
     v.x ^= (s0.x < 0.0f ? 0x8000u : 0u) | (s0.y < 0.0f ? 0x80000000u : 0u);
     v.y ^= (s0.z < 0.0f ? 0x8000u : 0u) | (s0.w < 0.0f ? 0x80000000u : 0u);
