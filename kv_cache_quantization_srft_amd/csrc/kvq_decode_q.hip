@@ -194,6 +194,18 @@ __device__ __forceinline__ void patch_superblock(SBRegs<D, KB>& r, int tl, const
   }
 }
 
+// c + a * h, with h the low (HI = 0) or high (HI = 1) fp16 half of h2, in one instruction
+// (the conversion of h is exact, so this equals fmaf(a, float(h), c))
+template <int HI>
+__device__ __forceinline__ float fma_mix_f16(float a, uint32_t h2, float c) {
+  float d;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(d) : "v"(a), "v"(h2), "v"(c));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[0,1,0]" : "=v"(d) : "v"(a), "v"(h2), "v"(c));
+  return d;
+}
+
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -218,13 +230,16 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB>& r, int base, i
 #pragma unroll
   for (int i = 0; i < Gm::VLU; ++i) *reinterpret_cast<uint4*>(vtile + (i * 64 + lane) * 16) = r.vw[i];
   {
-    const bool valid = base + lane < t_end;
+    // scale / 16 keeps code * scale inside the fp16 range (undone by the merge).  No mask is
+    // needed: a superblock never crosses a chunk end (chunks are whole multiples of the
+    // work-group stride), so its tokens past t_end are past the row end, where the loads
+    // returned zero.  (Kept in float: a packed-half multiply here was miscompiled, both
+    // halves stored from the low-half product.)
     const int pos = 16 * (lane >> 4) + kpos16(lane & 15);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const uint32_t bits = (r.vsw[g >> 1] >> (16 * (g & 1))) & 0xffffu;
-      // scale / 16 keeps code * scale inside the fp16 range; undone by the merge
-      const float sv = valid ? static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(bits))) * 0.0625f : 0.0f;
+      const float sv = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(bits))) * 0.0625f;
       stile[g * kSB + pos] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(sv));
     }
     uint32_t* kt = reinterpret_cast<uint32_t*>(ktile + lane * NG);
@@ -260,7 +275,6 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB>& r, int base, i
       }
     }
     // the fp16 group scales stay packed; the FMA takes them as fp16 operands (v_fma_mix_f32)
-    const v2h* ksp = reinterpret_cast<const v2h*>(kraw);
     const bool valid = base + 16 * sb + n16 < t_end;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
@@ -273,7 +287,9 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB>& r, int base, i
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int dot = chi[i] * 256 + clo[i];
-          s_acc = fmaf(static_cast<float>(dot), static_cast<float>(ksp[(i * NS + s) >> 1][(i * NS + s) & 1]), s_acc);
+          const int gi = i * NS + s;
+          s_acc = (gi & 1) ? fma_mix_f16<1>(static_cast<float>(dot), kraw[gi >> 1], s_acc)
+                           : fma_mix_f16<0>(static_cast<float>(dot), kraw[gi >> 1], s_acc);
         }
       }
       sc[sb][rb] = valid ? s_acc * sig[rb] : -INFINITY;
