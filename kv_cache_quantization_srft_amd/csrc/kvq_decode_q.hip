@@ -115,20 +115,15 @@ __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, int off) {
 
 // Loads of the superblock starting at token `base` (wave-uniform) of one (sequence, kv head)
 // row; L = the row's token count.  The resources start at the superblock, so every lane offset
-// is a constant and the address arithmetic is scalar.
+// is a constant and the address arithmetic is scalar.  Two parts: the K codes (consumed by the
+// scores) and the rest (V codes, V scales, K scales: staged in LDS first thing), so that the
+// rest of the next superblock can be requested as soon as this one's is staged.
 template <int D, int KB>
-__device__ __forceinline__ void load_superblock(SBRegs<D, KB>& r, const uint8_t* __restrict__ kc,
-                                                const uint16_t* __restrict__ ks, const uint8_t* __restrict__ vc,
-                                                const uint16_t* __restrict__ vs, int64_t rowbase, int base, int L,
-                                                int lane) {
+__device__ __forceinline__ void load_sb_kcodes(SBRegs<D, KB>& r, const uint8_t* kc, int64_t rowbase, int base, int L,
+                                               int lane) {
   using Gm = QGeom<D, KB>;
   const int n16 = lane & 15, r4 = lane >> 4;
-  const int nrem = L - base;
-  const int64_t t0 = rowbase + base;
-  const __amdgpu_buffer_rsrc_t rk = row_rsrc(kc + t0 * Gm::KRB, nrem * Gm::KRB);
-  const __amdgpu_buffer_rsrc_t rks = row_rsrc(ks + t0 * Gm::NG, nrem * Gm::NG * 2);
-  const __amdgpu_buffer_rsrc_t rv = row_rsrc(vc + t0 * Gm::VRB, nrem * Gm::VRB);
-  const __amdgpu_buffer_rsrc_t rvs = row_rsrc(vs + t0 * Gm::NG, nrem * Gm::NG * 2);
+  const __amdgpu_buffer_rsrc_t rk = row_rsrc(kc + (rowbase + base) * Gm::KRB, (L - base) * Gm::KRB);
 #pragma unroll
   for (int sb = 0; sb < 4; ++sb) {
 #pragma unroll
@@ -140,6 +135,17 @@ __device__ __forceinline__ void load_superblock(SBRegs<D, KB>& r, const uint8_t*
       r.kw[sb][i + 3] = v.w;
     }
   }
+}
+
+template <int D, int KB>
+__device__ __forceinline__ void load_sb_rest(SBRegs<D, KB>& r, const uint16_t* ks, const uint8_t* vc,
+                                             const uint16_t* vs, int64_t rowbase, int base, int L, int lane) {
+  using Gm = QGeom<D, KB>;
+  const int nrem = L - base;
+  const int64_t t0 = rowbase + base;
+  const __amdgpu_buffer_rsrc_t rks = row_rsrc(ks + t0 * Gm::NG, nrem * Gm::NG * 2);
+  const __amdgpu_buffer_rsrc_t rv = row_rsrc(vc + t0 * Gm::VRB, nrem * Gm::VRB);
+  const __amdgpu_buffer_rsrc_t rvs = row_rsrc(vs + t0 * Gm::NG, nrem * Gm::NG * 2);
 #pragma unroll
   for (int i = 0; i < Gm::SLW; i += 4) {
     const uint4 v = buf_ld16(rks, lane * Gm::NG * 2 + 4 * i);
@@ -158,6 +164,14 @@ __device__ __forceinline__ void load_superblock(SBRegs<D, KB>& r, const uint8_t*
     r.vsw[i + 2] = v.z;
     r.vsw[i + 3] = v.w;
   }
+}
+
+template <int D, int KB>
+__device__ __forceinline__ void load_superblock(SBRegs<D, KB>& r, const uint8_t* kc, const uint16_t* ks,
+                                                const uint8_t* vc, const uint16_t* vs, int64_t rowbase, int base,
+                                                int L, int lane) {
+  load_sb_kcodes<D, KB>(r, kc, rowbase, base, L, lane);
+  load_sb_rest<D, KB>(r, ks, vc, vs, rowbase, base, L, lane);
 }
 
 // Overwrite, in the registers of a loaded superblock, the token at superblock offset tl
@@ -247,6 +261,8 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB>& r, int base, i
     for (int i = 0; i < Gm::SLW; i += 4)
       *reinterpret_cast<uint4*>(kt + i) = make_uint4(r.ksw[i], r.ksw[i + 1], r.ksw[i + 2], r.ksw[i + 3]);
   }
+  // the staged parts of the next superblock load during this one's scores, softmax and values
+  if (next_base < t_end) load_sb_rest<D, KB>(r, ks, vc, vs, rowbase, next_base, L, lane);
   wave_sync_lds();
 
   // ---------------- scores (int8 MFMA, exact integer group dots) ----------------
@@ -296,8 +312,8 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB>& r, int base, i
     }
   }
 
-  // the registers of this superblock are consumed: the next one loads during softmax + values
-  if (next_base < t_end) load_superblock<D, KB>(r, kc, ks, vc, vs, rowbase, next_base, L, lane);
+  // the K codes of this superblock are consumed: the next one's load during softmax + values
+  if (next_base < t_end) load_sb_kcodes<D, KB>(r, kc, rowbase, next_base, L, lane);
 
   // ---------------- online softmax per head (16-lane rows) ----------------
   bool rescale = false;
