@@ -63,7 +63,7 @@ class Timer:
     def __init__(self, torch):
         self.torch = torch
 
-    def run(self, step_fn, n_copies, steps, warmup, repeats=3):
+    def run(self, step_fn, n_copies, steps, warmup, repeats=7):
         torch = self.torch
         if warmup > 0:
             gw = capture(torch, lambda: [step_fn(i % n_copies) for i in range(warmup)])
@@ -84,10 +84,11 @@ class Timer:
             wall = time.perf_counter() - t0
             times.append((e0.elapsed_time(e1), wall))
         del g
-        first = times[0]
-        per = [t / steps for t, _ in times]
-        return {"ms_mean": first[0] / steps, "wall_ms_per_step": 1e3 * first[1] / steps,
-                "ms_repeats": per, "ms_min": min(per), "ms_max": max(per)}
+        per = np.array([t / steps for t, _ in times])
+        return {"ms_mean": float(per.mean()), "ms_median": float(np.median(per)),
+                "ms_p10": float(np.percentile(per, 10)), "ms_p90": float(np.percentile(per, 90)),
+                "ms_min": float(per.min()), "ms_max": float(per.max()), "repeats": repeats, "steps": steps,
+                "wall_ms_per_step": 1e3 * float(np.mean([w for _, w in times])) / steps}
 
 
 def capture(torch, fn):
@@ -284,6 +285,31 @@ def main():
     res_step = timer.run(lambda i: step(planes[i]), R, steps, args.warmup)
     res_step3 = timer.run(lambda i: step_unfused(planes[i]), R, steps, args.warmup)
     res_dec = timer.run(lambda i: decode(planes[i]), R, steps, args.warmup)
+    # Mode B: the model's cadence, one decode launch per layer (batch B each), L launches a step
+    lay_l = kvq.make_layout(B, H, Hq, d, S, k_bits=w.k_bits, v_bits=w.v_bits, transform=args.transform)
+    qv_l, out_l = q.view(L, -1), out.view(L, -1)
+    lk_l = None if lam_k is None else lam_k.view(L, -1)
+    lv_l = None if lam_v is None else lam_v.view(L, -1)
+    views = [[tuple(t.view(L, -1)[l] for t in planes[i]) for l in range(L)] for i in range(R)]
+
+    def decode_per_layer(i):
+        for l in range(L):
+            p = views[i][l]
+            kvq.kvq_decode_attn(lay_l, qv_l[l], p[0], p[1], p[2], p[3], S, None, s, s, 0,
+                                None if lk_l is None else lk_l[l], None if lv_l is None else lv_l[l], lbs, 0.0, ws,
+                                out_l[l])
+
+    steps_b = min(steps, max(8, 4096 // L))
+    res_dec_b = timer.run(decode_per_layer, R, steps_b, min(args.warmup, 2))
+
+    # achievable bandwidth: a plain device copy of 1 GiB (read + write)
+    src = torch.empty(PMC_COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    res_copy = timer.run(lambda i: dst.copy_(src), 1, 4, 1)
+    copy_gbps = 2 * PMC_COPY_BYTES / (res_copy["ms_median"] * 1e-3) / 1e9
+    del src, dst
+
     Rf = len(kv16)
     res_f16 = timer.run(lambda i: kvq.kvq_decode_attn_fp16(lay, q, kv16[i][0], kv16[i][1], S, None, 0.0, ws, out16),
                         Rf, max(steps, 4 * Rf), args.warmup)
@@ -321,7 +347,15 @@ def main():
                                      "step_three_launches": "kvq_quantize K, kvq_quantize V, kvq_decode_attn",
                                      "decode_only": "kvq_decode_attn"}},
         "decode": {"GBps": round(dec_gbps, 2), "frac_hbm_peak": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                   "bytes_per_step": dec_bytes, "ms": round(res_dec["ms_mean"], 5)},
+                   "frac_of_copy_bandwidth": round(dec_gbps / copy_gbps, 4),
+                   "bytes_per_step": dec_bytes, "ms": round(res_dec["ms_mean"], 5),
+                   "ms_median_p10_p90": [round(res_dec[k], 5) for k in ("ms_median", "ms_p10", "ms_p90")]},
+        "decode_per_layer_launches": {
+            "launches_per_step": L, "ms": round(res_dec_b["ms_median"], 5),
+            "GBps": round(dec_bytes / (res_dec_b["ms_median"] * 1e-3) / 1e9, 2),
+            "note": "mode B: one kvq_decode_attn per layer (batch B), all in one HIP graph"},
+        "copy_1GiB": {"GBps": round(copy_gbps, 2), "frac_hbm_peak": round(copy_gbps / HBM_PEAK_GBPS, 4),
+                      "ms": round(res_copy["ms_median"], 5)},
         "fp16_decode": {"GBps": round(f16_gbps, 2), "frac_hbm_peak": round(f16_gbps / HBM_PEAK_GBPS, 4),
                         "bytes_per_step": f16_bytes, "ms": round(res_f16["ms_mean"], 5),
                         "speedup_quantized_vs_fp16": round(res_f16["ms_mean"] / res_dec["ms_mean"], 3),

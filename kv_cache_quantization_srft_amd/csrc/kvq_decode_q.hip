@@ -68,7 +68,7 @@ struct QGeom {
   static constexpr int LDS_Q = 4 * NS * 2 * 1024 + 256;  // prologue: digit operands + head maxima
   static constexpr int LDS_M = merge_lds_floats<D>() * 4;
   // append staging: K codes, K scales, V codes, V scales of the new token (16-byte aligned parts)
-  static constexpr int APP_KS = KRB, APP_V = KRB + NG * 2, APP_VS = APP_V + VRB, APP = APP_VS + NG * 2;
+  static constexpr int APP_KS = KRB, APP_V = KRB + NG * 2, APP_VS = APP_V + VRB, APP_BYTES = APP_VS + NG * 2;
   static constexpr int LDS = cmax(cmax(kWaves * LDS_WAVE, LDS_EPI), cmax(LDS_Q, LDS_M));
 };
 
@@ -425,7 +425,9 @@ struct QDecodeParams {
   const uint16_t* v_new;
 };
 
-template <int D, int KB, int NRB>
+// APP: the appending variant (kvq_decode_attn_append), a separate instance so that the plain
+// decode carries none of its code.
+template <int D, int KB, int NRB, bool APP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1))) void decode_kernel(
     const QDecodeParams P) {
   using Gm = QGeom<D, KB>;
@@ -433,7 +435,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   constexpr int NSTEP = D / 32, NBW = D / 16 / kWaves;
   __shared__ __align__(16) uint8_t smem[Gm::LDS];
   __shared__ int last_flag;
-  __shared__ __align__(16) uint8_t appbuf[Gm::APP];
+  __shared__ __align__(16) uint8_t appbuf[Gm::APP_BYTES];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index (uniform)
   const int n16 = lane & 15, r4 = lane >> 4;
@@ -465,7 +467,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   // work-group (the one holding position L - 1 of its row; the head tile is then at most 14)
   // also rotates the new K vector as row 14 (signs s_K) and the new V vector as row 15 (s_V).
   const int t_app = L - 1;
-  const bool app = P.k_new != nullptr && t_app >= t_begin && t_app < t_end;  // work-group uniform
+  const bool app = APP && t_app >= t_begin && t_app < t_end;  // work-group uniform
   const bool nrow = app && n16 >= 14;
   const bool live = n16 < GT || nrow;
   const float* srow_k = P.sign_k + b * P.sign_bs;
@@ -764,22 +766,29 @@ hipError_t launch_q(const DecodeArgs& a, const DecodePlan& p, const WsLayout& w,
   P.k_new = static_cast<const uint16_t*>(a.k_new);
   P.v_new = static_cast<const uint16_t*>(a.v_new);
   const dim3 grid(units * p.n_chunks), block(kThreads);
+  const bool app = a.k_new != nullptr;
+#define KVQ_DLAUNCH(NRB)                                                              \
+  if (app)                                                                            \
+    hipLaunchKernelGGL((decode_kernel<D, KB, NRB, true>), grid, block, 0, s, P);      \
+  else                                                                                \
+    hipLaunchKernelGGL((decode_kernel<D, KB, NRB, false>), grid, block, 0, s, P);
   switch ((p.head_tile + 3) / 4) {
     case 1:
-      hipLaunchKernelGGL((decode_kernel<D, KB, 1>), grid, block, 0, s, P);
+      KVQ_DLAUNCH(1);
       break;
     case 2:
-      hipLaunchKernelGGL((decode_kernel<D, KB, 2>), grid, block, 0, s, P);
+      KVQ_DLAUNCH(2);
       break;
     case 3:
-      hipLaunchKernelGGL((decode_kernel<D, KB, 3>), grid, block, 0, s, P);
+      KVQ_DLAUNCH(3);
       break;
     case 4:
-      hipLaunchKernelGGL((decode_kernel<D, KB, 4>), grid, block, 0, s, P);
+      KVQ_DLAUNCH(4);
       break;
     default:
       return hipErrorInvalidValue;
   }
+#undef KVQ_DLAUNCH
   return hipGetLastError();
 }
 
