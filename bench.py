@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--seq", type=int, default=0, help="override the workload's sequence length (a sweep point)")
+    ap.add_argument("--k-bits", type=int, choices=(4, 8), default=0, help="override the workload's K width")
+    ap.add_argument("--v-bits", type=int, choices=(4, 8), default=0, help="override the workload's V width")
     ap.add_argument("--transform", choices=("srft", "srht"), default="srft",
                     help="the rotation: SRFT (default) or the SRHT variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -189,9 +191,13 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = synth.WORKLOADS[args.workload]
+    import dataclasses
     if args.seq > 0:
-        import dataclasses
         w = dataclasses.replace(w, seq_len=args.seq)
+    if args.k_bits:
+        w = dataclasses.replace(w, k_bits=args.k_bits)
+    if args.v_bits:
+        w = dataclasses.replace(w, v_bits=args.v_bits)
     L, B, H, Hq, d, S = w.layers, w.batch, w.kv_heads, w.q_heads, w.head_dim, w.seq_len
     LB = L * B
     log(f"workload {w.name}: layers {L} batch {B} kv {H} q {Hq} d {d} seq {S} K{w.k_bits}V{w.v_bits}")

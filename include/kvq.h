@@ -67,8 +67,8 @@ typedef struct {
                       /* kv head h / G                                                          */
   int32_t head_dim;   /* d: 128 or 256                                                          */
   int32_t group_size; /* 16                                                                     */
-  int32_t k_bits;     /* 4 or 8                                                                 */
-  int32_t v_bits;     /* 4                                                                      */
+  int32_t k_bits;     /* 4 or 8 (K8V4 is [KS]'s pairing; K4V8 and K8V8 are the other widths)   */
+  int32_t v_bits;     /* 4 or 8                                                                 */
   int32_t capacity;   /* tokens allocated per (sequence, kv head): the token stride of planes   */
   int32_t transform;  /* rotation of the write path and of the decode: KVQ_TRANSFORM_SRFT (0,    */
                       /* [QF] Methodology 1) or KVQ_TRANSFORM_SRHT (1, the pages' alternative:  */

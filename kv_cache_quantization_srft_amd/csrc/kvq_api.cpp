@@ -221,7 +221,7 @@ kvq_status kvq_decode_attn(const kvq_layout* L, const void* q_f16, const void* k
   const char* fn = "kvq_decode_attn";
   KVQ_TRY(check_layout(L, fn));
   KVQ_TRY(check_bits(L->k_bits, fn, "k_bits"));
-  if (L->v_bits != 4) return fail(KVQ_ERR_UNSUPPORTED, "%s: v_bits %d (supported: 4)", fn, L->v_bits);
+  KVQ_TRY(check_bits(L->v_bits, fn, "v_bits"));
   KVQ_TRY(check_decode_common(L, q_f16, seq_len, seq_lens, sm_scale, workspace, workspace_bytes, out, fn));
   KVQ_TRY(check_ptr(k_codes, 16, fn, "k_codes"));
   KVQ_TRY(check_ptr(k_scales, 16, fn, "k_scales"));
@@ -252,7 +252,7 @@ kvq_status kvq_decode_attn_append(const kvq_layout* L, const void* q_f16, const 
   const char* fn = "kvq_decode_attn_append";
   KVQ_TRY(check_layout(L, fn));
   KVQ_TRY(check_bits(L->k_bits, fn, "k_bits"));
-  if (L->v_bits != 4) return fail(KVQ_ERR_UNSUPPORTED, "%s: v_bits %d (supported: 4)", fn, L->v_bits);
+  KVQ_TRY(check_bits(L->v_bits, fn, "v_bits"));
   KVQ_TRY(check_decode_common(L, q_f16, seq_len, seq_lens, sm_scale, workspace, workspace_bytes, out, fn, true));
   KVQ_TRY(check_ptr(k_new_f16, 16, fn, "k_new"));
   KVQ_TRY(check_ptr(v_new_f16, 16, fn, "v_new"));

@@ -48,12 +48,12 @@ __host__ __device__ constexpr int kbyte_channel(int b) {
 // ------------------------------------------------------------------------------------------
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-template <int D, int KB>
+template <int D, int KB, int VB>
 struct QGeom {
   static constexpr int NS = D / 64;             // score MFMA steps (64 channels each)
   static constexpr int NG = D / 16;             // groups of 16 channels
   static constexpr int KRB = D * KB / 8;        // K code bytes per token
-  static constexpr int VRB = D / 2;             // V code bytes per token (int4)
+  static constexpr int VRB = D * VB / 8;        // V code bytes per token
   static constexpr int KLB = KRB / 4;           // K code bytes per lane per 16-token block
   static constexpr int KLW = KLB / 4;           // ... in dwords
   static constexpr int VLU = kSB * VRB / 64 / 16;  // 16-byte V units per lane per superblock
@@ -93,9 +93,9 @@ __device__ __forceinline__ void nibbles_to_half_pairs(uint32_t x, uint32_t mask,
 }
 
 // Global data of one 64-token superblock held in registers (prefetched one superblock ahead).
-template <int D, int KB>
+template <int D, int KB, int VB>
 struct SBRegs {
-  using Gm = QGeom<D, KB>;
+  using Gm = QGeom<D, KB, VB>;
   uint32_t kw[4][Gm::KLW];  // K codes: 16-token block sb, token n16, lane group r4's bytes
   uint32_t ksw[Gm::SLW];    // K scales of token base + lane
   uint4 vw[Gm::VLU];        // V codes, coalesced 16-byte units
@@ -118,10 +118,10 @@ __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, int off) {
 // is a constant and the address arithmetic is scalar.  Two parts: the K codes (consumed by the
 // scores) and the rest (V codes, V scales, K scales: staged in LDS first thing), so that the
 // rest of the next superblock can be requested as soon as this one's is staged.
-template <int D, int KB>
-__device__ __forceinline__ void load_sb_kcodes(SBRegs<D, KB>& r, const uint8_t* kc, int64_t rowbase, int base, int L,
+template <int D, int KB, int VB>
+__device__ __forceinline__ void load_sb_kcodes(SBRegs<D, KB, VB>& r, const uint8_t* kc, int64_t rowbase, int base, int L,
                                                int lane) {
-  using Gm = QGeom<D, KB>;
+  using Gm = QGeom<D, KB, VB>;
   const int n16 = lane & 15, r4 = lane >> 4;
   const __amdgpu_buffer_rsrc_t rk = row_rsrc(kc + (rowbase + base) * Gm::KRB, (L - base) * Gm::KRB);
 #pragma unroll
@@ -137,10 +137,10 @@ __device__ __forceinline__ void load_sb_kcodes(SBRegs<D, KB>& r, const uint8_t* 
   }
 }
 
-template <int D, int KB>
-__device__ __forceinline__ void load_sb_rest(SBRegs<D, KB>& r, const uint16_t* ks, const uint8_t* vc,
+template <int D, int KB, int VB>
+__device__ __forceinline__ void load_sb_rest(SBRegs<D, KB, VB>& r, const uint16_t* ks, const uint8_t* vc,
                                              const uint16_t* vs, int64_t rowbase, int base, int L, int lane) {
-  using Gm = QGeom<D, KB>;
+  using Gm = QGeom<D, KB, VB>;
   const int nrem = L - base;
   const int64_t t0 = rowbase + base;
   const __amdgpu_buffer_rsrc_t rks = row_rsrc(ks + t0 * Gm::NG, nrem * Gm::NG * 2);
@@ -166,20 +166,20 @@ __device__ __forceinline__ void load_sb_rest(SBRegs<D, KB>& r, const uint16_t* k
   }
 }
 
-template <int D, int KB>
-__device__ __forceinline__ void load_superblock(SBRegs<D, KB>& r, const uint8_t* kc, const uint16_t* ks,
+template <int D, int KB, int VB>
+__device__ __forceinline__ void load_superblock(SBRegs<D, KB, VB>& r, const uint8_t* kc, const uint16_t* ks,
                                                 const uint8_t* vc, const uint16_t* vs, int64_t rowbase, int base,
                                                 int L, int lane) {
-  load_sb_kcodes<D, KB>(r, kc, rowbase, base, L, lane);
-  load_sb_rest<D, KB>(r, ks, vc, vs, rowbase, base, L, lane);
+  load_sb_kcodes<D, KB, VB>(r, kc, rowbase, base, L, lane);
+  load_sb_rest<D, KB, VB>(r, ks, vc, vs, rowbase, base, L, lane);
 }
 
 // Overwrite, in the registers of a loaded superblock, the token at superblock offset tl
 // (wave-uniform) with the new token staged in LDS (app: K codes, K scales, V codes, V scales).
 // The lanes holding each part follow load_superblock's layout.
-template <int D, int KB>
-__device__ __forceinline__ void patch_superblock(SBRegs<D, KB>& r, int tl, const uint8_t* app, int lane) {
-  using Gm = QGeom<D, KB>;
+template <int D, int KB, int VB>
+__device__ __forceinline__ void patch_superblock(SBRegs<D, KB, VB>& r, int tl, const uint8_t* app, int lane) {
+  using Gm = QGeom<D, KB, VB>;
   const int n16 = lane & 15, r4 = lane >> 4;
   const uint32_t* ak = reinterpret_cast<const uint32_t*>(app);
   const uint32_t* aks = reinterpret_cast<const uint32_t*>(app + Gm::APP_KS);
@@ -226,9 +226,65 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Token (0..15) of a 16-token lane group at position p of the value MFMA's k order (inverse of
+// kpos16).
+__host__ __device__ constexpr int kinv16(int p) {
+  return (p < 8 ? 0 : 8) + ((p & 7) % 2 == 0 ? (p & 7) / 2 : (p & 7) / 2 + 4);
+}
+
+// Value accumulation over int8 V codes staged in LDS (rows swizzled as in the staging).
+// ds_read_b64_tr_b8 hands lane c + 8 h of each 16-lane group byte c of the rows that lanes
+// 2 j + h supplied, j = 0..7; so lane 2 j + h points at channel half h of group g of the token
+// in k slot j, and lane n16 receives channel n16 of the 8 tokens of its k slots.  Bytes become
+// fp16 pairs with one v_perm_b32 (exponent byte 0x64 beside each offset-binary code) and one
+// packed add; B = code * (staged scale) split exactly into fp16 hi + lo.
+template <int D, int KB, int VB>
+__device__ __forceinline__ void values_int8(int lane, const v8h (&a_hi)[2], const v8h (&a_lo)[2],
+                                            v4f (&acc)[D / 16], const uint8_t* vtile, const uint16_t* stile) {
+  using Gm = QGeom<D, KB, VB>;
+  constexpr int NG = Gm::NG;
+  const int n16 = lane & 15, r4 = lane >> 4;
+  const int j = n16 >> 1, h = n16 & 1;
+  int tok[2];
+#pragma unroll
+  for (int hblk = 0; hblk < 2; ++hblk) tok[hblk] = 16 * r4 + kinv16(8 * hblk + j);
+  const uint32_t expo = 0x64646464u;
+  const v2h off = {static_cast<_Float16>(-1152.0f), static_cast<_Float16>(-1152.0f)};
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const uint4 s0 = *reinterpret_cast<const uint4*>(stile + g * kSB + 16 * r4);
+    const uint4 s1 = *reinterpret_cast<const uint4*>(stile + g * kSB + 16 * r4 + 8);
+    const uint32_t sp[2][4] = {{s0.x, s0.y, s0.z, s0.w}, {s1.x, s1.y, s1.z, s1.w}};
+#pragma unroll
+    for (int hblk = 0; hblk < 2; ++hblk) {
+      const int tk = tok[hblk];
+      lds_v2i_t* src = (lds_v2i_t*)(vtile + tk * Gm::VRB + 16 * (g ^ (tk & 7)) + 8 * h);
+      const v2i_t tr = __builtin_amdgcn_ds_read_tr8_b64_v2i32(src);
+      const uint32_t w0 = uint32_t(tr.x) ^ 0x80808080u, w1 = uint32_t(tr.y) ^ 0x80808080u;
+      const uint32_t raw[4] = {__builtin_amdgcn_perm(expo, w0, 0x04010400u), __builtin_amdgcn_perm(expo, w0, 0x04030402u),
+                               __builtin_amdgcn_perm(expo, w1, 0x04010400u), __builtin_amdgcn_perm(expo, w1, 0x04030402u)};
+      uint32_t bh[4], bl[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const v2h c = __builtin_bit_cast(v2h, raw[i]) + off;  // 1024 + code + 128 - 1152
+        const v2h sc2 = __builtin_bit_cast(v2h, sp[hblk][i]);
+        const v2h hi = c * sc2;
+        const v2h lo = __builtin_elementwise_fma(c, sc2, -hi);
+        bh[i] = __builtin_bit_cast(uint32_t, hi);
+        bl[i] = __builtin_bit_cast(uint32_t, lo);
+      }
+      const v8h b_hi = as_v8h(bh[0], bh[1], bh[2], bh[3]);
+      const v8h b_lo = as_v8h(bl[0], bl[1], bl[2], bl[3]);
+      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[hblk], b_hi, acc[g], 0, 0, 0);
+      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[hblk], b_lo, acc[g], 0, 0, 0);
+      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo[hblk], b_hi, acc[g], 0, 0, 0);
+    }
+  }
+}
+
 // Everything one wave does with one superblock already in registers.
-template <int D, int KB, int NRB>
-__device__ __forceinline__ void process_superblock(SBRegs<D, KB>& r, int base, int t_end, int lane,
+template <int D, int KB, int VB, int NRB>
+__device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int base, int t_end, int lane,
                                                    const v4i (&aop)[NRB][D / 64][2], const float (&sig)[NRB],
                                                    float (&m_run)[NRB], float (&l_run)[NRB], v4f (&acc)[D / 16],
                                                    uint8_t* vtile, uint16_t* stile, uint16_t* ktile, float* ptile,
@@ -236,15 +292,37 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB>& r, int base, i
                                                    const uint16_t* __restrict__ ks, const uint8_t* __restrict__ vc,
                                                    const uint16_t* __restrict__ vs, int64_t rowbase, int next_base,
                                                    int L) {
-  using Gm = QGeom<D, KB>;
+  using Gm = QGeom<D, KB, VB>;
   constexpr int NS = Gm::NS, NG = Gm::NG;
   const int n16 = lane & 15, r4 = lane >> 4;
 
-  // ---------------- stage V codes, V scales (k order, / 16) and K scales in LDS ----------------
+  // ---------------- stage V codes, V scales (k order, pre-scaled) and K scales in LDS ----------------
+  bool vbig = false;
+  if constexpr (VB == 8) {
+    uint32_t mx = 0;
 #pragma unroll
-  for (int i = 0; i < Gm::VLU; ++i) *reinterpret_cast<uint4*>(vtile + (i * 64 + lane) * 16) = r.vw[i];
+    for (int i = 0; i < Gm::SLW; ++i) mx = max(mx, max(r.vsw[i] & 0x7fffu, (r.vsw[i] >> 16) & 0x7fffu));
+    vbig = __builtin_amdgcn_ballot_w64(mx > 0x6000u) != 0ull;  // 0x6000 = 512 in fp16
+  }
+  const float vpre = VB == 4 ? 0.0625f : (vbig ? 0.0078125f : 1.0f);
+#pragma unroll
+  for (int i = 0; i < Gm::VLU; ++i) {
+    const int u = i * 64 + lane;  // 16-byte unit of the superblock, token-major
+    if constexpr (VB == 4) {
+      *reinterpret_cast<uint4*>(vtile + u * 16) = r.vw[i];
+    } else {
+      // int8: unit k (group k) of token t goes to slot k ^ (t & 7) of the token's row, so that
+      // the transposed reads of 8 tokens of one group hit 8 different bank quads
+      constexpr int UPT = Gm::VRB / 16;
+      const int tk = u / UPT, k = u % UPT;
+      *reinterpret_cast<uint4*>(vtile + tk * Gm::VRB + 16 * (k ^ (tk & 7))) = r.vw[i];
+    }
+  }
   {
-    // scale / 16 keeps code * scale inside the fp16 range (undone by the merge).  No mask is
+    // int4: scale / 16 keeps code * scale inside the fp16 range (undone by the merge).  int8:
+    // the scale as it is (scales of calibrated values are small, and a pre-factor would push
+    // them into fp16 subnormals), unless a scale of this superblock exceeds 512, where
+    // code * scale could overflow: then B takes scale / 128 and A takes p * 128.  No mask is
     // needed: a superblock never crosses a chunk end (chunks are whole multiples of the
     // work-group stride), so its tokens past t_end are past the row end, where the loads
     // returned zero.  (Kept in float: a packed-half multiply here was miscompiled, both
@@ -253,7 +331,7 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB>& r, int base, i
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const uint32_t bits = (r.vsw[g >> 1] >> (16 * (g & 1))) & 0xffffu;
-      const float sv = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(bits))) * 0.0625f;
+      const float sv = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(bits))) * vpre;
       stile[g * kSB + pos] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(sv));
     }
     uint32_t* kt = reinterpret_cast<uint32_t*>(ktile + lane * NG);
@@ -262,7 +340,7 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB>& r, int base, i
       *reinterpret_cast<uint4*>(kt + i) = make_uint4(r.ksw[i], r.ksw[i + 1], r.ksw[i + 2], r.ksw[i + 3]);
   }
   // the staged parts of the next superblock load during this one's scores, softmax and values
-  if (next_base < t_end) load_sb_rest<D, KB>(r, ks, vc, vs, rowbase, next_base, L, lane);
+  if (next_base < t_end) load_sb_rest<D, KB, VB>(r, ks, vc, vs, rowbase, next_base, L, lane);
   wave_sync_lds();
 
   // ---------------- scores (int8 MFMA, exact integer group dots) ----------------
@@ -313,7 +391,7 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB>& r, int base, i
   }
 
   // the K codes of this superblock are consumed: the next one's load during softmax + values
-  if (next_base < t_end) load_sb_kcodes<D, KB>(r, kc, rowbase, next_base, L, lane);
+  if (next_base < t_end) load_sb_kcodes<D, KB, VB>(r, kc, rowbase, next_base, L, lane);
 
   // ---------------- online softmax per head (16-lane rows) ----------------
   bool rescale = false;
@@ -351,10 +429,15 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB>& r, int base, i
   uint32_t ahi[2][4], alo[2][4];
   {
     const float* pr = ptile + n16 * kSB + 16 * r4;
+    const float pa = vbig ? 128.0f : 1.0f;
 #pragma unroll
     for (int hblk = 0; hblk < 2; ++hblk) {
-      const float4 p0 = *reinterpret_cast<const float4*>(pr + 8 * hblk);
-      const float4 p1 = *reinterpret_cast<const float4*>(pr + 8 * hblk + 4);
+      float4 p0 = *reinterpret_cast<const float4*>(pr + 8 * hblk);
+      float4 p1 = *reinterpret_cast<const float4*>(pr + 8 * hblk + 4);
+      if constexpr (VB == 8) {
+        p0 = make_float4(p0.x * pa, p0.y * pa, p0.z * pa, p0.w * pa);
+        p1 = make_float4(p1.x * pa, p1.y * pa, p1.z * pa, p1.w * pa);
+      }
       split_pair(p0.x, p0.y, ahi[hblk][0], alo[hblk][0]);
       split_pair(p0.z, p0.w, ahi[hblk][1], alo[hblk][1]);
       split_pair(p1.x, p1.y, ahi[hblk][2], alo[hblk][2]);
@@ -367,6 +450,11 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB>& r, int base, i
                        as_v8h(alo[1][0], alo[1][1], alo[1][2], alo[1][3])};
 
   // ---------------- values (fp16 MFMA over LDS-transposed codes) ----------------
+  if constexpr (VB == 8) {
+    values_int8<D, KB, VB>(lane, a_hi, a_lo, acc, vtile, stile);
+    wave_sync_lds();
+    return;
+  }
   uint32_t nmask = 0x000f000fu, nmagic = 0x64006400u;
   asm volatile("" : "+v"(nmask), "+v"(nmagic));
 #pragma unroll
@@ -427,10 +515,10 @@ struct QDecodeParams {
 
 // APP: the appending variant (kvq_decode_attn_append), a separate instance so that the plain
 // decode carries none of its code.
-template <int D, int KB, int NRB, bool APP>
+template <int D, int KB, int VB, int NRB, bool APP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1))) void decode_kernel(
     const QDecodeParams P) {
-  using Gm = QGeom<D, KB>;
+  using Gm = QGeom<D, KB, VB>;
   constexpr int NS = Gm::NS, NG = Gm::NG;
   constexpr int NSTEP = D / 32, NBW = D / 16 / kWaves;
   __shared__ __align__(16) uint8_t smem[Gm::LDS];
@@ -506,9 +594,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
       tbl[j][s] = ld4(T.fwd_lo[w + kWaves * j][s][lane]);
     }
 
-  SBRegs<D, KB> ra;
+  SBRegs<D, KB, VB> ra;
   int base = t_begin + w * kSB;
-  if (base < t_end) load_superblock<D, KB>(ra, kc, ks, vc, vs, rowbase, base, L, lane);
+  if (base < t_end) load_superblock<D, KB, VB>(ra, kc, ks, vc, vs, rowbase, base, L, lane);
 
   // LDS of the prologue (aliases the main-loop tiles): digit operands, per-wave head maxima
   constexpr int kDigBytes = NRB * NS * 2 * 1024;
@@ -566,10 +654,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
       const float uk = qa[2] * __builtin_amdgcn_rcpf(16.0f * nlk[j]);
       const float uv = qa[3] * __builtin_amdgcn_rcpf(16.0f * nlv[j]);
       const _Float16 shk = static_cast<_Float16>(scale_of<KB>(row_max16(fabsf(uk))));
-      const _Float16 shv = static_cast<_Float16>(scale_of<4>(row_max16(fabsf(uv))));
+      const _Float16 shv = static_cast<_Float16>(scale_of<VB>(row_max16(fabsf(uv))));
       const float sfk = static_cast<float>(shk), sfv = static_cast<float>(shv);
       const uint32_t ck = code_byte<KB>(uk, sfk > 0.0f ? __builtin_amdgcn_rcpf(sfk) : 0.0f);
-      const uint32_t cv = code_byte<4>(uv, sfv > 0.0f ? __builtin_amdgcn_rcpf(sfv) : 0.0f);
+      const uint32_t cv = code_byte<VB>(uv, sfv > 0.0f ? __builtin_amdgcn_rcpf(sfv) : 0.0f);
       // int4: two's-complement nibbles, the even channel low (odd partner n16 ^ 1 by DPP)
       const uint32_t nk = (ck ^ 8u) & 0xfu, nvv = (cv ^ 8u) & 0xfu;
       const uint32_t pk = uint32_t(__builtin_amdgcn_mov_dpp(int(nk), 0xB1, 0xf, 0xf, false));
@@ -579,7 +667,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
           appbuf[16 * g + n16] = uint8_t(ck ^ 0x80u);
         else if ((n16 & 1) == 0)
           appbuf[8 * g + n16 / 2] = uint8_t(nk | (pk << 4));
-        if ((n16 & 1) == 0) appbuf[Gm::APP_V + 8 * g + n16 / 2] = uint8_t(nvv | (pv << 4));
+        if constexpr (VB == 8)
+          appbuf[Gm::APP_V + 16 * g + n16] = uint8_t(cv ^ 0x80u);
+        else if ((n16 & 1) == 0)
+          appbuf[Gm::APP_V + 8 * g + n16 / 2] = uint8_t(nvv | (pv << 4));
         if (n16 == 0) {
           reinterpret_cast<uint16_t*>(appbuf + Gm::APP_KS)[g] = __builtin_bit_cast(uint16_t, shk);
           reinterpret_cast<uint16_t*>(appbuf + Gm::APP_VS)[g] = __builtin_bit_cast(uint16_t, shv);
@@ -707,8 +798,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   for (int g = 0; g < NG; ++g) acc[g] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   while (base < t_end) {
-    if (app && t_app >= base && t_app < base + kSB) patch_superblock<D, KB>(ra, t_app - base, appbuf, lane);
-    process_superblock<D, KB, NRB>(ra, base, t_end, lane, aop, sig, m_run, l_run, acc, vtile, stile, ktile, ptile,
+    if (app && t_app >= base && t_app < base + kSB) patch_superblock<D, KB, VB>(ra, t_app - base, appbuf, lane);
+    process_superblock<D, KB, VB, NRB>(ra, base, t_end, lane, aop, sig, m_run, l_run, acc, vtile, stile, ktile, ptile,
                                    atile, kc, ks, vc, vs, rowbase, base + kStride, L);
     base += kStride;
   }
@@ -731,7 +822,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   merge_unit<D, true>(P.merge, unit, reinterpret_cast<float*>(smem));
 }
 
-template <int D, int KB>
+template <int D, int KB, int VB>
 hipError_t launch_q(const DecodeArgs& a, const DecodePlan& p, const WsLayout& w, hipStream_t s) {
   char* ws = static_cast<char*>(a.workspace);
   const int units = a.batch * a.kv_heads * p.head_tiles;
@@ -759,9 +850,10 @@ hipError_t launch_q(const DecodeArgs& a, const DecodePlan& p, const WsLayout& w,
   P.counters = reinterpret_cast<uint32_t*>(ws + w.counters);
   P.pml = reinterpret_cast<float*>(ws + w.pml);
   P.pacc = reinterpret_cast<float*>(ws + w.pacc);
-  // code * scale was staged as code * scale / 16 in fp16: acc_scale 16 undoes it
+  // int4: code * scale was staged as code * scale / 16 in fp16, acc_scale 16 undoes it (int8
+  // keeps the product's scale)
   P.merge = MergeArgs{P.pml,      P.pacc,     p.n_chunks, p.max_chunks, p.head_tile, p.head_tiles,
-                      a.q_heads,  a.kv_heads, 16.0f,      a.sign_v,     a.sign_bs,   a.lambda_v,
+                      a.q_heads,  a.kv_heads, VB == 4 ? 16.0f : 1.0f, a.sign_v, a.sign_bs, a.lambda_v,
                       a.lambda_bs, a.out,     a.transform};
   P.k_new = static_cast<const uint16_t*>(a.k_new);
   P.v_new = static_cast<const uint16_t*>(a.v_new);
@@ -769,9 +861,9 @@ hipError_t launch_q(const DecodeArgs& a, const DecodePlan& p, const WsLayout& w,
   const bool app = a.k_new != nullptr;
 #define KVQ_DLAUNCH(NRB)                                                              \
   if (app)                                                                            \
-    hipLaunchKernelGGL((decode_kernel<D, KB, NRB, true>), grid, block, 0, s, P);      \
+    hipLaunchKernelGGL((decode_kernel<D, KB, VB, NRB, true>), grid, block, 0, s, P);      \
   else                                                                                \
-    hipLaunchKernelGGL((decode_kernel<D, KB, NRB, false>), grid, block, 0, s, P);
+    hipLaunchKernelGGL((decode_kernel<D, KB, VB, NRB, false>), grid, block, 0, s, P);
   switch ((p.head_tile + 3) / 4) {
     case 1:
       KVQ_DLAUNCH(1);
@@ -796,8 +888,23 @@ hipError_t launch_q(const DecodeArgs& a, const DecodePlan& p, const WsLayout& w,
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
   const WsLayout w = ws_layout(a.batch * a.kv_heads * p.head_tiles, p.head_tile, a.head_dim, p.max_chunks);
-  if (a.head_dim == 128) return a.k_bits == 4 ? launch_q<128, 4>(a, p, w, s) : launch_q<128, 8>(a, p, w, s);
-  return a.k_bits == 4 ? launch_q<256, 4>(a, p, w, s) : launch_q<256, 8>(a, p, w, s);
+  const int kv = a.k_bits * 10 + a.v_bits;
+  if (a.head_dim == 128) {
+    switch (kv) {
+      case 44: return launch_q<128, 4, 4>(a, p, w, s);
+      case 84: return launch_q<128, 8, 4>(a, p, w, s);
+      case 48: return launch_q<128, 4, 8>(a, p, w, s);
+      case 88: return launch_q<128, 8, 8>(a, p, w, s);
+    }
+  } else {
+    switch (kv) {
+      case 44: return launch_q<256, 4, 4>(a, p, w, s);
+      case 84: return launch_q<256, 8, 4>(a, p, w, s);
+      case 48: return launch_q<256, 4, 8>(a, p, w, s);
+      case 88: return launch_q<256, 8, 8>(a, p, w, s);
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace kvq_impl

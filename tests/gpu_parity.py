@@ -104,14 +104,14 @@ def oracle_planes(x16, s, lam, bits):
 
 
 def gpu_decode(q16, kc8, ks16, vc8, vs16, k_bits, s_k, s_v, lam_k, lam_v, seq_len, seq_lens=None, sm_scale=0.0,
-               capacity=None, sign_bs=0, lambda_bs=0, ws=None, transform="srft"):
+               capacity=None, sign_bs=0, lambda_bs=0, ws=None, transform="srft", v_bits=4):
     """Run kvq_decode_attn on given unpacked int8 codes (packed here by the oracle's packing)."""
     B, Hkv, S, d = kc8.shape
     Hq = q16.shape[1]
     cap = capacity or S
-    lay = kvq.make_layout(B, Hkv, Hq, d, cap, k_bits=k_bits, v_bits=4, transform=transform)
+    lay = kvq.make_layout(B, Hkv, Hq, d, cap, k_bits=k_bits, v_bits=v_bits, transform=transform)
     kb = O.pack_codes(kc8, k_bits)
-    vb = O.pack_codes(vc8, 4)
+    vb = O.pack_codes(vc8, v_bits)
     if ws is None:
         ws = torch.zeros(kvq.kvq_decode_attn_workspace_bytes(lay, seq_len), dtype=torch.uint8, device="cuda")
     out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device="cuda")

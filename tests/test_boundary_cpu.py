@@ -140,7 +140,7 @@ def decode(L, lay, q=GOOD, seq_len=16, seq_lens=NULL, sm=0.0, ws=GOOD, ws_bytes=
 @pytest.mark.parametrize("kw,status,needle", [
     (dict(lay=dict(q_heads=5)), 1, "multiple of kv_heads"),
     (dict(lay=dict(q_heads=2 * 65)), 2, "GQA"),
-    (dict(lay=dict(v_bits=8)), 2, "v_bits"),
+    (dict(lay=dict(v_bits=3)), 2, "v_bits"),
     (dict(lay=dict(k_bits=2)), 2, "k_bits"),
     (dict(seq_len=0), 1, "seq_len"),
     (dict(seq_len=65), 1, "seq_len"),
@@ -207,7 +207,7 @@ def append(L, lay, q=GOOD, k_new=GOOD, v_new=GOOD, seq_len=16, ws_bytes=1 << 30,
     (dict(v_new=MIS), 3, "v_new is not"),
     (dict(kc=MIS), 3, "k_codes"),
     (dict(seq_len=65), 1, "seq_len"),
-    (dict(lay=dict(v_bits=8)), 2, "v_bits"),
+    (dict(lay=dict(v_bits=3)), 2, "v_bits"),
     (dict(ws_bytes=16), 4, "workspace has 16 bytes"),
 ])
 def test_append_validation(L, kw, status, needle):

@@ -31,11 +31,11 @@ def _inputs(seed, B, Hkv, G, S, d, lam, transform):
     return k, v, q, sk, sv, lk, lv
 
 
-def _planes(k, v, sk, sv, lk, lv, kb, transform):
+def _planes(k, v, sk, sv, lk, lv, kb, transform, vb=4):
     l4 = lambda x: 1.0 if x is None else x[:, :, None, :]
     kc, ks = O.quantize(k, sk, l4(lk), kb, transform=transform)
-    vc, vs = O.quantize(v, sv, l4(lv), 4, transform=transform)
-    return O.pack_codes(kc, kb), ks.copy(), O.pack_codes(vc, 4), vs.copy()
+    vc, vs = O.quantize(v, sv, l4(lv), vb, transform=transform)
+    return O.pack_codes(kc, kb), ks.copy(), O.pack_codes(vc, vb), vs.copy()
 
 
 def _run_append(lay, q, k_new, v_new, pl, seq_len, lens, sk, sv, lk, lv):
@@ -54,23 +54,25 @@ def _run_append(lay, q, k_new, v_new, pl, seq_len, lens, sk, sv, lk, lv):
 
 
 CASES = [
-    # d, G, k_bits, S, lens, lambda, transform
-    (128, 6, 4, 1500, [1500, 700, 257, 1], True, "srft"),
-    (128, 1, 4, 256, None, False, "srft"),
-    (256, 4, 8, 900, [900, 1, 513], False, "srft"),
-    (128, 16, 4, 600, [600, 0, 65], True, "srft"),
-    (128, 6, 4, 1100, [1100, 64], True, "srht"),
-    (256, 4, 4, 700, [700, 300], True, "srht"),
+    # d, G, k_bits, S, lens, lambda, transform, v_bits
+    (128, 6, 4, 1500, [1500, 700, 257, 1], True, "srft", 4),
+    (128, 1, 4, 256, None, False, "srft", 4),
+    (256, 4, 8, 900, [900, 1, 513], False, "srft", 4),
+    (128, 16, 4, 600, [600, 0, 65], True, "srft", 4),
+    (128, 6, 4, 1100, [1100, 64], True, "srht", 4),
+    (256, 4, 4, 700, [700, 300], True, "srht", 4),
+    (128, 6, 4, 800, [800, 129], True, "srft", 8),
+    (256, 2, 8, 500, [500, 3], True, "srft", 8),
 ]
 
 
-@pytest.mark.parametrize("d,G,kb,S,lens,lam,transform", CASES)
-def test_append_parity(d, G, kb, S, lens, lam, transform):
+@pytest.mark.parametrize("d,G,kb,S,lens,lam,transform,vb", CASES)
+def test_append_parity(d, G, kb, S, lens, lam, transform, vb):
     Hkv = 2
     B = 1 if lens is None else len(lens)
     k, v, q, sk, sv, lk, lv = _inputs(d + G + S, B, Hkv, G, S, d, lam, transform)
     L = np.full(B, S) if lens is None else np.clip(np.asarray(lens), 0, S)
-    pl = _planes(k, v, sk, sv, lk, lv, kb, transform)
+    pl = _planes(k, v, sk, sv, lk, lv, kb, transform, vb)
     # the step's new vectors and, at their slots, stale bytes that the call must overwrite
     rng = np.random.default_rng(5)
     k_new = synth.to_fp16(rng.standard_normal((B, Hkv, d)) * 3)
@@ -81,8 +83,8 @@ def test_append_parity(d, G, kb, S, lens, lam, transform):
             k_new[b] = k[b, :, L[b] - 1]
             for a in before:
                 a[b, :, L[b] - 1] = np.array(0xAB, a.dtype) if a.dtype == np.uint8 else np.float16(-7.5)
-    lay = kvq.make_layout(B, Hkv, Hkv * G, d, S, k_bits=kb, v_bits=4, transform=transform)
-    say("append", d, G, kb, S, lens, lam, transform)
+    lay = kvq.make_layout(B, Hkv, Hkv * G, d, S, k_bits=kb, v_bits=vb, transform=transform)
+    say("append", d, G, kb, vb, S, lens, lam, transform)
     got, out = _run_append(lay, q, k_new, v_new, before, S, lens, sk, sv, lk, lv)
     # untouched elsewhere, bit-exact
     for b in range(B):
@@ -98,11 +100,11 @@ def test_append_parity(d, G, kb, S, lens, lam, transform):
     uv = O.rotated_scaled(v_new[live][:, :, None, :], sv, l4(lv), transform=transform)
     sel = lambda a: np.stack([a[b][:, L[b] - 1:L[b]] for b in live])
     check_quantize(sel(got[0]), sel(got[1]), uk, kb, label="append K")
-    check_quantize(sel(got[2]), sel(got[3]), uv, 4, label="append V")
+    check_quantize(sel(got[2]), sel(got[3]), uv, vb, label="append V")
     # attention over the planes the GPU left, on both sides
     ref = np.zeros_like(out)
     kc = O.unpack_codes(got[0], kb)
-    vc = O.unpack_codes(got[2], 4)
+    vc = O.unpack_codes(got[2], vb)
     ref[live] = O.decode_attention_quantized(q[live], kc[live], got[1][live], vc[live], got[3][live], sk, sv,
                                              l4(lk), l4(lv), L[live], transform=transform)
     assert np.abs(out - ref).max() <= ATTN_ATOL

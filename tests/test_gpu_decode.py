@@ -30,17 +30,17 @@ def _case(rng, B, Hkv, G, S, d, k_bits, lam=True, dist="t4"):
     return q, k, v, sk, sv, lk, lv
 
 
-def _check(q, k, v, sk, sv, lk, lv, k_bits, seq_len, seq_lens=None, label=""):
+def _check(q, k, v, sk, sv, lk, lv, k_bits, seq_len, seq_lens=None, label="", v_bits=4):
     B, Hkv, S, d = k.shape
     lkb = None if lk is None else lk[:, :, None, :]
     lvb = None if lv is None else lv[:, :, None, :]
     kc, ks = O.quantize(k, sk, 1.0 if lk is None else lkb, k_bits)
-    vc, vs = O.quantize(v, sv, 1.0 if lv is None else lvb, 4)
+    vc, vs = O.quantize(v, sv, 1.0 if lv is None else lvb, v_bits)
     # device lengths are clamped to [0, seq_len]; a length-0 sequence has a zero output (API rule)
     lens = np.full(B, seq_len) if seq_lens is None else np.clip(np.asarray(seq_lens), 0, seq_len)
     say("decode", label, (B, Hkv, q.shape[1], S, d), k_bits, seq_len)
     got = gpu_decode(q, kc, ks, vc, vs, k_bits, sk, sv, lk, lv, seq_len, seq_lens,
-                     lambda_bs=0 if lk is None else Hkv * d)
+                     lambda_bs=0 if lk is None else Hkv * d, v_bits=v_bits)
     ref = np.zeros_like(got)
     live = lens > 0
     if live.any():
@@ -66,6 +66,29 @@ def test_d256_k8v4(G):
     rng = np.random.default_rng(100 + G)
     args = _case(rng, 1, 2, G, 1030, 256, 8, lam=False, dist="normal")
     _check(*args, 8, 1030, label=f"k8v4 G{G}")
+
+
+@pytest.mark.parametrize("d,kb,G,S,lens", [(128, 4, 6, 1111, [1111, 300]), (128, 8, 4, 700, None),
+                                           (128, 4, 16, 515, [515, 1]), (256, 4, 4, 900, [900, 77]),
+                                           (256, 8, 2, 600, None)])
+def test_int8_values(d, kb, G, S, lens):
+    """The other bit pairings: int8 V codes (K4V8, K8V8)."""
+    rng = np.random.default_rng(d + kb + G)
+    B = 2
+    args = _case(rng, B, 2, G, S, d, kb, lam=True)
+    _check(*args, kb, S, seq_lens=lens, label=f"K{kb}V8 d{d} G{G}", v_bits=8)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_int8_values_large_scales(d):
+    """int8 V whose group scales exceed 512 (tiny lambda_V makes u = SRFT(v) / lambda ~ 1e5, while
+    the dequantized values stay O(1)): the superblocks that hold such scales take the
+    range-safe form (scale / 128 in B, p * 128 in A)."""
+    rng = np.random.default_rng(7 + d)
+    q, k, v, sk, sv, lk, lv = _case(rng, 2, 2, 4, 600, d, 4, lam=True)
+    lv = np.full_like(lv, 1e-5)
+    lv[1, 1] = O.calibrate_lambda(v, sv, 256)[1, 1]  # one row of ordinary scales beside them
+    _check(q, k, v, sk, sv, lk, lv, 4, 600, seq_lens=[600, 333], label=f"K4V8 big scales d{d}", v_bits=8)
 
 
 def test_tiny_workload_and_single_token():
