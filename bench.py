@@ -59,8 +59,9 @@ def parse():
 class Timer:
     """Time exactly `steps` steps: one HIP graph holds them all (each step on the next cache
     copy), so host launch overhead is paid once per graph, not per step.  A separate graph of
-    `warmup` steps runs first; the timed replay is bracketed by device synchronizations and HIP
-    events on the capturing stream; it is repeated `repeats` times for the spread."""
+    `warmup` steps runs first, then the timed graph is replayed untimed for at least 100 ms
+    (steady clocks); each timed replay is bracketed by device synchronizations and HIP events on
+    the capturing stream; it is repeated `repeats` times for the spread."""
 
     def __init__(self, torch):
         self.torch = torch
@@ -73,6 +74,12 @@ class Timer:
             torch.cuda.synchronize()
             del gw
         g = capture(torch, lambda: [step_fn(i % n_copies) for i in range(steps)])
+        # settle: replay for at least 100 ms so that clocks and caches are in steady state
+        t_settle, n_settle = time.perf_counter(), 0
+        while n_settle < 2 or time.perf_counter() - t_settle < 0.1:
+            g.replay()
+            torch.cuda.synchronize()
+            n_settle += 1
         times = []
         for _ in range(repeats):
             e0 = torch.cuda.Event(enable_timing=True)
