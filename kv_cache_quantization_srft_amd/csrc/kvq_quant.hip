@@ -213,7 +213,7 @@ __device__ __forceinline__ uint4 sign_mask(float4 s0, float4 s1) {
 // row 0 (sign_bs == 0), so the sign mask is fixed per thread and the prefetch ring holds data
 // only, which leaves the registers for a deeper ring.
 template <int D, int BITS, bool HAS_LAMBDA, bool SHARED>
-__global__ __launch_bounds__(2 * D) void quantize_mfma_kernel(const uint16_t* __restrict__ x, FastDiv fd_tok,
+__global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 ? 3 : 2))) void quantize_mfma_kernel(const uint16_t* __restrict__ x, FastDiv fd_tok,
                                                               FastDiv fd_heads, int pos, int capacity,
                                                               const float* __restrict__ sign, int64_t sign_bs,
                                                               const float* __restrict__ lambda, int64_t lambda_bs,
@@ -224,7 +224,8 @@ __global__ __launch_bounds__(2 * D) void quantize_mfma_kernel(const uint16_t* __
   constexpr int CB = D * BITS / 8;  // code bytes per vector
   constexpr int NG = D / 16;        // groups (= channel blocks) per vector
   using CM = CodeMagic<BITS>;
-  __shared__ __align__(16) uint4 xt[2][kVecs][NP];        // inputs, piece p of vector v at p ^ v
+  constexpr int HX = SHARED ? 4 : 1;                      // blocks staged per half
+  __shared__ __align__(16) uint4 xt[HX][kVecs][NP];       // inputs, piece p of vector v at p ^ v
   __shared__ __align__(16) uint8_t ct[2][kVecs][CB];      // packed codes
   __shared__ __align__(16) uint16_t st[2][kVecs][NG];     // scales
   const int tid = threadIdx.x;
@@ -258,41 +259,42 @@ __global__ __launch_bounds__(2 * D) void quantize_mfma_kernel(const uint16_t* __
 
   // this thread's piece: vector sv of the block, channels 8 spc .. 8 spc + 7
   const int sv = tid / NP, spc = tid % NP;
-  constexpr int kPF = 2;  // blocks prefetched ahead
+  // Blocks are processed in halves of H blocks (H = blocks of the grid stride).  A half first
+  // stages all of its H input blocks (loaded one half earlier) in LDS, then requests the next
+  // half's blocks into the other register set, then transforms and stores its blocks.  The
+  // loads and stores of a wave share one completion counter and may complete out of order, so
+  // the wait before staging is a full drain: staging first means it drains loads issued a whole
+  // half ago, not the ones just requested.
+  constexpr int H = HX;
   const uint4 smask0 = SHARED ? sign_mask(*reinterpret_cast<const float4*>(sign + spc * 8),
                                           *reinterpret_cast<const float4*>(sign + spc * 8 + 4))
                               : make_uint4(0u, 0u, 0u, 0u);
-  uint4 pd[kPF], pm[SHARED ? 1 : kPF];
-  auto load_piece = [&](uint32_t blk_, int f) {
-    const uint32_t gv = blk_ * kVecs + sv;
-    pd[f] = make_uint4(0u, 0u, 0u, 0u);
-    if constexpr (!SHARED) pm[f] = make_uint4(0u, 0u, 0u, 0u);
-    if (gv < n_vec) {
-      pd[f] = *reinterpret_cast<const uint4*>(x + int64_t(gv) * D + spc * 8);
-      if constexpr (!SHARED) {
-        const int b = int(fd_heads.div(fd_tok.div(gv)));
-        pm[f] = sign_mask(*reinterpret_cast<const float4*>(sign + b * sign_bs + spc * 8),
-                          *reinterpret_cast<const float4*>(sign + b * sign_bs + spc * 8 + 4));
-      }
+  uint4 pd[2][H], pm[2][SHARED ? 1 : H];
+  // Unconditional loads: a vector past the end reads the last vector again; its column of the
+  // product is never stored, and columns do not mix.
+  auto load_piece = [&](uint32_t blk_, uint4& d_, uint4& m_) {
+    const uint32_t gv = min(blk_ * kVecs + sv, n_vec - 1u);
+    d_ = *reinterpret_cast<const uint4*>(x + int64_t(gv) * D + spc * 8);
+    if constexpr (!SHARED) {
+      const int b = int(fd_heads.div(fd_tok.div(gv)));
+      m_ = sign_mask(*reinterpret_cast<const float4*>(sign + b * sign_bs + spc * 8),
+                     *reinterpret_cast<const float4*>(sign + b * sign_bs + spc * 8 + 4));
     }
   };
+  // this work-group's blocks: a contiguous range, so consecutive blocks share a row (and its
+  // lambda) except at row boundaries
+  const uint32_t nblk = (n_vec + kVecs - 1) / kVecs;
+  const uint32_t blk_end = uint32_t(uint64_t(blockIdx.x + 1) * nblk / gridDim.x);
 #pragma unroll
-  for (int f = 0; f < kPF; ++f) load_piece(blockIdx.x + uint32_t(f) * gridDim.x, f);
+  for (int i = 0; i < H; ++i) {
+    const uint32_t b0 = uint32_t(uint64_t(blockIdx.x) * nblk / gridDim.x);
+    load_piece(b0 + uint32_t(i), pd[0][i], pm[0][SHARED ? 0 : i]);
+  }
 
-  int buf = 0;
-  for (uint32_t blk = blockIdx.x; blk * kVecs < n_vec; blk += gridDim.x, buf ^= 1) {
-    // ---- stage 16 input vectors (sign bits flipped) in LDS; refill the prefetch ring ----
-    {
-      const uint4 m = SHARED ? smask0 : pm[0];
-      xt[buf][sv][spc ^ sv] = make_uint4(pd[0].x ^ m.x, pd[0].y ^ m.y, pd[0].z ^ m.z, pd[0].w ^ m.w);
-    }
-#pragma unroll
-    for (int f = 0; f + 1 < kPF; ++f) {
-      pd[f] = pd[f + 1];
-      if constexpr (!SHARED) pm[f] = pm[f + 1];
-    }
-    if ((blk + uint32_t(kPF) * gridDim.x) * kVecs < n_vec) load_piece(blk + uint32_t(kPF) * gridDim.x, kPF - 1);
-    __syncthreads();
+  // block blk from staged tile f (0..H-1); codes and scales go through LDS buffer f & 1
+  auto do_block = [&](uint32_t blk, auto F) {
+    constexpr int f = decltype(F)::value;
+    constexpr int buf = f & 1;
     // ---- transform: lane (vector n16, channels 16 cb + 4 r4 + i) ----
     // four independent accumulation chains (hi and lo operands of both blocks)
     v4f acc[2], accl[2];
@@ -300,7 +302,7 @@ __global__ __launch_bounds__(2 * D) void quantize_mfma_kernel(const uint16_t* __
     for (int i = 0; i < 2; ++i) acc[i] = accl[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
-      const uint4 bx = xt[buf][n16][(4 * s + r4) ^ n16];
+      const uint4 bx = xt[f][n16][(4 * s + r4) ^ n16];
       const v8h bop = dec::as_v8h(bx.x, bx.y, bx.z, bx.w);
 #pragma unroll
       for (int i = 0; i < 2; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[i][s], bop, acc[i], 0, 0, 0);
@@ -379,6 +381,28 @@ __global__ __launch_bounds__(2 * D) void quantize_mfma_kernel(const uint16_t* __
               *reinterpret_cast<const uint4*>(&st[buf][v][pc * 8]);
       }
     }
+  };
+  for (uint32_t blk = uint32_t(uint64_t(blockIdx.x) * nblk / gridDim.x); blk < blk_end;) {
+    static_for<0, 2>([&](auto HF) {
+      constexpr int hf = decltype(HF)::value;
+      if (blk >= blk_end) return;  // work-group uniform
+      // ---- stage this half's input blocks (sign bits flipped) in LDS ----
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        const uint4 m = SHARED ? smask0 : pm[hf][SHARED ? 0 : i];
+        const uint4 v = pd[hf][i];
+        xt[i][sv][spc ^ sv] = make_uint4(v.x ^ m.x, v.y ^ m.y, v.z ^ m.z, v.w ^ m.w);
+      }
+      // ---- request the next half (past the range: harmless in-bounds re-reads) ----
+#pragma unroll
+      for (int i = 0; i < H; ++i) load_piece(blk + uint32_t(H + i), pd[1 - hf][i], pm[1 - hf][SHARED ? 0 : i]);
+      __syncthreads();
+      static_for<0, H>([&](auto F) {
+        const uint32_t bk = blk + uint32_t(decltype(F)::value);
+        if (bk < blk_end) do_block(bk, F);  // work-group uniform
+      });
+      blk += uint32_t(H);
+    });
   }
 }
 
