@@ -28,13 +28,16 @@
  *   - Non-finite inputs give unspecified (but in-range) codes.
  *
  * Cache layout ("planes"; separate code and scale planes per tensor)
- *   For a tensor quantized with `bits` (4 or 8), head dimension d and group size 16:
+ *   For a tensor quantized with `bits` (4 or 8), head dimension d and group size g (16, or d):
  *     codes : uint8 [batch, kv_heads, capacity, d*bits/8]
  *             int4: byte j of a token holds channel 2j in its low nibble and channel 2j+1 in its
  *             high nibble, each a two's-complement 4-bit code in [-7, 7];
  *             int8: one two's-complement byte per channel, codes in [-127, 127].
- *     scales: fp16  [batch, kv_heads, capacity, d/16], one scale per group of 16 consecutive
- *             channels of the rotated vector.
+ *     scales: fp16  [batch, kv_heads, capacity, d/g], one scale per group of g consecutive
+ *             channels of the rotated vector.  g = 16 is the method's grouping ([QF]
+ *             Methodology 3); g = d (one scale per vector, the per-token scaling that the
+ *             per-group scheme replaces) is a comparison mode of kvq_quantize and
+ *             kvq_dequantize only.
  *   Channel c of the rotated vector is the real, norm-preserving layout of the unitary DFT of
  *   s*x: c=0 -> Re X0, c=1 -> Re X_{d/2}, c=2k -> sqrt2 Re Xk, c=2k+1 -> sqrt2 Im Xk (0<k<d/2),
  *   with Xk = d^-1/2 sum_n s_n x_n exp(-2 pi i k n / d).
@@ -53,7 +56,8 @@ extern "C" {
 typedef enum {
   KVQ_OK = 0,
   KVQ_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, q_heads % kv_heads != 0, range */
-  KVQ_ERR_UNSUPPORTED = 2,      /* head_dim not 128/256, group != 16, bits not 4/8, G > 64 */
+  KVQ_ERR_UNSUPPORTED = 2,      /* head_dim not 128/256, group not 16 (or d: write path   */
+                                /* only), bits not 4/8, G > 64                            */
   KVQ_ERR_MISALIGNED = 3,       /* a pointer violates the alignment rule above */
   KVQ_ERR_WORKSPACE_TOO_SMALL = 4,
   KVQ_ERR_HIP = 5               /* a HIP runtime call or kernel launch failed */
@@ -66,7 +70,8 @@ typedef struct {
   int32_t q_heads;    /* multiple of kv_heads; GQA ratio G = q_heads / kv_heads; head h reads  */
                       /* kv head h / G                                                          */
   int32_t head_dim;   /* d: 128 or 256                                                          */
-  int32_t group_size; /* 16                                                                     */
+  int32_t group_size; /* 16; or head_dim: one scale per vector (kvq_quantize, kvq_dequantize and */
+                      /* the sizing calls only; the decode calls return KVQ_ERR_UNSUPPORTED)   */
   int32_t k_bits;     /* 4 or 8 (K8V4 is [KS]'s pairing; K4V8 and K8V8 are the other widths)   */
   int32_t v_bits;     /* 4 or 8                                                                 */
   int32_t capacity;   /* tokens allocated per (sequence, kv head): the token stride of planes   */

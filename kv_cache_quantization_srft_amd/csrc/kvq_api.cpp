@@ -39,7 +39,9 @@ kvq_status check_layout(const kvq_layout* L, const char* fn) {
                 L->batch, L->kv_heads, L->capacity);
   if (L->head_dim != 128 && L->head_dim != 256)
     return fail(KVQ_ERR_UNSUPPORTED, "%s: head_dim %d (supported: 128, 256)", fn, L->head_dim);
-  if (L->group_size != 16) return fail(KVQ_ERR_UNSUPPORTED, "%s: group_size %d (supported: 16)", fn, L->group_size);
+  if (L->group_size != 16 && L->group_size != L->head_dim)
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: group_size %d (supported: 16, or head_dim for one scale per vector)", fn,
+                L->group_size);
   if (L->transform != KVQ_TRANSFORM_SRFT && L->transform != KVQ_TRANSFORM_SRHT)
     return fail(KVQ_ERR_UNSUPPORTED, "%s: transform %d (supported: 0 = SRFT, 1 = SRHT)", fn, L->transform);
   const long long rows = (long long)L->batch * L->kv_heads;
@@ -88,6 +90,14 @@ kvq_status hip_status(hipError_t e, const char* fn) {
     kvq_status _s = (expr);         \
     if (_s != KVQ_OK) return _s;    \
   } while (0)
+
+// The quantized decode reads group-of-16 scale planes only.
+kvq_status check_decode_group(const kvq_layout* L, const char* fn) {
+  if (L->group_size != 16)
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: group_size %d (decode supports 16; one scale per vector is a write-path mode)",
+                fn, L->group_size);
+  return KVQ_OK;
+}
 
 kvq_status check_decode_common(const kvq_layout* L, const void* q, int32_t seq_len, const int32_t* seq_lens,
                                float sm_scale, void* workspace, size_t workspace_bytes, float* out,
@@ -170,6 +180,7 @@ kvq_status kvq_quantize(const kvq_layout* L, int32_t bits, const void* x_f16, in
   kvq_impl::QuantArgs a{L->batch, L->kv_heads, L->head_dim, bits, L->capacity, pos, n_tok, x_f16, sign,
                         sign_batch_stride, lambda, lambda_batch_stride, codes, scales};
   a.transform = L->transform;
+  a.group = L->group_size;
   return hip_status(kvq_impl::launch_quantize(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -189,6 +200,7 @@ kvq_status kvq_dequantize(const kvq_layout* L, int32_t bits, const void* codes, 
   kvq_impl::DequantArgs a{L->batch, L->kv_heads, L->head_dim, bits, L->capacity, pos, n_tok, codes, scales, sign,
                           sign_batch_stride, lambda, lambda_batch_stride, out};
   a.transform = L->transform;
+  a.group = L->group_size;
   return hip_status(kvq_impl::launch_dequantize(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -222,6 +234,7 @@ kvq_status kvq_decode_attn(const kvq_layout* L, const void* q_f16, const void* k
   KVQ_TRY(check_layout(L, fn));
   KVQ_TRY(check_bits(L->k_bits, fn, "k_bits"));
   KVQ_TRY(check_bits(L->v_bits, fn, "v_bits"));
+  KVQ_TRY(check_decode_group(L, fn));
   KVQ_TRY(check_decode_common(L, q_f16, seq_len, seq_lens, sm_scale, workspace, workspace_bytes, out, fn));
   KVQ_TRY(check_ptr(k_codes, 16, fn, "k_codes"));
   KVQ_TRY(check_ptr(k_scales, 16, fn, "k_scales"));
@@ -253,6 +266,7 @@ kvq_status kvq_decode_attn_append(const kvq_layout* L, const void* q_f16, const 
   KVQ_TRY(check_layout(L, fn));
   KVQ_TRY(check_bits(L->k_bits, fn, "k_bits"));
   KVQ_TRY(check_bits(L->v_bits, fn, "v_bits"));
+  KVQ_TRY(check_decode_group(L, fn));
   KVQ_TRY(check_decode_common(L, q_f16, seq_len, seq_lens, sm_scale, workspace, workspace_bytes, out, fn, true));
   KVQ_TRY(check_ptr(k_new_f16, 16, fn, "k_new"));
   KVQ_TRY(check_ptr(v_new_f16, 16, fn, "v_new"));

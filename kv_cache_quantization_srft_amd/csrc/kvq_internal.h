@@ -19,6 +19,7 @@ struct QuantArgs {
   void* codes;
   void* scales;
   int transform;  // 0 = SRFT, 1 = SRHT
+  int group;      // 16, or head_dim (one scale per vector)
 };
 
 struct DequantArgs {
@@ -32,6 +33,7 @@ struct DequantArgs {
   int64_t lambda_bs;
   float* out;
   int transform;
+  int group;  // 16, or head_dim (one scale per vector)
 };
 
 struct CalibArgs {

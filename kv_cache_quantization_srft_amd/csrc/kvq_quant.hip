@@ -66,7 +66,7 @@ __device__ __forceinline__ float code_at(const uint8_t* __restrict__ row, int c)
   }
 }
 
-template <int D, int BITS, bool HAS_LAMBDA, bool HAD>
+template <int D, int BITS, bool HAS_LAMBDA, bool HAD, bool PT>
 __global__ __launch_bounds__(kQuantThreads) void dequantize_kernel(
     const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales, int n_tok, int kv_heads,
     int tiles_per_row, int pos, int capacity, const float* __restrict__ sign, int64_t sign_bs,
@@ -86,11 +86,11 @@ __global__ __launch_bounds__(kQuantThreads) void dequantize_kernel(
   if (t >= n_tok) return;
   const int64_t slot = int64_t(row) * capacity + pos + t;
   const uint8_t* crow = codes + slot * (D * BITS / 8);
-  const uint16_t* srow = scales + slot * (D / 16);
+  const uint16_t* srow = scales + slot * (PT ? 1 : D / 16);
   float a[D];
   static_for<0, D / 16>([&](auto G) {
     constexpr int g = decltype(G)::value;
-    const float sc = static_cast<float>(__builtin_bit_cast(_Float16, srow[g]));
+    const float sc = static_cast<float>(__builtin_bit_cast(_Float16, srow[PT ? 0 : g]));
     static_for<0, 16>([&](auto C) {
       constexpr int c = 16 * g + decltype(C)::value;
       a[c] = code_at<BITS>(crow, c) * sc * lam[c];
@@ -212,7 +212,7 @@ __device__ __forceinline__ uint4 sign_mask(float4 s0, float4 s1) {
 // with kPF blocks' inputs in flight; LDS tiles are double-buffered.  SHARED: every row uses sign
 // row 0 (sign_bs == 0), so the sign mask is fixed per thread and the prefetch ring holds data
 // only, which leaves the registers for a deeper ring.
-template <int D, int BITS, bool HAS_LAMBDA, bool SHARED>
+template <int D, int BITS, bool HAS_LAMBDA, bool SHARED, bool PT>
 __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 ? 3 : 2))) void quantize_mfma_kernel(const uint16_t* __restrict__ x, FastDiv fd_tok,
                                                               FastDiv fd_heads, int pos, int capacity,
                                                               const float* __restrict__ sign, int64_t sign_bs,
@@ -228,6 +228,7 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
   __shared__ __align__(16) uint4 xt[HX][kVecs][NP];       // inputs, piece p of vector v at p ^ v
   __shared__ __align__(16) uint8_t ct[2][kVecs][CB];      // packed codes
   __shared__ __align__(16) uint16_t st[2][kVecs][NG];     // scales
+  __shared__ float tmax[PT ? D / 32 : 1][kVecs];          // per-token mode: per-wave absmax
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int n16 = lane & 15, r4 = lane >> 4;
@@ -270,8 +271,8 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
                                           *reinterpret_cast<const float4*>(sign + spc * 8 + 4))
                               : make_uint4(0u, 0u, 0u, 0u);
   uint4 pd[2][H], pm[2][SHARED ? 1 : H];
-  // Unconditional loads: a vector past the end reads the last vector again; its column of the
-  // product is never stored, and columns do not mix.
+  // A vector past the end reads the last vector again (no divergent branch around the load); its
+  // column of the product is never stored, and columns do not mix.
   auto load_piece = [&](uint32_t blk_, uint4& d_, uint4& m_) {
     const uint32_t gv = min(blk_ * kVecs + sv, n_vec - 1u);
     d_ = *reinterpret_cast<const uint4*>(x + int64_t(gv) * D + spc * 8);
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
 #pragma unroll
   for (int i = 0; i < H; ++i) {
     const uint32_t b0 = uint32_t(uint64_t(blockIdx.x) * nblk / gridDim.x);
-    load_piece(b0 + uint32_t(i), pd[0][i], pm[0][SHARED ? 0 : i]);
+    if (b0 + uint32_t(i) < blk_end) load_piece(b0 + uint32_t(i), pd[0][i], pm[0][SHARED ? 0 : i]);
   }
 
   // block blk from staged tile f (0..H-1); codes and scales go through LDS buffer f & 1
@@ -331,22 +332,35 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
         }
       }
     }
+    float u[2][4], a[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) u[i][j] = acc[i][j] * linv[i][j];
+      const uint32_t am = max(max(__float_as_uint(fabsf(u[i][0])), __float_as_uint(fabsf(u[i][1]))),
+                              max(__float_as_uint(fabsf(u[i][2])), __float_as_uint(fabsf(u[i][3]))));
+      a[i] = __uint_as_float(rows_max4(am));
+    }
+    if constexpr (PT) {
+      // one scale per vector: the absmax over all channels, i.e. over this wave's two groups and
+      // then over the waves (every lane of vector n16 holds the same per-wave value)
+      if (r4 == 0) tmax[w][n16] = fmaxf(a[0], a[1]);
+      __syncthreads();
+      float m = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < D / 32; ++ww) m = fmaxf(m, tmax[ww][n16]);
+      a[0] = a[1] = m;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int g = 2 * w + i;
-      float u[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) u[j] = acc[i][j] * linv[i][j];
-      const uint32_t am = max(max(__float_as_uint(fabsf(u[0])), __float_as_uint(fabsf(u[1]))),
-                              max(__float_as_uint(fabsf(u[2])), __float_as_uint(fabsf(u[3]))));
-      const float a = __uint_as_float(rows_max4(am));
-      const _Float16 sh = static_cast<_Float16>(scale_of<BITS>(a));
+      const _Float16 sh = static_cast<_Float16>(scale_of<BITS>(a[i]));
       const float sf = static_cast<float>(sh);
       const float inv = sf > 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
       uint32_t tq[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float vq = fmaf(u[j], inv, CM::magic);
+        float vq = fmaf(u[i][j], inv, CM::magic);
         vq = fminf(fmaxf(vq, CM::magic - CM::qmax), CM::magic + CM::qmax);
         tq[j] = __float_as_uint(vq);
       }
@@ -359,7 +373,7 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
                               CM::to_twos;
         *reinterpret_cast<uint32_t*>(&ct[buf][n16][16 * g + 4 * r4]) = word;
       }
-      if (r4 == 0) st[buf][n16][g] = __builtin_bit_cast(uint16_t, sh);
+      if (r4 == 0 && (!PT || g == 0)) st[buf][n16][g] = __builtin_bit_cast(uint16_t, sh);
     }
     __syncthreads();
     // ---- store codes (16 B per thread) and scales ----
@@ -372,7 +386,11 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
         if (gvs < n_vec)
           *reinterpret_cast<uint4*>(codes + slot_of(gvs) * CB + pc * 16) =
               *reinterpret_cast<const uint4*>(&ct[buf][v][pc * 16]);
-      } else if (tid >= UNITS && tid < UNITS + SUNITS) {
+      } else if (PT && tid >= UNITS && tid < UNITS + kVecs) {
+        const int v = tid - UNITS;  // one fp16 scale per vector
+        const uint32_t gvs = blk * kVecs + v;
+        if (gvs < n_vec) scales[slot_of(gvs)] = st[buf][v][0];
+      } else if (!PT && tid >= UNITS && tid < UNITS + SUNITS) {
         const int u = tid - UNITS;
         const int v = u / (NG / 8), pc = u - v * (NG / 8);
         const uint32_t gvs = blk * kVecs + v;
@@ -382,7 +400,8 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
       }
     }
   };
-  for (uint32_t blk = uint32_t(uint64_t(blockIdx.x) * nblk / gridDim.x); blk < blk_end;) {
+  uint32_t blk = uint32_t(uint64_t(blockIdx.x) * nblk / gridDim.x);
+  while (blk < blk_end) {  // blk advances inside the halves
     static_for<0, 2>([&](auto HF) {
       constexpr int hf = decltype(HF)::value;
       if (blk >= blk_end) return;  // work-group uniform
@@ -393,9 +412,11 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
         const uint4 v = pd[hf][i];
         xt[i][sv][spc ^ sv] = make_uint4(v.x ^ m.x, v.y ^ m.y, v.z ^ m.z, v.w ^ m.w);
       }
-      // ---- request the next half (past the range: harmless in-bounds re-reads) ----
+      // ---- request the next half's blocks of this range (a slot past the range keeps stale data
+      //      and is never processed) ----
 #pragma unroll
-      for (int i = 0; i < H; ++i) load_piece(blk + uint32_t(H + i), pd[1 - hf][i], pm[1 - hf][SHARED ? 0 : i]);
+      for (int i = 0; i < H; ++i)
+        if (blk + uint32_t(H + i) < blk_end) load_piece(blk + uint32_t(H + i), pd[1 - hf][i], pm[1 - hf][SHARED ? 0 : i]);
       __syncthreads();
       static_for<0, H>([&](auto F) {
         const uint32_t bk = blk + uint32_t(decltype(F)::value);
@@ -409,7 +430,7 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
 }  // namespace mq
 
 
-template <int D, int BITS, bool HAD>
+template <int D, int BITS, bool HAD, bool PT>
 hipError_t dequantize_dispatch_lambda(const DequantArgs& a, hipStream_t s) {
   const int rows = a.batch * a.kv_heads;
   const int tiles = (a.n_tok + kQuantThreads - 1) / kQuantThreads;
@@ -417,10 +438,10 @@ hipError_t dequantize_dispatch_lambda(const DequantArgs& a, hipStream_t s) {
   auto* codes = static_cast<const uint8_t*>(a.codes);
   auto* scales = static_cast<const uint16_t*>(a.scales);
   if (a.lambda)
-    hipLaunchKernelGGL((dequantize_kernel<D, BITS, true, HAD>), grid, block, 0, s, codes, scales, a.n_tok,
+    hipLaunchKernelGGL((dequantize_kernel<D, BITS, true, HAD, PT>), grid, block, 0, s, codes, scales, a.n_tok,
                        a.kv_heads, tiles, a.pos, a.capacity, a.sign, a.sign_bs, a.lambda, a.lambda_bs, a.out);
   else
-    hipLaunchKernelGGL((dequantize_kernel<D, BITS, false, HAD>), grid, block, 0, s, codes, scales, a.n_tok,
+    hipLaunchKernelGGL((dequantize_kernel<D, BITS, false, HAD, PT>), grid, block, 0, s, codes, scales, a.n_tok,
                        a.kv_heads, tiles, a.pos, a.capacity, a.sign, a.sign_bs, a.lambda, a.lambda_bs, a.out);
   return hipGetLastError();
 }
@@ -435,7 +456,7 @@ hipError_t calibrate_dispatch(const CalibArgs& a, hipStream_t s) {
 
 }  // namespace
 
-template <int D, int BITS>
+template <int D, int BITS, bool PT>
 hipError_t quantize_mfma_dispatch(const QuantArgs& a, hipStream_t s) {
   const uint32_t n_vec = uint32_t(a.batch) * uint32_t(a.kv_heads) * uint32_t(a.n_tok);  // < 2^31 (validated)
   const FastDiv fd_tok = FastDiv::make(uint32_t(a.n_tok)), fd_heads = FastDiv::make(uint32_t(a.kv_heads));
@@ -447,7 +468,7 @@ hipError_t quantize_mfma_dispatch(const QuantArgs& a, hipStream_t s) {
   auto* codes = static_cast<uint8_t*>(a.codes);
   auto* scales = static_cast<uint16_t*>(a.scales);
 #define KVQ_QLAUNCH(LAM, SH)                                                                                        \
-  hipLaunchKernelGGL((mq::quantize_mfma_kernel<D, BITS, LAM, SH>), dim3(grid), dim3(2 * D), 0, s, x, fd_tok, fd_heads, \
+  hipLaunchKernelGGL((mq::quantize_mfma_kernel<D, BITS, LAM, SH, PT>), dim3(grid), dim3(2 * D), 0, s, x, fd_tok, fd_heads, \
                      a.pos, a.capacity, a.sign, a.sign_bs, a.lambda, a.lambda_bs, codes, scales, n_vec, a.transform)
   const bool shared = a.sign_bs == 0;
   if (a.lambda) {
@@ -465,22 +486,33 @@ hipError_t quantize_mfma_dispatch(const QuantArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
+template <bool PT>
+hipError_t launch_quantize_g(const QuantArgs& a, hipStream_t s) {
   if (a.head_dim == 128)
-    return a.bits == 4 ? quantize_mfma_dispatch<128, 4>(a, s) : quantize_mfma_dispatch<128, 8>(a, s);
-  return a.bits == 4 ? quantize_mfma_dispatch<256, 4>(a, s) : quantize_mfma_dispatch<256, 8>(a, s);
+    return a.bits == 4 ? quantize_mfma_dispatch<128, 4, PT>(a, s) : quantize_mfma_dispatch<128, 8, PT>(a, s);
+  return a.bits == 4 ? quantize_mfma_dispatch<256, 4, PT>(a, s) : quantize_mfma_dispatch<256, 8, PT>(a, s);
 }
 
-hipError_t launch_dequantize(const DequantArgs& a, hipStream_t s) {
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
+  // group == head_dim: one scale per vector (the per-token comparison mode)
+  return a.group == a.head_dim ? launch_quantize_g<true>(a, s) : launch_quantize_g<false>(a, s);
+}
+
+template <bool PT>
+hipError_t launch_dequantize_g(const DequantArgs& a, hipStream_t s) {
   const bool had = a.transform != 0;
   if (a.head_dim == 128) {
     if (a.bits == 4)
-      return had ? dequantize_dispatch_lambda<128, 4, true>(a, s) : dequantize_dispatch_lambda<128, 4, false>(a, s);
-    return had ? dequantize_dispatch_lambda<128, 8, true>(a, s) : dequantize_dispatch_lambda<128, 8, false>(a, s);
+      return had ? dequantize_dispatch_lambda<128, 4, true, PT>(a, s) : dequantize_dispatch_lambda<128, 4, false, PT>(a, s);
+    return had ? dequantize_dispatch_lambda<128, 8, true, PT>(a, s) : dequantize_dispatch_lambda<128, 8, false, PT>(a, s);
   }
   if (a.bits == 4)
-    return had ? dequantize_dispatch_lambda<256, 4, true>(a, s) : dequantize_dispatch_lambda<256, 4, false>(a, s);
-  return had ? dequantize_dispatch_lambda<256, 8, true>(a, s) : dequantize_dispatch_lambda<256, 8, false>(a, s);
+    return had ? dequantize_dispatch_lambda<256, 4, true, PT>(a, s) : dequantize_dispatch_lambda<256, 4, false, PT>(a, s);
+  return had ? dequantize_dispatch_lambda<256, 8, true, PT>(a, s) : dequantize_dispatch_lambda<256, 8, false, PT>(a, s);
+}
+
+hipError_t launch_dequantize(const DequantArgs& a, hipStream_t s) {
+  return a.group == a.head_dim ? launch_dequantize_g<true>(a, s) : launch_dequantize_g<false>(a, s);
 }
 
 hipError_t launch_calibrate(const CalibArgs& a, hipStream_t s) {

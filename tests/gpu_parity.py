@@ -45,12 +45,12 @@ def planes(layout, bits, fill=0xAB):
     return codes, scales
 
 
-def gpu_quantize(x16, s, lam, bits, capacity=None, pos=0, sign_bs=0, lambda_bs=None, transform="srft"):
+def gpu_quantize(x16, s, lam, bits, capacity=None, pos=0, sign_bs=0, lambda_bs=None, transform="srft", group=16):
     """x16 [B, H, n, d] fp16; lam [B?, H, d] or None.  Returns (codes u8 [B,H,cap,d*bits/8],
-    scales f16 [B,H,cap,d/16]) as numpy, plus the layout."""
+    scales f16 [B,H,cap,d/group]) as numpy, plus the layout."""
     B, H, n, d = x16.shape
     cap = capacity or (pos + n)
-    lay = kvq.make_layout(B, H, H, d, cap, k_bits=bits, v_bits=4, transform=transform)
+    lay = kvq.make_layout(B, H, H, d, cap, k_bits=bits, v_bits=4, transform=transform, group_size=group)
     codes, scales = planes(lay, bits)
     lam_t = None if lam is None else dev(np.asarray(lam, np.float32))
     if lambda_bs is None:
@@ -59,16 +59,16 @@ def gpu_quantize(x16, s, lam, bits, capacity=None, pos=0, sign_bs=0, lambda_bs=N
                      codes, scales)
     torch.cuda.synchronize()
     cb = codes.cpu().numpy().reshape(B, H, cap, d * bits // 8)
-    sc = scales.cpu().numpy().view(np.float16).reshape(B, H, cap, d // 16)
+    sc = scales.cpu().numpy().view(np.float16).reshape(B, H, cap, d // group)
     return cb, sc, lay
 
 
-def check_quantize(gpu_bytes, gpu_scales, u, bits, label=""):
+def check_quantize(gpu_bytes, gpu_scales, u, bits, label="", group=16):
     """Compare GPU planes (for the vectors whose rotated, lambda-scaled values are u) with the
     oracle's decision.  u: float64 [..., d]; gpu_bytes/scales: matching leading shape."""
     qmax = O.QMAX[bits]
     d = u.shape[-1]
-    oc, osc = O.quantize_decision(u, bits)
+    oc, osc = O.quantize_decision(u, bits, group)
     gc = O.unpack_codes(gpu_bytes, bits)
     # packing: the GPU bytes are exactly the oracle packing of the codes they hold
     assert np.array_equal(O.pack_codes(gc, bits), gpu_bytes), f"{label}: packing not bit-exact"
@@ -79,18 +79,18 @@ def check_quantize(gpu_bytes, gpu_scales, u, bits, label=""):
     assert ulp.max() <= 1, f"{label}: scale differs by {ulp.max()} ulp"
     n_groups = ulp.size
     assert (ulp > 0).sum() <= max(1, CODE_MISMATCH_RATE * n_groups), f"{label}: {(ulp > 0).sum()} scale ulps"
-    same = np.repeat(ulp == 0, 16, axis=-1).reshape(gc.shape)
+    same = np.repeat(ulp == 0, group, axis=-1).reshape(gc.shape)
     diff = (gc != oc) & same
     n_diff = int(diff.sum())
     assert n_diff <= max(1, CODE_MISMATCH_RATE * gc.size), f"{label}: {n_diff} codes differ"
     if n_diff:
         assert np.abs(gc[diff].astype(int) - oc[diff].astype(int)).max() == 1, f"{label}: code off by > 1"
-        sc = np.repeat(osc.astype(np.float64), 16, axis=-1).reshape(u.shape)
+        sc = np.repeat(osc.astype(np.float64), group, axis=-1).reshape(u.shape)
         ratio = u[diff] / sc[diff]
         dist = np.abs(np.abs(ratio - np.floor(ratio)) - 0.5)
         assert dist.max() <= TIE_WINDOW, f"{label}: non-tie mismatch (distance {dist.max():.3g})"
     if (~same).any():
-        sc = np.repeat(gs.astype(np.float64), 16, axis=-1).reshape(u.shape)
+        sc = np.repeat(gs.astype(np.float64), group, axis=-1).reshape(u.shape)
         r = u[~same] / np.where(sc[~same] > 0, sc[~same], 1.0)
         err = np.abs(r - gc[~same])
         ok = (sc[~same] == 0) | (err <= 0.5 + TIE_WINDOW) | (np.abs(gc[~same]) == qmax)

@@ -111,6 +111,22 @@ def test_group_size_unsupported(L):
     assert quantize(L, lay) == 2 and "group_size" in msg(L)
 
 
+@pytest.mark.parametrize("d", [128, 256])
+def test_per_token_group_is_a_write_path_mode(L, d):
+    """group_size == head_dim (one scale per vector): accepted by the write path, dequantize and
+    the sizing calls (one fp16 scale per token), rejected by both quantized decode calls."""
+    lay = layout(head_dim=d, group_size=d)
+    assert kvq.kvq_scales_bytes(lay) == 2 * 2 * 64 * 2
+    assert kvq.kvq_scales_bytes(layout(head_dim=d)) == 2 * 2 * 64 * (d // 16) * 2
+    assert quantize(L, lay, x=MIS) == 3  # validation passes the group check, stops at x
+    st = L.kvq_dequantize(ctypes.byref(lay), 4, GOOD, GOOD, 0, 1, GOOD, 0, NULL, 0, MIS, NULL)
+    assert st == 3 and "out" in msg(L)
+    assert decode(L, lay) == 2 and "group_size" in msg(L)
+    st = L.kvq_decode_attn_append(ctypes.byref(lay), GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 16, NULL, GOOD,
+                                  GOOD, 0, NULL, NULL, 0, ctypes.c_float(0), GOOD, 1 << 30, GOOD, NULL)
+    assert st == 2 and "group_size" in msg(L)
+
+
 def test_transform_field(L):
     lay = layout(transform="srht")
     assert lay.transform == 1 and layout().transform == 0

@@ -178,3 +178,68 @@ def test_exact_ties_round_half_to_even():
     codes, scales = O.quantize_decision(u, 4)
     assert scales[0, 0] == np.float16(1.0)
     assert codes[0].tolist() == [7, 2, -2, 4, -4, 0, 0, 2, -2, 4, -4, 6, -6, 6, -6, 0]
+
+
+# ---- one scale per vector (group = d): the per-token comparison mode ----
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("d", [128, 256])
+def test_per_token_equals_grouped_when_every_group_has_the_same_absmax(bits, d):
+    """If every group of 16 holds the same absmax, the vector's one scale equals every group's
+    scale, so the codes of the two modes are identical (catches a wrong axis or reshape)."""
+    rng = np.random.default_rng(11 + d + bits)
+    u = rng.uniform(-1, 1, size=(40, d))
+    amax = rng.uniform(0.5, 3.0, size=(40, 1))
+    u = u / np.abs(u).max(-1, keepdims=True) * 0.999 * amax
+    g = u.reshape(40, d // G, G)
+    idx = rng.integers(0, G, size=(40, d // G))
+    sign = np.where(rng.random((40, d // G)) < 0.5, -1.0, 1.0)
+    np.put_along_axis(g, idx[..., None], (sign * amax)[..., None], axis=-1)
+    u = g.reshape(40, d)
+    c_tok, s_tok = O.quantize_decision(u, bits, group=d)
+    c_grp, s_grp = O.quantize_decision(u, bits)
+    assert s_tok.shape == (40, 1) and s_grp.shape == (40, d // G)
+    assert np.array_equal(np.repeat(s_tok, d // G, axis=-1), s_grp)
+    assert np.array_equal(c_tok, c_grp)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_per_token_scale_is_the_vector_absmax(bits):
+    """group = d: scale = fp16(max|u| / qmax); the largest element maps to +-qmax; every code is
+    within half a step of u / scale; dequantize inverts up to that error."""
+    d = 128
+    x, s, lam = _data(21, 64, d)
+    qmax = O.QMAX[bits]
+    u = O.rotated_scaled(x, s, lam)
+    c, sc = O.quantize_decision(u, bits, group=d)
+    u32 = u.astype(np.float32)
+    want = (np.abs(u32).max(-1) / np.float32(qmax)).astype(np.float16)
+    assert np.array_equal(sc[:, 0], want)
+    top = np.abs(u32).argmax(-1)
+    assert np.all(np.abs(c[np.arange(64), top]) == qmax)
+    step = sc.astype(np.float64)
+    assert np.all(np.abs(u - c * step) <= 0.5 * step * (1 + 1e-6) + 1e-12)
+    xh = O.dequantize(c, sc, s, lam, group=d)
+    bound = np.linalg.norm(lam * 0.5 * step, axis=-1) * (1 + 1e-9)
+    assert np.all(np.linalg.norm(xh - x.astype(np.float64), axis=-1) <= bound + 1e-9)
+
+
+def test_grouped_scales_beat_one_scale_per_vector_after_rotation():
+    """With the rotation and lambda in place, 16-channel groups still lower the reconstruction
+    error against one scale per vector on outlier keys (Methodology 3's per-group claim), and
+    one scale per vector without rotation is the worst of the three."""
+    d = 128
+    rng = np.random.default_rng(9)
+    x = rng.standard_t(3, size=(512, d))
+    x[:, rng.choice(d, 4, replace=False)] *= 20
+    x16 = x.astype(np.float16)
+    x64 = x16.astype(np.float64)
+    s = np.where(rng.random(d) < 0.5, -1.0, 1.0)
+    lam = O.calibrate_lambda(x16, s, 256)
+    err = {}
+    for name, grp in (("group16", G), ("per_token", d)):
+        c, sc = O.quantize(x16, s, lam, 4, group=grp)
+        err[name] = np.linalg.norm(O.dequantize(c, sc, s, lam, group=grp) - x64)
+    a = np.abs(x64).max(-1, keepdims=True) / 7
+    err["per_token_unrotated"] = np.linalg.norm(np.clip(np.rint(x64 / a), -7, 7) * a - x64)
+    assert err["group16"] < err["per_token"] < err["per_token_unrotated"]
