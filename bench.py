@@ -330,6 +330,34 @@ def main():
     nb = max(R, Rf)
     res_bq = timer.run(lambda i: quantize_all(planes[i % R], *kv16[i % Rf]), nb, 2 * nb, args.warmup)
 
+    # one scale per vector (group = d), the per-token comparison mode of the write path: bulk
+    # quantize of K and V, all layers, and the round-trip error of both modes on layer 0's K
+    lay_pt = kvq.make_layout(LB, H, Hq, d, S, k_bits=w.k_bits, v_bits=w.v_bits, transform=args.transform,
+                             group_size=d)
+    pt = (torch.empty(kvq.kvq_codes_bytes(lay_pt, w.k_bits), dtype=torch.uint8, device="cuda"),
+          torch.empty(kvq.kvq_scales_bytes(lay_pt) // 2, dtype=torch.int16, device="cuda"),
+          torch.empty(kvq.kvq_codes_bytes(lay_pt, w.v_bits), dtype=torch.uint8, device="cuda"),
+          torch.empty(kvq.kvq_scales_bytes(lay_pt) // 2, dtype=torch.int16, device="cuda"))
+
+    def quantize_all_pt(xk, xv):
+        kvq.kvq_quantize(lay_pt, w.k_bits, xk, 0, S, s, 0, lam_k, lbs, pt[0], pt[1])
+        kvq.kvq_quantize(lay_pt, w.v_bits, xv, 0, S, s, 0, lam_v, lbs, pt[2], pt[3])
+
+    res_pt = timer.run(lambda i: quantize_all_pt(*kv16[i % Rf]), Rf, 2 * Rf, args.warmup)
+    quantize_all_pt(kx, vx)
+    n_err = min(S, 4096)
+    x0 = kx[:B, :, :n_err].float()
+    round_trip = {}
+    for name, lay_e, p in (("group16", lay, base), ("per_token", lay_pt, pt)):
+        lay0 = kvq.make_layout(B, H, Hq, d, S, k_bits=w.k_bits, v_bits=w.v_bits, transform=args.transform,
+                               group_size=lay_e.group_size)
+        rec = torch.empty(B * H * n_err * d, dtype=torch.float32, device="cuda")
+        kvq.kvq_dequantize(lay0, w.k_bits, p[0][:kvq.kvq_codes_bytes(lay0, w.k_bits)],
+                           p[1][:kvq.kvq_scales_bytes(lay0) // 2], 0, n_err, s, 0,
+                           None if lam_k is None else lam_k[:B * H * d], lbs, rec)
+        round_trip[name] = float(torch.linalg.vector_norm(rec.view_as(x0) - x0) / torch.linalg.vector_norm(x0))
+    del x0, rec
+
     dec_bytes = q_bytes  # every code and scale byte of the cache is read once per decode step
     n_vec = 2 * LB * H * S
     bq_bytes = n_vec * 2 * d + q_bytes
@@ -377,6 +405,11 @@ def main():
                           "GBps_moved": round(bq_bytes / (res_bq["ms_mean"] * 1e-3) / 1e9, 2),
                           "frac_hbm_peak": round(bq_bytes / (res_bq["ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                           "vectors": n_vec, "ms": round(res_bq["ms_mean"], 5)},
+        "quantize_per_token_scale": {
+            "Mvectors_per_s": round(n_vec / (res_pt["ms_mean"] * 1e-3) / 1e6, 2), "ms": round(res_pt["ms_mean"], 5),
+            "k_relative_error": {k: round(v, 5) for k, v in round_trip.items()},
+            "note": "group = head_dim (one fp16 scale per vector), K and V of all layers; the error is "
+                    "||dequant(quant(K)) - K|| / ||K|| over layer 0's first tokens, both modes"},
         "roofline": {"bound": "hbm", "kernel": "decode_kernel (one launch per kvq_decode_attn call)",
                      "achieved": round(dec_gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": profiled_traffic(w.name),
