@@ -204,6 +204,36 @@ kvq_status kvq_decode_attn_append(const kvq_layout* layout, const void* q_f16, c
                                   size_t workspace_bytes, float* out, void* stream);
 
 /*
+ * kvq_decode_attn_paged -- kvq_decode_attn (and, with k_new_f16/v_new_f16, the fused append of
+ * kvq_decode_attn_append) over a paged cache: the planes hold num_pages pages of page_size
+ * tokens, codes uint8 [num_pages, kv_heads, page_size, d*bits/8] and scales fp16
+ * [num_pages, kv_heads, page_size, d/16], and token t of sequence b lives in page
+ * page_table[b * pages_per_seq + t / page_size] at offset t % page_size.  Serving caches grow
+ * by pages instead of reserving `capacity` tokens per sequence (the pages' paged / sliding
+ * window serving setting).  The computation, its precision and its result are those of
+ * kvq_decode_attn on the same tokens.
+ *   page_table    : device int32 [batch, pages_per_seq]; entries are clamped to [0, num_pages)
+ *                   on the device (an out-of-range entry reads a wrong page, never out of the
+ *                   planes); entries of pages past a sequence's length are not read
+ *   page_size     : a positive multiple of 64 (KVQ_ERR_UNSUPPORTED otherwise)
+ *   pages_per_seq : >= 1, and layout->capacity must equal pages_per_seq * page_size
+ *   num_pages     : >= 1, pages in the planes
+ *   k_new_f16, v_new_f16 : both NULL (attend only) or both set (append token L - 1 of every
+ *                   sequence into its page first, as kvq_decode_attn_append; the head tile
+ *                   limit of that call applies)
+ * Other arguments, the workspace rules and the errors are those of kvq_decode_attn; the
+ * workspace size from kvq_decode_attn_workspace_bytes covers paged calls.
+ */
+kvq_status kvq_decode_attn_paged(const kvq_layout* layout, const void* q_f16, const void* k_new_f16,
+                                 const void* v_new_f16, void* k_codes, void* k_scales, void* v_codes,
+                                 void* v_scales, const int32_t* page_table, int32_t pages_per_seq,
+                                 int32_t page_size, int32_t num_pages, int32_t seq_len,
+                                 const int32_t* seq_lens, const float* sign_k, const float* sign_v,
+                                 int64_t sign_batch_stride, const float* lambda_k,
+                                 const float* lambda_v, int64_t lambda_batch_stride, float sm_scale,
+                                 void* workspace, size_t workspace_bytes, float* out, void* stream);
+
+/*
  * kvq_decode_attn_fp16 -- the same decode attention over an unquantized fp16 cache (the
  * comparator): k_f16, v_f16 are fp16 [batch, kv_heads, capacity, head_dim]; no rotation, no
  * lambda.  layout->k_bits/v_bits are ignored.  Other arguments as kvq_decode_attn.

@@ -292,6 +292,61 @@ kvq_status kvq_decode_attn_append(const kvq_layout* L, const void* q_f16, const 
   return hip_status(kvq_impl::launch_decode(a, p, static_cast<hipStream_t>(stream)), fn);
 }
 
+kvq_status kvq_decode_attn_paged(const kvq_layout* L, const void* q_f16, const void* k_new_f16,
+                                 const void* v_new_f16, void* k_codes, void* k_scales, void* v_codes, void* v_scales,
+                                 const int32_t* page_table, int32_t pages_per_seq, int32_t page_size,
+                                 int32_t num_pages, int32_t seq_len, const int32_t* seq_lens, const float* sign_k,
+                                 const float* sign_v, int64_t sign_batch_stride, const float* lambda_k,
+                                 const float* lambda_v, int64_t lambda_batch_stride, float sm_scale, void* workspace,
+                                 size_t workspace_bytes, float* out, void* stream) {
+  const char* fn = "kvq_decode_attn_paged";
+  KVQ_TRY(check_layout(L, fn));
+  KVQ_TRY(check_bits(L->k_bits, fn, "k_bits"));
+  KVQ_TRY(check_bits(L->v_bits, fn, "v_bits"));
+  KVQ_TRY(check_decode_group(L, fn));
+  if (page_size < 64 || page_size % 64 != 0)
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: page_size %d (supported: a positive multiple of 64)", fn, page_size);
+  if (pages_per_seq < 1 || num_pages < 1)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: pages_per_seq (%d) and num_pages (%d) must be >= 1", fn,
+                pages_per_seq, num_pages);
+  if ((long long)pages_per_seq * page_size != L->capacity)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: capacity (%d) must equal pages_per_seq x page_size (%lld)", fn,
+                L->capacity, (long long)pages_per_seq * page_size);
+  if ((long long)num_pages * L->kv_heads * page_size > (1LL << 40))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: num_pages*kv_heads*page_size too large", fn);
+  const bool append = k_new_f16 != nullptr || v_new_f16 != nullptr;
+  KVQ_TRY(check_decode_common(L, q_f16, seq_len, seq_lens, sm_scale, workspace, workspace_bytes, out, fn, append));
+  if (append) {
+    KVQ_TRY(check_ptr(k_new_f16, 16, fn, "k_new"));
+    KVQ_TRY(check_ptr(v_new_f16, 16, fn, "v_new"));
+  }
+  KVQ_TRY(check_ptr(page_table, 4, fn, "page_table"));
+  KVQ_TRY(check_ptr(k_codes, 16, fn, "k_codes"));
+  KVQ_TRY(check_ptr(k_scales, 16, fn, "k_scales"));
+  KVQ_TRY(check_ptr(v_codes, 16, fn, "v_codes"));
+  KVQ_TRY(check_ptr(v_scales, 16, fn, "v_scales"));
+  KVQ_TRY(check_ptr(sign_k, 4, fn, "sign_k"));
+  KVQ_TRY(check_ptr(sign_v, 4, fn, "sign_v"));
+  KVQ_TRY(check_opt_ptr(lambda_k, 4, fn, "lambda_k"));
+  KVQ_TRY(check_opt_ptr(lambda_v, 4, fn, "lambda_v"));
+  KVQ_TRY(check_strides(sign_batch_stride, lambda_batch_stride, fn));
+  const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt(float(L->head_dim));
+  const kvq_impl::DecodePlan p =
+      kvq_impl::plan_decode(L->batch, L->kv_heads, L->q_heads, L->head_dim, seq_len, seq_len, false, append, true);
+  kvq_impl::DecodeArgs a{L->batch,   L->kv_heads, L->q_heads, L->head_dim, L->k_bits,   L->v_bits,
+                         L->capacity, seq_len,    seq_lens,   q_f16,       k_codes,     k_scales,
+                         v_codes,    v_scales,    sign_k,     sign_v,      sign_batch_stride, lambda_k,
+                         lambda_v,   lambda_batch_stride,     scale,       workspace,   out};
+  a.transform = L->transform;
+  a.k_new = k_new_f16;
+  a.v_new = v_new_f16;
+  a.page_table = page_table;
+  a.page_size = page_size;
+  a.pages_per_seq = pages_per_seq;
+  a.num_pages = num_pages;
+  return hip_status(kvq_impl::launch_decode(a, p, static_cast<hipStream_t>(stream)), fn);
+}
+
 kvq_status kvq_decode_attn_fp16(const kvq_layout* L, const void* q_f16, const void* k_f16, const void* v_f16,
                                 int32_t seq_len, const int32_t* seq_lens, float sm_scale, void* workspace,
                                 size_t workspace_bytes, float* out, void* stream) {

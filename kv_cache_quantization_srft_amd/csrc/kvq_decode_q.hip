@@ -10,7 +10,7 @@
 //   prologue: the first superblock's loads go out, then the work-group rotates its query heads
 //             (v_mfma_f32_16x16x32_f16, A = the sign-flipped fp16 query, B = 16 Q split into
 //             fp16 hi + lo from a constant table in operand order) and splits every rotated
-//             channel into a 16-bit integer (two int8 digits, per-head step sigma) laid out as
+//             channel into a 24-bit integer (three int8 digits, per-head step sigma) laid out as
 //             the A operand of the score MFMA.
 //   main loop: each wave walks 64-token superblocks:
 //     scores : v_mfma_i32_16x16x64_i8.  A rows are (head, group) pairs holding the query digits
@@ -65,7 +65,7 @@ struct QGeom {
   static constexpr int LDS_P = 16 * kSB * 4;
   static constexpr int LDS_WAVE = LDS_V + LDS_S + LDS_K + LDS_P + 16 * 4;
   static constexpr int LDS_EPI = (kWaves * 16 * 2 + 16 * kWaves + 32 + kWaves * (D == 128 ? 16 : 8) * D) * 4;
-  static constexpr int LDS_Q = 4 * NS * 2 * 1024 + 256;  // prologue: digit operands + head maxima
+  static constexpr int LDS_Q = 4 * NS * 3 * 1024 + 256;  // prologue: digit operands + head maxima
   static constexpr int LDS_M = merge_lds_floats<D>() * 4;
   // append staging: K codes, K scales, V codes, V scales of the new token (16-byte aligned parts)
   static constexpr int APP_KS = KRB, APP_V = KRB + NG * 2, APP_VS = APP_V + VRB, APP_BYTES = APP_VS + NG * 2;
@@ -113,17 +113,16 @@ __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, int off) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// Loads of the superblock starting at token `base` (wave-uniform) of one (sequence, kv head)
-// row; L = the row's token count.  The resources start at the superblock, so every lane offset
+// Loads of the superblock whose first token sits at plane slot t0 (wave-uniform); nrem = the
+// row's tokens from that one on (loads past them return zero).  The resources start at the superblock, so every lane offset
 // is a constant and the address arithmetic is scalar.  Two parts: the K codes (consumed by the
 // scores) and the rest (V codes, V scales, K scales: staged in LDS first thing), so that the
 // rest of the next superblock can be requested as soon as this one's is staged.
 template <int D, int KB, int VB>
-__device__ __forceinline__ void load_sb_kcodes(SBRegs<D, KB, VB>& r, const uint8_t* kc, int64_t rowbase, int base, int L,
-                                               int lane) {
+__device__ __forceinline__ void load_sb_kcodes(SBRegs<D, KB, VB>& r, const uint8_t* kc, int64_t t0, int nrem, int lane) {
   using Gm = QGeom<D, KB, VB>;
   const int n16 = lane & 15, r4 = lane >> 4;
-  const __amdgpu_buffer_rsrc_t rk = row_rsrc(kc + (rowbase + base) * Gm::KRB, (L - base) * Gm::KRB);
+  const __amdgpu_buffer_rsrc_t rk = row_rsrc(kc + t0 * Gm::KRB, nrem * Gm::KRB);
 #pragma unroll
   for (int sb = 0; sb < 4; ++sb) {
 #pragma unroll
@@ -139,10 +138,8 @@ __device__ __forceinline__ void load_sb_kcodes(SBRegs<D, KB, VB>& r, const uint8
 
 template <int D, int KB, int VB>
 __device__ __forceinline__ void load_sb_rest(SBRegs<D, KB, VB>& r, const uint16_t* ks, const uint8_t* vc,
-                                             const uint16_t* vs, int64_t rowbase, int base, int L, int lane) {
+                                             const uint16_t* vs, int64_t t0, int nrem, int lane) {
   using Gm = QGeom<D, KB, VB>;
-  const int nrem = L - base;
-  const int64_t t0 = rowbase + base;
   const __amdgpu_buffer_rsrc_t rks = row_rsrc(ks + t0 * Gm::NG, nrem * Gm::NG * 2);
   const __amdgpu_buffer_rsrc_t rv = row_rsrc(vc + t0 * Gm::VRB, nrem * Gm::VRB);
   const __amdgpu_buffer_rsrc_t rvs = row_rsrc(vs + t0 * Gm::NG, nrem * Gm::NG * 2);
@@ -168,10 +165,10 @@ __device__ __forceinline__ void load_sb_rest(SBRegs<D, KB, VB>& r, const uint16_
 
 template <int D, int KB, int VB>
 __device__ __forceinline__ void load_superblock(SBRegs<D, KB, VB>& r, const uint8_t* kc, const uint16_t* ks,
-                                                const uint8_t* vc, const uint16_t* vs, int64_t rowbase, int base,
-                                                int L, int lane) {
-  load_sb_kcodes<D, KB, VB>(r, kc, rowbase, base, L, lane);
-  load_sb_rest<D, KB, VB>(r, ks, vc, vs, rowbase, base, L, lane);
+                                                const uint8_t* vc, const uint16_t* vs, int64_t t0, int nrem,
+                                                int lane) {
+  load_sb_kcodes<D, KB, VB>(r, kc, t0, nrem, lane);
+  load_sb_rest<D, KB, VB>(r, ks, vc, vs, t0, nrem, lane);
 }
 
 // Overwrite, in the registers of a loaded superblock, the token at superblock offset tl
@@ -285,13 +282,13 @@ __device__ __forceinline__ void values_int8(int lane, const v8h (&a_hi)[2], cons
 // Everything one wave does with one superblock already in registers.
 template <int D, int KB, int VB, int NRB>
 __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int base, int t_end, int lane,
-                                                   const v4i (&aop)[NRB][D / 64][2], const float (&sig)[NRB],
+                                                   const v4i (&aop)[NRB][D / 64][3], const float (&sig)[NRB],
                                                    float (&m_run)[NRB], float (&l_run)[NRB], v4f (&acc)[D / 16],
                                                    uint8_t* vtile, uint16_t* stile, uint16_t* ktile, float* ptile,
                                                    float* atile, const uint8_t* __restrict__ kc,
                                                    const uint16_t* __restrict__ ks, const uint8_t* __restrict__ vc,
-                                                   const uint16_t* __restrict__ vs, int64_t rowbase, int next_base,
-                                                   int L) {
+                                                   const uint16_t* __restrict__ vs, int next_base, int64_t next_t0,
+                                                   int next_nrem) {
   using Gm = QGeom<D, KB, VB>;
   constexpr int NS = Gm::NS, NG = Gm::NG;
   const int n16 = lane & 15, r4 = lane >> 4;
@@ -340,7 +337,7 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int bas
       *reinterpret_cast<uint4*>(kt + i) = make_uint4(r.ksw[i], r.ksw[i + 1], r.ksw[i + 2], r.ksw[i + 3]);
   }
   // the staged parts of the next superblock load during this one's scores, softmax and values
-  if (next_base < t_end) load_sb_rest<D, KB, VB>(r, ks, vc, vs, rowbase, next_base, L, lane);
+  if (next_base < t_end) load_sb_rest<D, KB, VB>(r, ks, vc, vs, next_t0, next_nrem, lane);
   wave_sync_lds();
 
   // ---------------- scores (int8 MFMA, exact integer group dots) ----------------
@@ -377,13 +374,15 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int bas
       for (int s = 0; s < NS; ++s) {
         const v4i zero = {0, 0, 0, 0};
         const v4i chi = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[rb][s][0], bop[s], zero, 0, 0, 0);
-        const v4i clo = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[rb][s][1], bop[s], zero, 0, 0, 0);
+        const v4i cmi = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[rb][s][1], bop[s], zero, 0, 0, 0);
+        const v4i clo = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[rb][s][2], bop[s], zero, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int dot = chi[i] * 256 + clo[i];
+          // 256 hi + mid exactly in int32 (|.| < 2^26), the lo digit's dot added in fp32
+          const int dot = chi[i] * 256 + cmi[i];
+          const float f = fmaf(static_cast<float>(clo[i]), 1.0f / 256.0f, static_cast<float>(dot));
           const int gi = i * NS + s;
-          s_acc = (gi & 1) ? fma_mix_f16<1>(static_cast<float>(dot), kraw[gi >> 1], s_acc)
-                           : fma_mix_f16<0>(static_cast<float>(dot), kraw[gi >> 1], s_acc);
+          s_acc = (gi & 1) ? fma_mix_f16<1>(f, kraw[gi >> 1], s_acc) : fma_mix_f16<0>(f, kraw[gi >> 1], s_acc);
         }
       }
       sc[sb][rb] = valid ? s_acc * sig[rb] : -INFINITY;
@@ -391,7 +390,7 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int bas
   }
 
   // the K codes of this superblock are consumed: the next one's load during softmax + values
-  if (next_base < t_end) load_sb_kcodes<D, KB, VB>(r, kc, rowbase, next_base, L, lane);
+  if (next_base < t_end) load_sb_kcodes<D, KB, VB>(r, kc, next_t0, next_nrem, lane);
 
   // ---------------- online softmax per head (16-lane rows) ----------------
   bool rescale = false;
@@ -511,6 +510,11 @@ struct QDecodeParams {
   // row, quantized into position L - 1 of the planes by the work-group holding that position
   const uint16_t* k_new;
   const uint16_t* v_new;
+  // paged cache (page_table == nullptr: contiguous rows of `capacity` tokens): token t of
+  // sequence b sits at slot (page * kv_heads + kv head) * page_size + t % page_size of the
+  // planes, page = page_table[b * pages_per_seq + t / page_size] clamped to [0, num_pages)
+  const int32_t* page_table;
+  int page_size, pages_per_seq, num_pages;
 };
 
 // APP: the appending variant (kvq_decode_attn_append), a separate instance so that the plain
@@ -546,6 +550,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   const uint8_t* vc = P.vc;
   const uint16_t* vs = P.vs;
   constexpr int kStride = kWaves * kSB;
+
+  // Paged cache: lane k of this wave holds the page of the wave's superblock k (token
+  // t_begin + 64 w + 256 k; a superblock never straddles a page since page_size is a multiple
+  // of 64).  Issued first, so the first superblock's address waits only for this load.  Entries
+  // past the row's tokens read a valid entry and are not used; pages are clamped to the planes.
+  const bool paged = P.page_table != nullptr;
+  int pg_v = 0;
+  if (paged) {
+    const int tb = min(t_begin + w * kSB + lane * kStride, max(L - 1, 0));
+    const int e = min(tb / P.page_size, P.pages_per_seq - 1);
+    pg_v = min(max(P.page_table[int64_t(b) * P.pages_per_seq + e], 0), P.num_pages - 1);
+  }
+  // plane slot of superblock k of this wave (first token bs)
+  auto sb_slot = [&](int bs, int k) -> int64_t {
+    if (!paged) return rowbase + bs;
+    const int pg = __builtin_amdgcn_readlane(pg_v, min(k, 63));
+    return (int64_t(pg) * P.kv_heads + kvh) * P.page_size + bs % P.page_size;
+  };
 
   // ---------------- prologue: rotated query -> int8 digit operands ----------------
   // Its few loads go out first (loads complete in issue order), then the first superblock's.
@@ -596,10 +618,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
 
   SBRegs<D, KB, VB> ra;
   int base = t_begin + w * kSB;
-  if (base < t_end) load_superblock<D, KB, VB>(ra, kc, ks, vc, vs, rowbase, base, L, lane);
+  if (base < t_end) load_superblock<D, KB, VB>(ra, kc, ks, vc, vs, sb_slot(base, 0), L - base, lane);
 
   // LDS of the prologue (aliases the main-loop tiles): digit operands, per-wave head maxima
-  constexpr int kDigBytes = NRB * NS * 2 * 1024;
+  constexpr int kDigBytes = NRB * NS * 3 * 1024;
   uint8_t* dig = smem;
   float* pmax = reinterpret_cast<float*>(smem + kDigBytes);  // [kWaves][16]
   for (int i = threadIdx.x; i < kDigBytes / 16; i += kThreads)
@@ -692,7 +714,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
     // the new token leaves for the planes (every head tile patches its own registers)
     constexpr int UK = Gm::KRB / 16, US = NG * 2 / 16, UV = Gm::VRB / 16;
     const int tid = threadIdx.x;
-    const int64_t slot = rowbase + t_app;
+    int64_t slot = rowbase + t_app;
+    if (paged) {
+      const int e = min(t_app / P.page_size, P.pages_per_seq - 1);
+      const int pg = min(max(P.page_table[int64_t(b) * P.pages_per_seq + e], 0), P.num_pages - 1);
+      slot = (int64_t(pg) * P.kv_heads + kvh) * P.page_size + t_app % P.page_size;
+    }
     if (tid < UK) {
       *reinterpret_cast<uint4*>(const_cast<uint8_t*>(kc) + slot * Gm::KRB + 16 * tid) =
           *reinterpret_cast<const uint4*>(appbuf + 16 * tid);
@@ -710,7 +737,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
           *reinterpret_cast<const uint4*>(appbuf + Gm::APP_VS + 16 * u);
     }
   }
-  // per-head step: the largest |q_hat| maps to 32639 so both digits fit int8
+  // per-head step: the largest |q_hat| maps to 32639 * 256 so all three digits fit int8 (two
+  // digits, 16 bits relative to the largest channel, left score errors up to ~1e-2 when lambda_K
+  // spans a decade and keys exceed the calibration range)
   float sgm[4];
   {
     float4 mx = *reinterpret_cast<const float4*>(pmax + 4 * r4);
@@ -721,7 +750,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
     }
     const float m4[4] = {mx.x, mx.y, mx.z, mx.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sgm[i] = m4[i] > 0.0f ? m4[i] / 32639.0f : 1.0f;
+    for (int i = 0; i < 4; ++i) sgm[i] = m4[i] > 0.0f ? m4[i] / (32639.0f * 256.0f) : 1.0f;
   }
   // score multiplier of the rows this lane's scores belong to: heads 4 rb + r4
   float sig[NRB];
@@ -731,13 +760,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) mxh = fmaxf(mxh, pmax[ww * 16 + 4 * rb + r4]);
     const float sg = mxh > 0.0f ? mxh / 32639.0f : 1.0f;
-    // step, times 1/16 for int4 codes widened as 16*code
+    // step of the combined dot (256 hi + mid + lo / 256), times 1/16 for int4 codes widened as
+    // 16*code
     sig[rb] = (4 * rb + r4 < GT ? sg : 0.0f) * (KB == 4 ? 0.0625f : 1.0f);
   }
-  // the two int8 digits of every channel, scattered into the score MFMA's A operands: for
-  // (row block rb, step s, digit dg) lane l holds row r = l%16 = (head 4rb + r/4, slot r%4) and
-  // the k bytes of lane group l/16; it is non-zero only when l/16 == r%4, where the 16 bytes are
-  // the digits of group g = (r%4) NS + s
+  // the three int8 digits of every channel (Q = 65536 hi + 256 mid + lo), scattered into the score
+  // MFMA's A operands: for (row block rb, step s, digit dg) lane l holds row r = l%16 = (head
+  // 4rb + r/4, slot r%4) and the k bytes of lane group l/16; it is non-zero only when
+  // l/16 == r%4, where the 16 bytes are the digits of group g = (r%4) NS + s
   {
     int bt_of_c = 0;  // byte of the widened K codes that holds channel n16 of a group
 #pragma unroll
@@ -752,26 +782,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
         const int h = 4 * r4 + i;
         if (h < GT) {
           int Q = static_cast<int>(rintf(qv_[j][i] * (1.0f / sgm[i])));
-          Q = min(max(Q, -32639), 32639);
-          const int hi = (Q + 128) >> 8;
-          const int lo = Q - 256 * hi;
+          Q = min(max(Q, -32639 * 256), 32639 * 256);
+          const int t1 = (Q + 128) >> 8;  // in [-32639, 32639]
+          const int lo = Q - 256 * t1;     // in [-128, 127]
+          const int hi = (t1 + 128) >> 8;  // in [-127, 127]
+          const int mid = t1 - 256 * hi;   // in [-128, 127]
           const int rb = h >> 2, row = (h & 3) * 4 + slot;
-          const int off = ((rb * NS + s) * 2) * 1024 + (row + 16 * slot) * 16 + bt_of_c;
+          const int off = ((rb * NS + s) * 3) * 1024 + (row + 16 * slot) * 16 + bt_of_c;
           dig[off] = uint8_t(hi & 0xff);
-          dig[off + 1024] = uint8_t(lo & 0xff);
+          dig[off + 1024] = uint8_t(mid & 0xff);
+          dig[off + 2048] = uint8_t(lo & 0xff);
         }
       }
     }
   }
   __syncthreads();
-  v4i aop[NRB][NS][2];
+  v4i aop[NRB][NS][3];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int dg = 0; dg < 2; ++dg) {
-        const uint4 v = *reinterpret_cast<const uint4*>(dig + ((rb * NS + s) * 2 + dg) * 1024 + lane * 16);
+      for (int dg = 0; dg < 3; ++dg) {
+        const uint4 v = *reinterpret_cast<const uint4*>(dig + ((rb * NS + s) * 3 + dg) * 1024 + lane * 16);
         aop[rb][s][dg] = v4i{int(v.x), int(v.y), int(v.z), int(v.w)};
       }
   __syncthreads();  // the main loop's tiles overwrite the prologue's LDS
@@ -797,10 +830,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
 #pragma unroll
   for (int g = 0; g < NG; ++g) acc[g] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  while (base < t_end) {
+  for (int k = 0; base < t_end; ++k) {
     if (app && t_app >= base && t_app < base + kSB) patch_superblock<D, KB, VB>(ra, t_app - base, appbuf, lane);
     process_superblock<D, KB, VB, NRB>(ra, base, t_end, lane, aop, sig, m_run, l_run, acc, vtile, stile, ktile, ptile,
-                                   atile, kc, ks, vc, vs, rowbase, base + kStride, L);
+                                   atile, kc, ks, vc, vs, base + kStride, sb_slot(base + kStride, k + 1),
+                                   L - (base + kStride));
     base += kStride;
   }
 
@@ -857,6 +891,10 @@ hipError_t launch_q(const DecodeArgs& a, const DecodePlan& p, const WsLayout& w,
                       a.lambda_bs, a.out,     a.transform};
   P.k_new = static_cast<const uint16_t*>(a.k_new);
   P.v_new = static_cast<const uint16_t*>(a.v_new);
+  P.page_table = a.page_table;
+  P.page_size = a.page_size;
+  P.pages_per_seq = a.pages_per_seq;
+  P.num_pages = a.num_pages;
   const dim3 grid(units * p.n_chunks), block(kThreads);
   const bool app = a.k_new != nullptr;
 #define KVQ_DLAUNCH(NRB)                                                              \

@@ -78,6 +78,10 @@ struct DecodeArgs {
   // position L - 1 of every row before it is attended (the planes above are then written)
   const void* k_new = nullptr;
   const void* v_new = nullptr;
+  // paged cache (nullptr: contiguous rows): page_table [batch, pages_per_seq] device int32;
+  // planes [num_pages, kv_heads, page_size, .]; page_size a multiple of 64
+  const int32_t* page_table = nullptr;
+  int page_size = 0, pages_per_seq = 0, num_pages = 0;
 };
 
 struct DecodeF16Args {
@@ -118,7 +122,7 @@ __host__ __device__ inline WsLayout ws_layout(int units, int head_tile, int head
 
 // Host-side planning (pure host code, no HIP call).
 DecodePlan plan_decode(int batch, int kv_heads, int q_heads, int head_dim, int seq_len, int max_seq_len, bool f16,
-                       bool append = false);
+                       bool append = false, bool paged = false);
 size_t decode_workspace_bytes(int batch, int kv_heads, int q_heads, int head_dim, int max_seq_len);
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);

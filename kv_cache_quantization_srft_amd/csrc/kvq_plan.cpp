@@ -17,7 +17,7 @@ int token_align(bool f16) { return f16 ? 4 * 32 : 4 * 64; }  // 4 waves x superb
 }  // namespace
 
 DecodePlan plan_decode(int batch, int kv_heads, int q_heads, int head_dim, int seq_len, int max_seq_len, bool f16,
-                       bool append) {
+                       bool append, bool paged) {
   DecodePlan p{};
   const int G = q_heads / kv_heads;
   // epilogue LDS holds 4 x tile x d floats; an appending call rotates the new K and V vectors
@@ -37,6 +37,8 @@ DecodePlan plan_decode(int batch, int kv_heads, int q_heads, int head_dim, int s
   auto chunk_for = [&](int len) {
     long per = (std::max(len, 1) + cap_chunks - 1) / cap_chunks;
     per = ((per + align - 1) / align) * align;
+    // a paged call keeps each wave's page list in one register: at most 64 superblocks a wave
+    if (paged) per = std::min<long>(per, 64L * align);
     return int(std::max<long>(align, per));
   };
   p.chunk = chunk_for(seq_len);
@@ -48,9 +50,10 @@ DecodePlan plan_decode(int batch, int kv_heads, int q_heads, int head_dim, int s
 
 size_t decode_workspace_bytes(int batch, int kv_heads, int q_heads, int head_dim, int max_seq_len) {
   size_t need = 0;
-  for (int variant = 0; variant < 3; ++variant) {
-    const DecodePlan p =
-        plan_decode(batch, kv_heads, q_heads, head_dim, max_seq_len, max_seq_len, variant == 1, variant == 2);
+  // variants: quantized, fp16, quantized + append, then both quantized ones on a paged cache
+  for (int variant = 0; variant < 5; ++variant) {
+    const DecodePlan p = plan_decode(batch, kv_heads, q_heads, head_dim, max_seq_len, max_seq_len, variant == 1,
+                                     variant == 2 || variant == 4, variant >= 3);
     const WsLayout w = ws_layout(batch * kv_heads * p.head_tiles, p.head_tile, head_dim, p.max_chunks);
     need = std::max(need, w.total);
   }

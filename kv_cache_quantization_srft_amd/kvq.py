@@ -22,7 +22,7 @@ STATUS_NAMES = {
 EXPORTS = (
     "kvq_version", "kvq_status_string", "kvq_last_error_message", "kvq_codes_bytes", "kvq_scales_bytes",
     "kvq_quantize", "kvq_dequantize", "kvq_calibrate_lambda", "kvq_decode_attn_workspace_bytes",
-    "kvq_decode_attn", "kvq_decode_attn_append", "kvq_decode_attn_fp16",
+    "kvq_decode_attn", "kvq_decode_attn_append", "kvq_decode_attn_paged", "kvq_decode_attn_fp16",
 )
 
 
@@ -85,6 +85,9 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_attn_append.restype = ctypes.c_int
         L.kvq_decode_attn_append.argtypes = [_LP, _P, _P, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _I64, _P, _P,
                                              _I64, ctypes.c_float, _P, _SZ, _P, _P]
+        L.kvq_decode_attn_paged.restype = ctypes.c_int
+        L.kvq_decode_attn_paged.argtypes = [_LP, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P,
+                                            _P, _I64, _P, _P, _I64, ctypes.c_float, _P, _SZ, _P, _P]
         L.kvq_decode_attn_fp16.restype = ctypes.c_int
         L.kvq_decode_attn_fp16.argtypes = [_LP, _P, _P, _P, _I32, _P, ctypes.c_float, _P, _SZ, _P, _P]
         _lib = L
@@ -220,6 +223,35 @@ def kvq_decode_attn_append(layout, q, k_new, v_new, k_codes, k_scales, v_codes, 
         _ptr(v_codes, _u8(), "v_codes", min_bytes=kvq_codes_bytes(layout, layout.v_bits)),
         _ptr(v_scales, _scale_t(), "v_scales", min_bytes=kvq_scales_bytes(layout)), seq_len,
         _ptr(seq_lens, torch.int32, "seq_lens", layout.batch), _ptr(sign_k, _f32(), "sign_k"),
+        _ptr(sign_v, _f32(), "sign_v"), sign_batch_stride, _ptr(lambda_k, _f32(), "lambda_k"),
+        _ptr(lambda_v, _f32(), "lambda_v"), lambda_batch_stride, float(sm_scale),
+        _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(out, _f32(), "out", layout.batch * layout.q_heads * d), _stream(stream)))
+
+
+def _page_plane_bytes(layout, bits, num_pages, page_size, scales=False):
+    """Bytes of one paged plane [num_pages, kv_heads, page_size, .] (codes, or scales)."""
+    per_tok = layout.head_dim // layout.group_size * 2 if scales else layout.head_dim * bits // 8
+    return num_pages * layout.kv_heads * page_size * per_tok
+
+
+def kvq_decode_attn_paged(layout, q, k_new, v_new, k_codes, k_scales, v_codes, v_scales, page_table, pages_per_seq,
+                          page_size, num_pages, seq_len, seq_lens, sign_k, sign_v, sign_batch_stride, lambda_k,
+                          lambda_v, lambda_batch_stride, sm_scale, workspace, out, stream=None):
+    import torch
+    d = layout.head_dim
+    n_new = layout.batch * layout.kv_heads * d
+    _check(lib().kvq_decode_attn_paged(
+        ctypes.byref(layout), _ptr(q, _f16(), "q", layout.batch * layout.q_heads * d),
+        _ptr(k_new, _f16(), "k_new", n_new), _ptr(v_new, _f16(), "v_new", n_new),
+        _ptr(k_codes, _u8(), "k_codes", min_bytes=_page_plane_bytes(layout, layout.k_bits, num_pages, page_size)),
+        _ptr(k_scales, _scale_t(), "k_scales",
+             min_bytes=_page_plane_bytes(layout, 0, num_pages, page_size, scales=True)),
+        _ptr(v_codes, _u8(), "v_codes", min_bytes=_page_plane_bytes(layout, layout.v_bits, num_pages, page_size)),
+        _ptr(v_scales, _scale_t(), "v_scales",
+             min_bytes=_page_plane_bytes(layout, 0, num_pages, page_size, scales=True)),
+        _ptr(page_table, torch.int32, "page_table", layout.batch * pages_per_seq), pages_per_seq, page_size,
+        num_pages, seq_len, _ptr(seq_lens, torch.int32, "seq_lens", layout.batch), _ptr(sign_k, _f32(), "sign_k"),
         _ptr(sign_v, _f32(), "sign_v"), sign_batch_stride, _ptr(lambda_k, _f32(), "lambda_k"),
         _ptr(lambda_v, _f32(), "lambda_v"), lambda_batch_stride, float(sm_scale),
         _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),

@@ -239,3 +239,38 @@ def test_append_head_tile_limit(L):
     lay = layout(batch=8193, kv_heads=1, q_heads=16)
     assert decode(L, lay, ws_bytes=16) == 4 and "workspace has 16 bytes" in msg(L)
     assert append(L, lay, ws_bytes=16) == 2 and "exceeds 16384" in msg(L)
+
+
+def paged(L, lay, q=GOOD, kn=NULL, vn=NULL, table=GOOD, pps=4, psz=16, npages=9, seq_len=16, ws_bytes=1 << 30):
+    return L.kvq_decode_attn_paged(ctypes.byref(lay), q, kn, vn, GOOD, GOOD, GOOD, GOOD, table, pps, psz, npages,
+                                   seq_len, NULL, GOOD, GOOD, 0, NULL, NULL, 0, ctypes.c_float(0), GOOD, ws_bytes,
+                                   GOOD, NULL)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(psz=16), 2, "page_size"),
+    (dict(psz=96, pps=2, lay=dict(capacity=192)), 2, "page_size"),
+    (dict(psz=64, pps=0), 1, "pages_per_seq"),
+    (dict(psz=64, pps=1, npages=0), 1, "num_pages"),
+    (dict(psz=64, pps=2), 1, "capacity"),
+    (dict(psz=64, pps=1, table=NULL), 1, "page_table"),
+    (dict(psz=64, pps=1, table=P((1 << 20) + 2)), 3, "page_table"),
+    (dict(psz=64, pps=1, kn=GOOD), 1, "v_new"),
+    (dict(psz=64, pps=1, seq_len=65), 1, "seq_len"),
+    (dict(psz=64, pps=1, lay=dict(group_size=128)), 2, "group_size"),
+])
+def test_paged_decode_validation(L, kw, status, needle):
+    """capacity = 64 unless set: one 64-token page per sequence is the valid base case."""
+    lay = layout(**kw.pop("lay", {}))
+    assert paged(L, lay, **kw) == status
+    assert needle in msg(L)
+
+
+def test_paged_workspace_covers_long_chunks(L):
+    """A paged call caps a work-group's chunk at 64 superblocks per wave (16384 tokens), so with
+    many units and long sequences it needs more chunk partials than a contiguous call; the
+    workspace query covers both."""
+    lay = layout(batch=512, kv_heads=1, q_heads=1, capacity=65536)
+    need = kvq.kvq_decode_attn_workspace_bytes(lay, 65536)
+    assert need > 0
+    assert paged(L, lay, pps=1024, psz=64, npages=512 * 1024, seq_len=65536, ws_bytes=need - 1) == 4

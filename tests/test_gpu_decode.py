@@ -177,3 +177,21 @@ def test_shared_workspace_across_shapes():
             got16 = gpu_decode_fp16(q, k, v, S, ws=ws)
             assert np.abs(got16 - O.decode_attention(q, k, v, S)).max() <= ATTN_ATOL, f"fp16 call {i}"
             assert int(ws[:65536].count_nonzero()) == 0, f"counters not reset after fp16 call {i}"
+
+
+@pytest.mark.parametrize("seed", [1634, 7, 2024])
+def test_keys_beyond_a_wide_calibrated_lambda(seed):
+    """Student-t (nu = 3) keys with x20 outlier channels and lambda_K calibrated on the first 256
+    tokens: lambda_K spans more than a decade and later keys exceed it, so the rotated query has
+    a wide dynamic range across channels.  The query digits must keep the score error small
+    relative to the largest channel (a 16-bit query gave 2.9e-3 here, over the 2e-3 bar)."""
+    rng = np.random.default_rng(seed)
+    B, Hkv, G, S, d = 4, 2, 6, 1500, 128
+    k = synth.to_fp16(rng.standard_t(3, size=(B, Hkv, S, d)) * np.where(rng.random((B, Hkv, 1, d)) < 0.03, 20, 1))
+    v = synth.to_fp16(rng.standard_normal((B, Hkv, S, d)))
+    q = synth.to_fp16(rng.standard_normal((B, Hkv * G, d)))
+    sk = synth.random_signs(seed * 5 + 1, d)
+    sv = synth.random_signs(seed * 5 + 2, d)
+    lk = O.calibrate_lambda(k, sk, 256).astype(np.float32)
+    lv = O.calibrate_lambda(v, sv, 256).astype(np.float32)
+    _check(q, k, v, sk, sv, lk, lv, 4, S, [1500, 700, 257, 1], label=f"wide lambda seed {seed}")

@@ -1,0 +1,151 @@
+"""GPU parity of kvq_decode_attn_paged (decode attention, and the fused append, over a paged
+quantized cache) through the C ABI.
+
+A paged cache only moves where each token's bytes live, so the bars are:
+- the output equals kvq_decode_attn / kvq_decode_attn_append on the same tokens stored
+  contiguously, bit for bit (same plan, same arithmetic);
+- the output matches the oracle's attention over the same packed planes within 2e-3 max-abs;
+- an appending call writes the new token into its page slot exactly as the contiguous append
+  writes it into its row, and no other page byte changes (unused pages hold garbage that is
+  never read).
+"""
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_quantization_srft_amd import kvq, synth
+from oracle import kvq_oracle as O
+
+from gpu_parity import ATTN_ATOL, dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(seed, B, Hkv, G, S, d, lam):
+    rng = np.random.default_rng(seed)
+    k = synth.to_fp16(rng.standard_t(3, size=(B, Hkv, S, d)) * np.where(rng.random((B, Hkv, 1, d)) < 0.03, 20, 1))
+    v = synth.to_fp16(rng.standard_normal((B, Hkv, S, d)))
+    q = synth.to_fp16(rng.standard_normal((B, Hkv * G, d)))
+    sk = synth.random_signs(seed * 5 + 1, d)
+    sv = synth.random_signs(seed * 5 + 2, d)
+    lk = O.calibrate_lambda(k, sk, min(S, 256)).astype(np.float32) if lam else None
+    lv = O.calibrate_lambda(v, sv, min(S, 256)).astype(np.float32) if lam else None
+    return k, v, q, sk, sv, lk, lv
+
+
+def _paginate(plane, P, table, num_pages, fill):
+    """Contiguous plane [B, H, cap, w] -> paged plane [num_pages, H, P, w] by the page table."""
+    B, H, cap, wdt = plane.shape
+    out = np.full((num_pages, H, P, wdt), fill, dtype=plane.dtype)
+    for b in range(B):
+        for j in range(cap // P):
+            out[table[b, j]] = plane[b, :, j * P:(j + 1) * P]
+    return out
+
+
+def _setup(seed, B, Hkv, G, S, d, kb, P, lam, extra_pages=3):
+    k, v, q, sk, sv, lk, lv = _inputs(seed, B, Hkv, G, S, d, lam)
+    cap = -(-S // P) * P
+    l4 = lambda x: 1.0 if x is None else x[:, :, None, :]
+    kc, ks = O.quantize(k, sk, l4(lk), kb)
+    vc, vs = O.quantize(v, sv, l4(lv), 4)
+    pad = lambda a, fill: np.concatenate([a, np.full(a.shape[:2] + (cap - S,) + a.shape[3:], fill, a.dtype)], 2)
+    cont = (pad(O.pack_codes(kc, kb), 0xAB), pad(ks, np.float16(np.nan)), pad(O.pack_codes(vc, 4), 0xAB),
+            pad(vs, np.float16(np.nan)))
+    pps = cap // P
+    num_pages = B * pps + extra_pages
+    rng = np.random.default_rng(seed + 99)
+    table = rng.permutation(num_pages)[:B * pps].reshape(B, pps).astype(np.int32)
+    paged = tuple(_paginate(a, P, table, num_pages, f) for a, f in
+                  zip(cont, (0xAB, np.float16(np.nan), 0xAB, np.float16(np.nan))))
+    return dict(k=k, v=v, q=q, sk=sk, sv=sv, lk=lk, lv=lv, kc=kc, ks=ks, vc=vc, vs=vs, cont=cont, paged=paged,
+                table=table, pps=pps, num_pages=num_pages, cap=cap)
+
+
+def _dev_planes(pl):
+    return [dev(pl[0]), dev(pl[1].view(np.int16)), dev(pl[2]), dev(pl[3].view(np.int16))]
+
+
+def _call(c, lay, P, seq_len, lens, paged, k_new=None, v_new=None):
+    B, Hkv, d = lay.batch, lay.kv_heads, lay.head_dim
+    planes = _dev_planes(c["paged"] if paged else c["cont"])
+    ws = torch.zeros(kvq.kvq_decode_attn_workspace_bytes(lay, seq_len), dtype=torch.uint8, device="cuda")
+    out = torch.full((B, lay.q_heads, d), float("nan"), dtype=torch.float32, device="cuda")
+    sl = None if lens is None else dev(np.asarray(lens, np.int32))
+    lk = None if c["lk"] is None else dev(c["lk"])
+    lv = None if c["lv"] is None else dev(c["lv"])
+    lbs = 0 if c["lk"] is None else Hkv * d
+    kn = None if k_new is None else dev(k_new)
+    vn = None if v_new is None else dev(v_new)
+    if paged:
+        kvq.kvq_decode_attn_paged(lay, dev(c["q"]), kn, vn, *planes, dev(c["table"]), c["pps"], P, c["num_pages"],
+                                  seq_len, sl, dev(c["sk"]), dev(c["sv"]), 0, lk, lv, lbs, 0.0, ws, out)
+    elif kn is None:
+        kvq.kvq_decode_attn(lay, dev(c["q"]), *planes, seq_len, sl, dev(c["sk"]), dev(c["sv"]), 0, lk, lv, lbs, 0.0,
+                            ws, out)
+    else:
+        kvq.kvq_decode_attn_append(lay, dev(c["q"]), kn, vn, *planes, seq_len, sl, dev(c["sk"]), dev(c["sv"]), 0, lk,
+                                   lv, lbs, 0.0, ws, out)
+    torch.cuda.synchronize()
+    got = (planes[0].cpu().numpy(), planes[1].cpu().numpy().view(np.float16), planes[2].cpu().numpy(),
+           planes[3].cpu().numpy().view(np.float16))
+    return out.cpu().numpy().astype(np.float64), got
+
+
+CASES = [
+    # d, G, k_bits, S, lens, lambda, page_size
+    (128, 6, 4, 1500, [1500, 700, 257, 1], True, 64),
+    (128, 1, 4, 256, None, False, 256),
+    (256, 4, 8, 900, [900, 1, 513], False, 128),
+    (128, 16, 4, 5000, [5000, 0], True, 512),
+    (128, 4, 4, 3000, [3000, 2999, 64, 65], False, 192),
+]
+
+
+@pytest.mark.parametrize("d,G,kb,S,lens,lam,P", CASES)
+def test_paged_decode_matches_contiguous_and_oracle(d, G, kb, S, lens, lam, P):
+    B = 1 if lens is None else len(lens)
+    Hkv = 2
+    c = _setup(d + G + S, B, Hkv, G, S, d, kb, P, lam)
+    lay = kvq.make_layout(B, Hkv, Hkv * G, d, c["cap"], k_bits=kb)
+    say("paged decode", (B, Hkv, G, S, d), kb, "page", P)
+    got_p, _ = _call(c, lay, P, S, lens, True)
+    got_c, _ = _call(c, lay, P, S, lens, False)
+    assert np.isfinite(got_p).all()
+    assert np.array_equal(got_p, got_c), np.abs(got_p - got_c).max()
+    L = np.full(B, S) if lens is None else np.clip(np.asarray(lens), 0, S)
+    ref = np.zeros_like(got_p)
+    live = L > 0
+    l4 = lambda x: 1.0 if x is None else x[live][:, :, None, :]
+    ref[live] = O.decode_attention_quantized(c["q"][live], c["kc"][live], c["ks"][live], c["vc"][live],
+                                             c["vs"][live], c["sk"], c["sv"], l4(c["lk"]), l4(c["lv"]), L[live])
+    err = np.abs(got_p - ref).max()
+    assert err <= ATTN_ATOL, err
+
+
+@pytest.mark.parametrize("d,G,kb,S,lens,lam,P", [CASES[0], CASES[2], CASES[4]])
+def test_paged_append_matches_contiguous_append(d, G, kb, S, lens, lam, P):
+    B = len(lens)
+    Hkv = 2
+    c = _setup(3 * d + G + S, B, Hkv, G, S, d, kb, P, lam)
+    lay = kvq.make_layout(B, Hkv, Hkv * G, d, c["cap"], k_bits=kb)
+    rng = np.random.default_rng(S)
+    k_new = synth.to_fp16(rng.standard_normal((B, Hkv, d)) * 3)
+    v_new = synth.to_fp16(rng.standard_normal((B, Hkv, d)))
+    say("paged append", (B, Hkv, G, S, d), kb, "page", P)
+    got_p, planes_p = _call(c, lay, P, S, lens, True, k_new, v_new)
+    got_c, planes_c = _call(c, lay, P, S, lens, False, k_new, v_new)
+    assert np.array_equal(got_p, got_c), np.abs(got_p - got_c).max()
+    # every page byte equals the contiguous planes after the append, mapped through the table;
+    # pages outside the table keep their garbage
+    for a_p, a_c, orig in zip(planes_p, planes_c, c["paged"]):
+        want = orig.copy()
+        cont = a_c.reshape(B, Hkv, c["cap"], -1)
+        for b in range(B):
+            for j in range(c["pps"]):
+                want[c["table"][b, j]] = cont[b, :, j * P:(j + 1) * P]
+        got = a_p.reshape(want.shape)
+        if want.dtype == np.float16:
+            assert np.array_equal(got.view(np.int16), want.view(np.int16))
+        else:
+            assert np.array_equal(got, want)
