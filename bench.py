@@ -330,6 +330,46 @@ def main():
     nb = max(R, Rf)
     res_bq = timer.run(lambda i: quantize_all(planes[i % R], *kv16[i % Rf]), nb, 2 * nb, args.warmup)
 
+    # paged cache: every copy cut into pages of PAGE tokens, stored in a shuffled page order and
+    # addressed through a page table (kvq_decode_attn_paged); same tokens, same bytes read
+    page = 256 if S % 256 == 0 else 64
+    pps = -(-S // page)
+    paged_planes, tables = [], []
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(7)
+    for i in range(R):
+        perm = torch.randperm(LB * pps, generator=gen).to("cuda")
+        tbl = perm.view(LB, pps).to(torch.int32).contiguous()
+        pp = []
+        for t in planes[i]:
+            w_ = t.numel() // (LB * H * S)
+            nat = t.view(LB, H, S, w_)
+            if pps * page != S:
+                nat = torch.cat([nat, nat.new_zeros(LB, H, pps * page - S, w_)], 2)
+            nat = nat.view(LB, H, pps, page, w_).permute(0, 2, 1, 3, 4).reshape(LB * pps, H, page, w_)
+            out_p = torch.empty_like(nat)
+            out_p[perm] = nat
+            pp.append(out_p.view(-1))
+        paged_planes.append(pp)
+        tables.append(tbl)
+    lay_pg = kvq.make_layout(LB, H, Hq, d, pps * page, k_bits=w.k_bits, v_bits=w.v_bits, transform=args.transform)
+    ws_pg = torch.zeros(kvq.kvq_decode_attn_workspace_bytes(lay_pg, S), dtype=torch.uint8, device="cuda")
+    out_pg = torch.empty_like(out)
+
+    def decode_paged(i):
+        p = paged_planes[i]
+        kvq.kvq_decode_attn_paged(lay_pg, q, None, None, p[0], p[1], p[2], p[3], tables[i], pps, page, LB * pps, S,
+                                  None, s, s, 0, lam_k, lam_v, lbs, 0.0, ws_pg, out_pg)
+
+    res_pg = timer.run(decode_paged, R, steps, args.warmup)
+    decode_paged(0)
+    decode(planes[0])
+    torch.cuda.synchronize()
+    # identical plans give identical bits; a paged chunk is capped at 16384 tokens, so longer
+    # single-chunk rows split into more chunks and differ only by the merge's rounding
+    paged_diff = float((out_pg - out).abs().max())
+    del paged_planes
+
     # one scale per vector (group = d), the per-token comparison mode of the write path: bulk
     # quantize of K and V, all layers, and the round-trip error of both modes on layer 0's K
     lay_pt = kvq.make_layout(LB, H, Hq, d, S, k_bits=w.k_bits, v_bits=w.v_bits, transform=args.transform,
@@ -405,6 +445,10 @@ def main():
                           "GBps_moved": round(bq_bytes / (res_bq["ms_mean"] * 1e-3) / 1e9, 2),
                           "frac_hbm_peak": round(bq_bytes / (res_bq["ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                           "vectors": n_vec, "ms": round(res_bq["ms_mean"], 5)},
+        "decode_paged": {
+            "GBps": round(dec_bytes / (res_pg["ms_mean"] * 1e-3) / 1e9, 2), "ms": round(res_pg["ms_mean"], 5),
+            "page_tokens": page, "pages": LB * pps, "max_abs_diff_vs_contiguous": paged_diff,
+            "note": "kvq_decode_attn_paged over the same cache cut into pages stored in a shuffled order"},
         "quantize_per_token_scale": {
             "Mvectors_per_s": round(n_vec / (res_pt["ms_mean"] * 1e-3) / 1e6, 2), "ms": round(res_pt["ms_mean"], 5),
             "k_relative_error": {k: round(v, 5) for k, v in round_trip.items()},
