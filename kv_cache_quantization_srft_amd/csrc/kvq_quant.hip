@@ -297,10 +297,11 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
     constexpr int f = decltype(F)::value;
     constexpr int buf = f & 1;
     // ---- transform: lane (vector n16, channels 16 cb + 4 r4 + i) ----
-    // four independent accumulation chains (hi and lo operands of both blocks)
-    v4f acc[2], accl[2];
+    // two accumulation chains (one per channel block), the hi and lo operands accumulating into
+    // the same fp32 sum
+    v4f acc[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) acc[i] = accl[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < 2; ++i) acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
       const uint4 bx = xt[f][n16][(4 * s + r4) ^ n16];
@@ -308,10 +309,8 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
 #pragma unroll
       for (int i = 0; i < 2; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[i][s], bop, acc[i], 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) accl[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[i][s], bop, accl[i], 0, 0, 0);
+      for (int i = 0; i < 2; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[i][s], bop, acc[i], 0, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) acc[i] += accl[i];
     // ---- per-channel factor 1/(16 lambda) (recomputed when this lane's row changes), the group
     //      absmax, scale, codes ----
     if constexpr (HAS_LAMBDA) {
@@ -332,14 +331,16 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
         }
       }
     }
+    // u = acc / (16 lambda).  Without lambda the factor is the exact 1/16, applied to the group
+    // maximum and to the group's reciprocal instead of to every value (bit-identical codes)
     float u[2][4], a[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) u[i][j] = acc[i][j] * linv[i][j];
+      for (int j = 0; j < 4; ++j) u[i][j] = HAS_LAMBDA ? acc[i][j] * linv[i][j] : acc[i][j];
       const uint32_t am = max(max(__float_as_uint(fabsf(u[i][0])), __float_as_uint(fabsf(u[i][1]))),
                               max(__float_as_uint(fabsf(u[i][2])), __float_as_uint(fabsf(u[i][3]))));
-      a[i] = __uint_as_float(rows_max4(am));
+      a[i] = __uint_as_float(rows_max4(am)) * (HAS_LAMBDA ? 1.0f : 0.0625f);
     }
     if constexpr (PT) {
       // one scale per vector: the absmax over all channels, i.e. over this wave's two groups and
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
       const int g = 2 * w + i;
       const _Float16 sh = static_cast<_Float16>(scale_of<BITS>(a[i]));
       const float sf = static_cast<float>(sh);
-      const float inv = sf > 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f;
+      const float inv = (sf > 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f) * (HAS_LAMBDA ? 1.0f : 0.0625f);
       uint32_t tq[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -378,24 +379,31 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
     __syncthreads();
     // ---- store codes (16 B per thread) and scales ----
     {
+      // the block's first slot (work-group uniform); a block inside one row needs no division
+      const uint32_t gv0 = blk * kVecs;
+      const uint32_t row0 = fd_tok.div(gv0);
+      const uint32_t t0 = gv0 - row0 * fd_tok.d;
+      const bool one_row = t0 + kVecs <= fd_tok.d;
+      const int64_t slot0 = int64_t(row0) * capacity + pos + t0;
+      auto vslot = [&](uint32_t gvs, int v) { return one_row ? slot0 + v : slot_of(gvs); };
       constexpr int UNITS = kVecs * CB / 16;  // 16-byte code units
       constexpr int SUNITS = kVecs * NG / 8;  // 16-byte scale units
       if (tid < UNITS) {
         const int v = tid / (CB / 16), pc = tid - v * (CB / 16);
         const uint32_t gvs = blk * kVecs + v;
         if (gvs < n_vec)
-          *reinterpret_cast<uint4*>(codes + slot_of(gvs) * CB + pc * 16) =
+          *reinterpret_cast<uint4*>(codes + vslot(gvs, v) * CB + pc * 16) =
               *reinterpret_cast<const uint4*>(&ct[buf][v][pc * 16]);
       } else if (PT && tid >= UNITS && tid < UNITS + kVecs) {
         const int v = tid - UNITS;  // one fp16 scale per vector
         const uint32_t gvs = blk * kVecs + v;
-        if (gvs < n_vec) scales[slot_of(gvs)] = st[buf][v][0];
+        if (gvs < n_vec) scales[vslot(gvs, v)] = st[buf][v][0];
       } else if (!PT && tid >= UNITS && tid < UNITS + SUNITS) {
         const int u = tid - UNITS;
         const int v = u / (NG / 8), pc = u - v * (NG / 8);
         const uint32_t gvs = blk * kVecs + v;
         if (gvs < n_vec)
-          *reinterpret_cast<uint4*>(scales + slot_of(gvs) * NG + pc * 8) =
+          *reinterpret_cast<uint4*>(scales + vslot(gvs, v) * NG + pc * 8) =
               *reinterpret_cast<const uint4*>(&st[buf][v][pc * 8]);
       }
     }
