@@ -7,6 +7,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 import threading
 
 import pytest
@@ -274,3 +275,13 @@ def test_paged_workspace_covers_long_chunks(L):
     need = kvq.kvq_decode_attn_workspace_bytes(lay, 65536)
     assert need > 0
     assert paged(L, lay, pps=1024, psz=64, npages=512 * 1024, seq_len=65536, ws_bytes=need - 1) == 4
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU; --gpus N > 1 prints a one-line JSON error and exits 2 before
+    touching a device."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    line = r.stdout.strip().splitlines()[-1]
+    assert "one GPU" in line and line.startswith("{")
