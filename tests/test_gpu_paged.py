@@ -21,15 +21,15 @@ from gpu_parity import ATTN_ATOL, dev, say
 pytestmark = pytest.mark.gpu
 
 
-def _inputs(seed, B, Hkv, G, S, d, lam):
+def _inputs(seed, B, Hkv, G, S, d, lam, transform="srft"):
     rng = np.random.default_rng(seed)
     k = synth.to_fp16(rng.standard_t(3, size=(B, Hkv, S, d)) * np.where(rng.random((B, Hkv, 1, d)) < 0.03, 20, 1))
     v = synth.to_fp16(rng.standard_normal((B, Hkv, S, d)))
     q = synth.to_fp16(rng.standard_normal((B, Hkv * G, d)))
     sk = synth.random_signs(seed * 5 + 1, d)
     sv = synth.random_signs(seed * 5 + 2, d)
-    lk = O.calibrate_lambda(k, sk, min(S, 256)).astype(np.float32) if lam else None
-    lv = O.calibrate_lambda(v, sv, min(S, 256)).astype(np.float32) if lam else None
+    lk = O.calibrate_lambda(k, sk, min(S, 256), transform).astype(np.float32) if lam else None
+    lv = O.calibrate_lambda(v, sv, min(S, 256), transform).astype(np.float32) if lam else None
     return k, v, q, sk, sv, lk, lv
 
 
@@ -43,14 +43,14 @@ def _paginate(plane, P, table, num_pages, fill):
     return out
 
 
-def _setup(seed, B, Hkv, G, S, d, kb, P, lam, extra_pages=3):
-    k, v, q, sk, sv, lk, lv = _inputs(seed, B, Hkv, G, S, d, lam)
+def _setup(seed, B, Hkv, G, S, d, kb, P, lam, extra_pages=3, vb=4, transform="srft"):
+    k, v, q, sk, sv, lk, lv = _inputs(seed, B, Hkv, G, S, d, lam, transform)
     cap = -(-S // P) * P
     l4 = lambda x: 1.0 if x is None else x[:, :, None, :]
-    kc, ks = O.quantize(k, sk, l4(lk), kb)
-    vc, vs = O.quantize(v, sv, l4(lv), 4)
+    kc, ks = O.quantize(k, sk, l4(lk), kb, transform=transform)
+    vc, vs = O.quantize(v, sv, l4(lv), vb, transform=transform)
     pad = lambda a, fill: np.concatenate([a, np.full(a.shape[:2] + (cap - S,) + a.shape[3:], fill, a.dtype)], 2)
-    cont = (pad(O.pack_codes(kc, kb), 0xAB), pad(ks, np.float16(np.nan)), pad(O.pack_codes(vc, 4), 0xAB),
+    cont = (pad(O.pack_codes(kc, kb), 0xAB), pad(ks, np.float16(np.nan)), pad(O.pack_codes(vc, vb), 0xAB),
             pad(vs, np.float16(np.nan)))
     pps = cap // P
     num_pages = B * pps + extra_pages
@@ -59,7 +59,7 @@ def _setup(seed, B, Hkv, G, S, d, kb, P, lam, extra_pages=3):
     paged = tuple(_paginate(a, P, table, num_pages, f) for a, f in
                   zip(cont, (0xAB, np.float16(np.nan), 0xAB, np.float16(np.nan))))
     return dict(k=k, v=v, q=q, sk=sk, sv=sv, lk=lk, lv=lv, kc=kc, ks=ks, vc=vc, vs=vs, cont=cont, paged=paged,
-                table=table, pps=pps, num_pages=num_pages, cap=cap)
+                table=table, pps=pps, num_pages=num_pages, cap=cap, transform=transform)
 
 
 def _dev_planes(pl):
@@ -149,3 +149,22 @@ def test_paged_append_matches_contiguous_append(d, G, kb, S, lens, lam, P):
             assert np.array_equal(got.view(np.int16), want.view(np.int16))
         else:
             assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("d,kb,vb,transform", [(128, 4, 8, "srft"), (128, 4, 4, "srht"), (256, 8, 4, "srht"),
+                                               (256, 8, 8, "srft")])
+def test_paged_decode_bit_pairings_and_srht(d, kb, vb, transform):
+    B, Hkv, G, S, P = 3, 2, 4, 777, 128
+    lens = [777, 300, 129]
+    c = _setup(d + kb + vb, B, Hkv, G, S, d, kb, P, True, vb=vb, transform=transform)
+    lay = kvq.make_layout(B, Hkv, Hkv * G, d, c["cap"], k_bits=kb, v_bits=vb, transform=transform)
+    say("paged decode", (B, Hkv, G, S, d), f"K{kb}V{vb}", transform, "page", P)
+    got_p, _ = _call(c, lay, P, S, lens, True)
+    got_c, _ = _call(c, lay, P, S, lens, False)
+    assert np.array_equal(got_p, got_c), np.abs(got_p - got_c).max()
+    L = np.asarray(lens)
+    l4 = lambda x: x[:, :, None, :]
+    ref = O.decode_attention_quantized(c["q"], c["kc"], c["ks"], c["vc"], c["vs"], c["sk"], c["sv"], l4(c["lk"]),
+                                       l4(c["lv"]), L, transform=transform)
+    err = np.abs(got_p - ref).max()
+    assert err <= ATTN_ATOL, err
