@@ -208,10 +208,13 @@ kvq_status kvq_decode_attn_append(const kvq_layout* layout, const void* q_f16, c
  * kvq_decode_attn_append) over a paged cache: the planes hold num_pages pages of page_size
  * tokens, codes uint8 [num_pages, kv_heads, page_size, d*bits/8] and scales fp16
  * [num_pages, kv_heads, page_size, d/16], and token t of sequence b lives in page
- * page_table[b * pages_per_seq + t / page_size] at offset t % page_size.  Serving caches grow
- * by pages instead of reserving `capacity` tokens per sequence (the pages' paged / sliding
- * window serving setting).  The computation, its precision and its result are those of
- * kvq_decode_attn on the same tokens.
+ * page_table[b * pages_per_seq + t / page_size] at offset t % page_size.  This answers the
+ * cache-management concerns of [GM] ("KV 缓存分片与内存管理": a full num_ctx reservation per
+ * sequence, prefix reuse across requests, sliding-window eviction): a cache grows by pages,
+ * sequences may point at the same pages for a shared prefix, and a window is a table whose
+ * leading entries the caller retires.  The computation, its precision and its result are those
+ * of kvq_decode_attn on the same tokens.  An appending call writes only the page holding
+ * position L - 1 of each sequence, which must not be shared with another sequence of the call.
  *   page_table    : device int32 [batch, pages_per_seq]; entries are clamped to [0, num_pages)
  *                   on the device (an out-of-range entry reads a wrong page, never out of the
  *                   planes); entries of pages past a sequence's length are not read
