@@ -168,3 +168,35 @@ def test_paged_decode_bit_pairings_and_srht(d, kb, vb, transform):
                                        l4(c["lv"]), L, transform=transform)
     err = np.abs(got_p - ref).max()
     assert err <= ATTN_ATOL, err
+
+
+def test_paged_decode_shared_prefix_pages():
+    """Two sequences whose tables point at the same physical pages for a common prefix (prefix
+    reuse) read the same bytes: the output equals the contiguous decode over a cache in which
+    the second sequence holds a copy of that prefix, and the oracle's attention."""
+    d, G, kb, S, P, B, Hkv = 128, 4, 4, 640, 128, 2, 2
+    lens = [640, 600]
+    c = _setup(4242, B, Hkv, G, S, d, kb, P, True)
+    n_shared = 3  # pages of the common prefix
+    # the contiguous cache: sequence 1's first n_shared pages become a copy of sequence 0's
+    cont = [a.copy() for a in c["cont"]]
+    for a in cont:
+        a[1, :, :n_shared * P] = a[0, :, :n_shared * P]
+    for key in ("kc", "ks", "vc", "vs"):
+        c[key] = c[key].copy()
+        c[key][1, :, :n_shared * P] = c[key][0, :, :n_shared * P]
+    c["cont"] = tuple(cont)
+    table = c["table"].copy()
+    table[1, :n_shared] = table[0, :n_shared]  # sequence 1's prefix pages are sequence 0's
+    c["table"] = table
+    c["paged"] = tuple(_paginate(a, P, table, c["num_pages"], f) for a, f in
+                       zip(cont, (0xAB, np.float16(np.nan), 0xAB, np.float16(np.nan))))
+    lay = kvq.make_layout(B, Hkv, Hkv * G, d, c["cap"], k_bits=kb)
+    say("paged decode, shared prefix pages", n_shared)
+    got_p, _ = _call(c, lay, P, S, lens, True)
+    got_c, _ = _call(c, lay, P, S, lens, False)
+    assert np.array_equal(got_p, got_c), np.abs(got_p - got_c).max()
+    l4 = lambda x: x[:, :, None, :]
+    ref = O.decode_attention_quantized(c["q"], c["kc"], c["ks"], c["vc"], c["vs"], c["sk"], c["sv"], l4(c["lk"]),
+                                       l4(c["lv"]), np.asarray(lens))
+    assert np.abs(got_p - ref).max() <= ATTN_ATOL
