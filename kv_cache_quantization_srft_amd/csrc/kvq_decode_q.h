@@ -25,6 +25,8 @@
 //   epilogue: the work-group merges its waves and stores a chunk partial; the last work-group
 //             of the unit to finish merges the chunks, applies lambda_V and the inverse rotation
 //             and writes the output.  A unit covered by a single chunk skips the workspace.
+#pragma once
+
 #include <algorithm>
 
 #include "kvq_decode_common.h"
@@ -924,23 +926,15 @@ hipError_t launch_q(const DecodeArgs& a, const DecodePlan& p, const WsLayout& w,
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
+// The instances of one head dimension (each is built in a translation unit of its own).
+template <int D>
+hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
   const WsLayout w = ws_layout(a.batch * a.kv_heads * p.head_tiles, p.head_tile, a.head_dim, p.max_chunks);
-  const int kv = a.k_bits * 10 + a.v_bits;
-  if (a.head_dim == 128) {
-    switch (kv) {
-      case 44: return launch_q<128, 4, 4>(a, p, w, s);
-      case 84: return launch_q<128, 8, 4>(a, p, w, s);
-      case 48: return launch_q<128, 4, 8>(a, p, w, s);
-      case 88: return launch_q<128, 8, 8>(a, p, w, s);
-    }
-  } else {
-    switch (kv) {
-      case 44: return launch_q<256, 4, 4>(a, p, w, s);
-      case 84: return launch_q<256, 8, 4>(a, p, w, s);
-      case 48: return launch_q<256, 4, 8>(a, p, w, s);
-      case 88: return launch_q<256, 8, 8>(a, p, w, s);
-    }
+  switch (a.k_bits * 10 + a.v_bits) {
+    case 44: return launch_q<D, 4, 4>(a, p, w, s);
+    case 84: return launch_q<D, 8, 4>(a, p, w, s);
+    case 48: return launch_q<D, 4, 8>(a, p, w, s);
+    case 88: return launch_q<D, 8, 8>(a, p, w, s);
   }
   return hipErrorInvalidValue;
 }

@@ -129,6 +129,9 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_calibrate(const CalibArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream);
+// instances of one head dimension (128, 256), each built in its own translation unit
+template <int D>
+hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream);
 hipError_t launch_decode_f16(const DecodeF16Args& a, const DecodePlan& p, hipStream_t stream);
 
 }  // namespace kvq_impl

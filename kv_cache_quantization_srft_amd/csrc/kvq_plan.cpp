@@ -60,4 +60,10 @@ size_t decode_workspace_bytes(int batch, int kv_heads, int q_heads, int head_dim
   return need;
 }
 
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
+  if (a.head_dim == 128) return launch_decode_d<128>(a, p, s);
+  if (a.head_dim == 256) return launch_decode_d<256>(a, p, s);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace kvq_impl
