@@ -1,17 +1,21 @@
 """Benchmark of the SRFT-rotated int4 KV-cache hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5]
 
 One step is one decode step of the hot path over every layer of the workload (layers folded
 into the batch): append-quantize the new token's K and V (write path), then fused
 dequant + decode attention over the whole cache (read path).  The fp16-KV decode of the same
 build and the bulk (prefill) quantize are timed the same way and reported beside it.
 
-Timing: the K timed steps of each measured unit are captured in one HIP graph, step i reading
-cache copy i mod R (R copies span >= 1 GB, four times the MI355X Infinity Cache), so every step
-reads cold data and host launch overhead is paid once per graph.  A graph of W warm-up steps runs
-first; the timed replay is bracketed by device synchronizations and HIP events.  Inputs are
-resident in HBM before the timed region starts.
+The default workload is the long-context serving shard (32 layers x 8 sequences x 8 kv heads,
+32 query heads, d = 128, 32768 tokens, int4): the largest configuration that fits one GPU.
+
+Timing: the K timed steps of each measured unit are captured in HIP graphs, step i of graph j
+reading cache copy (j K + i) mod R (R copies span >= 1 GB, four times the MI355X Infinity Cache;
+the timed replays cycle through the graphs when R > K), so every step reads cold data and host
+launch overhead is paid once per graph.  A graph of W warm-up steps runs first; each timed replay
+is bracketed by device synchronizations and HIP events.  Inputs are resident in HBM before the
+timed region starts.
 
 Prints ONE JSON line (rank 0).
 """
@@ -43,7 +47,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=0, help="timed steps (default: 4 x the cache copies)")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=5,
+                    help="1 tiny, 2 Qwen-like, 3 Gemma-like (d 256, K8V4), 4 48 L x 16 H, 5 serving shard (default)")
     ap.add_argument("--seq", type=int, default=0, help="override the workload's sequence length (a sweep point)")
     ap.add_argument("--k-bits", type=int, choices=(4, 8), default=0, help="override the workload's K width")
     ap.add_argument("--v-bits", type=int, choices=(4, 8), default=0, help="override the workload's V width")
@@ -57,11 +62,13 @@ def parse():
 
 
 class Timer:
-    """Time exactly `steps` steps: one HIP graph holds them all (each step on the next cache
-    copy), so host launch overhead is paid once per graph, not per step.  A separate graph of
-    `warmup` steps runs first, then the timed graph is replayed untimed for at least 100 ms
-    (steady clocks); each timed replay is bracketed by device synchronizations and HIP events on
-    the capturing stream; it is repeated `repeats` times for the spread."""
+    """Time exactly `steps` steps per replay: a HIP graph holds `steps` steps, step i of graph j on
+    cache copy (j * steps + i) mod n_copies.  When the copies outnumber the steps, several graphs
+    cover them all and the timed replays cycle through the graphs, so the data read between two
+    replays of one graph spans every copy (>= 1 GB) whatever `steps` is.  Host launch overhead is
+    paid once per graph.  A graph of `warmup` steps runs first, then the timed graphs are replayed
+    untimed for at least 100 ms (steady clocks); each timed replay is bracketed by device
+    synchronizations and HIP events on the replaying stream, `repeats` replays for the spread."""
 
     def __init__(self, torch):
         self.torch = torch
@@ -73,30 +80,34 @@ class Timer:
             gw.replay()
             torch.cuda.synchronize()
             del gw
-        g = capture(torch, lambda: [step_fn(i % n_copies) for i in range(steps)])
+        n_graphs = max(1, -(-n_copies // steps))
+        graphs = [capture(torch, lambda j=j: [step_fn((j * steps + i) % n_copies) for i in range(steps)])
+                  for j in range(n_graphs)]
+        repeats = max(repeats, n_graphs)
         # settle: replay for at least 100 ms so that clocks and caches are in steady state
         t_settle, n_settle = time.perf_counter(), 0
-        while n_settle < 2 or time.perf_counter() - t_settle < 0.1:
-            g.replay()
+        while n_settle < 2 * n_graphs or time.perf_counter() - t_settle < 0.1:
+            graphs[n_settle % n_graphs].replay()
             torch.cuda.synchronize()
             n_settle += 1
         times = []
-        for _ in range(repeats):
+        for r in range(repeats):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             e0.record()
-            g.replay()
+            graphs[r % n_graphs].replay()
             e1.record()
             torch.cuda.synchronize()
             wall = time.perf_counter() - t0
             times.append((e0.elapsed_time(e1), wall))
-        del g
+        del graphs
         per = np.array([t / steps for t, _ in times])
         return {"ms_mean": float(per.mean()), "ms_median": float(np.median(per)),
                 "ms_p10": float(np.percentile(per, 10)), "ms_p90": float(np.percentile(per, 90)),
                 "ms_min": float(per.min()), "ms_max": float(per.max()), "repeats": repeats, "steps": steps,
+                "graphs": n_graphs, "copies": n_copies,
                 "wall_ms_per_step": 1e3 * float(np.mean([w for _, w in times])) / steps}
 
 
@@ -114,39 +125,85 @@ def capture(torch, fn):
     return g
 
 
+def cpu_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "usable_cpus": usable}
+
+
 def cpu_baseline(w, budget_s, transform="srft"):
-    """Time the CPU oracle, as it stands, on a bounded sample of the same workload."""
+    """Time the CPU oracle, as it stands, on a bounded sample of the same workload: units of one
+    sequence of one layer (all its kv heads and query heads), drawn with the workload's recipe,
+    each quantized (K and V, oracle write path) and decoded (oracle attention over the oracle's
+    planes) until `budget_s` of oracle time is spent.  BLAS threads are pinned with threadpoolctl:
+    once to one thread, once to every usable CPU (capped by OMP_NUM_THREADS when set)."""
+    import dataclasses
+
+    from threadpoolctl import threadpool_limits
+
     from kv_cache_quantization_srft_amd import synth
     from oracle import kvq_oracle as O
 
+    info = cpu_info()
+    all_threads = info["usable_cpus"]
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        all_threads = min(all_threads, int(os.environ["OMP_NUM_THREADS"]))
     s = synth.signs(w)
-    layers_done, t_dec, t_q, vec_q = 0, 0.0, 0.0, 0
-    t_start = time.perf_counter()
-    layer = 0
-    while layers_done < 1 or time.perf_counter() - t_start < budget_s:
-        k = synth.kv(w, layer, synth.K_TENSOR)
-        v = synth.kv(w, layer, synth.V_TENSOR)
-        q = synth.query(w, layer)
-        lk = O.calibrate_lambda(k, s, w.n_cal, transform)[:, :, None, :] if w.calibrate else 1.0
-        lv = O.calibrate_lambda(v, s, w.n_cal, transform)[:, :, None, :] if w.calibrate else 1.0
-        t0 = time.perf_counter()
-        kc, ks = O.quantize(k, s, lk, w.k_bits, transform=transform)
-        vc, vs = O.quantize(v, s, lv, w.v_bits, transform=transform)
-        t1 = time.perf_counter()
-        O.decode_attention_quantized(q, kc, ks, vc, vs, s, s, lk, lv, w.seq_len, transform=transform)
-        t2 = time.perf_counter()
-        t_q += t1 - t0
-        t_dec += t2 - t1
-        vec_q += k.size // w.head_dim + v.size // w.head_dim
-        layers_done += 1
-        layer = (layer + 1) % w.layers
-    bytes_layer = w.batch * w.kv_heads * w.seq_len * (w.head_dim * (w.k_bits + w.v_bits) // 8 + 2 * 2 * w.head_dim // 16)
+    w1 = dataclasses.replace(w, batch=1)  # one sequence of a layer per unit
+
+    G = w.q_heads // w.kv_heads
+
+    def run(threads, budget):
+        units, t_dec, t_q, vec_q, t_start, c_start = 0, 0.0, 0.0, 0, time.perf_counter(), time.process_time()
+        with threadpool_limits(limits=threads):
+            while units < 1 or time.perf_counter() - t_start < budget:
+                layer, j = divmod(units, w.kv_heads)
+                layer %= w.layers
+                k = synth.kv(w1, layer, synth.K_TENSOR)[:, j:j + 1]
+                v = synth.kv(w1, layer, synth.V_TENSOR)[:, j:j + 1]
+                q = synth.query(w1, layer)[:, j * G:(j + 1) * G]
+                lk = O.calibrate_lambda(k, s, w.n_cal, transform)[:, :, None, :] if w.calibrate else 1.0
+                lv = O.calibrate_lambda(v, s, w.n_cal, transform)[:, :, None, :] if w.calibrate else 1.0
+                t0 = time.perf_counter()
+                kc, ks = O.quantize(k, s, lk, w.k_bits, transform=transform)
+                vc, vs = O.quantize(v, s, lv, w.v_bits, transform=transform)
+                t1 = time.perf_counter()
+                O.decode_attention_quantized(q, kc, ks, vc, vs, s, s, lk, lv, w.seq_len, transform=transform)
+                t2 = time.perf_counter()
+                t_q += t1 - t0
+                t_dec += t2 - t1
+                vec_q += k.size // w.head_dim + v.size // w.head_dim
+                units += 1
+        # cores the run kept busy: process CPU time (all threads) over wall time
+        busy = (time.process_time() - c_start) / max(time.perf_counter() - t_start, 1e-9)
+        bytes_unit = w.seq_len * (w.head_dim * (w.k_bits + w.v_bits) // 8 + 2 * 2 * w.head_dim // 16)
+        return {"decode_GBps": bytes_unit * units / t_dec / 1e9, "decode_ms_per_unit": 1e3 * t_dec / units,
+                "quantize_Mvectors_per_s": vec_q / t_q / 1e6, "units": units, "blas_threads": threads,
+                "cores_busy": round(busy, 2)}
+
+    single = run(1, budget_s / 2)
+    multi = run(all_threads, budget_s / 2)
+    units_step = w.layers * w.batch * w.kv_heads
     return {
-        "value": bytes_layer * layers_done / t_dec / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": (f"{layers_done} of {w.layers} layers: oracle decode (dequantize K,V by the O(d^2) inverse {transform.upper()} + attention "
-                   f"over {w.seq_len} tokens, {w.q_heads} heads); numpy float64, single thread"),
-        "decode_ms_per_layer": 1e3 * t_dec / layers_done,
-        "quantize_Mvectors_per_s": vec_q / t_q / 1e6,
+        "value": round(multi["decode_GBps"], 4), "unit": "GB/s", "cores": max(1, round(multi["cores_busy"])),
+        "kind": "oracle", "blas_threads_allowed": all_threads,
+        "sample": (f"{multi['units']} units of one (layer, sequence, kv head) with its {G} query heads over "
+                   f"{w.seq_len} tokens (a decode step of the workload is {units_step} such units): oracle write "
+                   f"path on K and V, then oracle decode (dequantize by the O(d^2) inverse {transform.upper()} + "
+                   f"attention); numpy float64 with BLAS pinned to {all_threads} threads (the oracle's DFT is an "
+                   f"einsum that runs on one core; `cores` is the measured CPU time over wall time)"),
+        "decode_ms_per_step_extrapolated": round(multi["decode_ms_per_unit"] * units_step, 1),
+        "quantize_Mvectors_per_s": round(multi["quantize_Mvectors_per_s"], 4),
+        "single_thread": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in single.items()},
+        "host": info,
     }
 
 
@@ -159,7 +216,8 @@ def decode_sources_sha():
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "kv_cache_quantization_srft_amd", "csrc")
-    for name in ("kvq_decode_q.hip", "kvq_decode_common.h", "kvq_internal.h", "kvq_device.h", "kvq_plan.cpp"):
+    for name in ("kvq_decode_q.h", "kvq_decode_q128.hip", "kvq_decode_q256.hip", "kvq_decode_common.h",
+                 "kvq_internal.h", "kvq_device.h", "kvq_plan.cpp"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -324,8 +382,18 @@ def main():
     del src, dst
 
     Rf = len(kv16)
+    steps_f = args.steps if args.steps > 0 else 4 * Rf
     res_f16 = timer.run(lambda i: kvq.kvq_decode_attn_fp16(lay, q, kv16[i][0], kv16[i][1], S, None, 0.0, ws, out16),
-                        Rf, max(steps, 4 * Rf), args.warmup)
+                        Rf, steps_f, args.warmup)
+    # mode B for the fp16 comparator: one launch per layer
+    out16_l = out16.view(L, -1)
+    views16 = [[(kv16[i][0].view(L, -1)[l], kv16[i][1].view(L, -1)[l]) for l in range(L)] for i in range(Rf)]
+
+    def decode_f16_per_layer(i):
+        for l in range(L):
+            kvq.kvq_decode_attn_fp16(lay_l, qv_l[l], views16[i][l][0], views16[i][l][1], S, None, 0.0, ws, out16_l[l])
+
+    res_f16_b = timer.run(decode_f16_per_layer, Rf, min(steps_f, max(8, 4096 // L)), min(args.warmup, 2))
     # bulk quantize: all layers, K and V, from rotating fp16 copies into rotating planes
     nb = max(R, Rf)
     res_bq = timer.run(lambda i: quantize_all(planes[i % R], *kv16[i % Rf]), nb, 2 * nb, args.warmup)
@@ -435,6 +503,11 @@ def main():
             "launches_per_step": L, "ms": round(res_dec_b["ms_median"], 5),
             "GBps": round(dec_bytes / (res_dec_b["ms_median"] * 1e-3) / 1e9, 2),
             "note": "mode B: one kvq_decode_attn per layer (batch B), all in one HIP graph"},
+        "fp16_decode_per_layer_launches": {
+            "launches_per_step": L, "ms": round(res_f16_b["ms_median"], 5),
+            "GBps": round(f16_bytes / (res_f16_b["ms_median"] * 1e-3) / 1e9, 2),
+            "speedup_quantized_vs_fp16_per_layer": round(res_f16_b["ms_median"] / res_dec_b["ms_median"], 3),
+            "note": "mode B for the fp16 comparator: one kvq_decode_attn_fp16 per layer, one HIP graph"},
         "copy_1GiB": {"GBps": round(copy_gbps, 2), "frac_hbm_peak": round(copy_gbps / HBM_PEAK_GBPS, 4),
                       "ms": round(res_copy["ms_median"], 5)},
         "fp16_decode": {"GBps": round(f16_gbps, 2), "frac_hbm_peak": round(f16_gbps / HBM_PEAK_GBPS, 4),

@@ -96,7 +96,9 @@ const char* kvq_last_error_message(void);
  * Returns 0 if the layout or bits are invalid. Host-only, no HIP call. */
 size_t kvq_codes_bytes(const kvq_layout* layout, int32_t bits);
 
-/* Bytes of one scale plane: batch * kv_heads * capacity * (head_dim / 16) * 2.  0 if invalid. */
+/* Bytes of one scale plane: batch * kv_heads * capacity * (head_dim / group_size) * 2: one fp16
+ * scale per group of 16 channels ([QF] Methodology 3, per-group scaling), the scale term of the
+ * hotdry blog's footprint formula ("INT8/INT4 量化策略").  0 if the layout is invalid. */
 size_t kvq_scales_bytes(const kvq_layout* layout);
 
 /*
@@ -121,7 +123,8 @@ kvq_status kvq_quantize(const kvq_layout* layout, int32_t bits, const void* x_f1
                         void* scales, void* stream);
 
 /*
- * kvq_dequantize -- inverse of the write path, for inspection and tests.
+ * kvq_dequantize -- inverse of the write path ([QF] Methodology 2 run backwards: unpack, times
+ * scale and lambda, inverse rotation, sign), for inspection and tests.
  *   out[b, h, t, :] = s * SRFT^-1(lambda * code * scale) for tokens pos .. pos+n_tok-1,
  *   out: float [batch, kv_heads, n_tok, head_dim], contiguous.  Other arguments as kvq_quantize.
  */
@@ -163,7 +166,11 @@ size_t kvq_decode_attn_workspace_bytes(const kvq_layout* layout, int32_t max_seq
  *   sm_scale     : softmax scale; <= 0 selects 1/sqrt(head_dim)
  *   workspace    : >= kvq_decode_attn_workspace_bytes(layout, seq_len) bytes, 256-byte aligned.
  *                  Its first 65536 bytes are completion counters: zero them once after
- *                  allocating the workspace; every call leaves them zero.  The rest is scratch.
+ *                  allocating the workspace; every call that runs to completion leaves them
+ *                  zero.  The rest is scratch.  After a call that did not complete (a launch
+ *                  error reported by a later call, a device fault, a stream torn down while
+ *                  it ran), zero the first 65536 bytes again before the next call: stale
+ *                  counters make later calls merge at the wrong count.
  *                  One workspace serves one call at a time (calls in flight on different
  *                  streams need their own); in use until the work on `stream` completes.
  *                  batch * kv_heads * (G / head tile) must not exceed 16384, where the head
@@ -237,14 +244,52 @@ kvq_status kvq_decode_attn_paged(const kvq_layout* layout, const void* q_f16, co
                                  void* workspace, size_t workspace_bytes, float* out, void* stream);
 
 /*
- * kvq_decode_attn_fp16 -- the same decode attention over an unquantized fp16 cache (the
- * comparator): k_f16, v_f16 are fp16 [batch, kv_heads, capacity, head_dim]; no rotation, no
- * lambda.  layout->k_bits/v_bits are ignored.  Other arguments as kvq_decode_attn.
+ * kvq_decode_attn_fp16 -- the same decode attention over an unquantized fp16 cache, the baseline
+ * the quantized cache is measured against ([GM] "INT8/INT4 量化策略": the fp16 cache of 2 bytes
+ * per element that int4 shrinks to 25%; [QF] Key results: int4 decode against fp16 KV).
+ * k_f16, v_f16 are fp16 [batch, kv_heads, capacity, head_dim]; no rotation, no lambda.
+ * layout->k_bits/v_bits are ignored.  Other arguments as kvq_decode_attn.
  */
 kvq_status kvq_decode_attn_fp16(const kvq_layout* layout, const void* q_f16, const void* k_f16,
                                 const void* v_f16, int32_t seq_len, const int32_t* seq_lens,
                                 float sm_scale, void* workspace, size_t workspace_bytes,
                                 float* out, void* stream);
+
+/*
+ * kvq_launch_plan -- how a call splits its work (host only, no HIP call): for capacity planning,
+ * occupancy reasoning and tests that must reach a given loop depth.  The split is the one the
+ * call itself launches with; it depends on the layout and n only.
+ *   call : KVQ_CALL_QUANTIZE (n = n_tok of kvq_quantize) or one of the decode calls (n = seq_len)
+ *   out  : host struct, written on success
+ * Decode calls: one work-group per (sequence, kv head, head tile, chunk of `chunk` tokens); each
+ * of its 4 waves walks superblocks of `wave_tokens` tokens, so a wave handles up to
+ * superblocks_per_wave of them.  Quantize: 16-vector blocks, each work-group a contiguous range of
+ * at most blocks_per_work_group of them.  Fields that do not apply to a call are 0.
+ * Errors: KVQ_ERR_INVALID_ARGUMENT / KVQ_ERR_UNSUPPORTED as the call itself would return for the
+ * layout and n.
+ */
+typedef enum {
+  KVQ_CALL_QUANTIZE = 0,
+  KVQ_CALL_DECODE = 1,              /* kvq_decode_attn */
+  KVQ_CALL_DECODE_APPEND = 2,       /* kvq_decode_attn_append */
+  KVQ_CALL_DECODE_PAGED = 3,        /* kvq_decode_attn_paged without new vectors */
+  KVQ_CALL_DECODE_PAGED_APPEND = 4, /* kvq_decode_attn_paged with new vectors */
+  KVQ_CALL_DECODE_FP16 = 5          /* kvq_decode_attn_fp16 */
+} kvq_call;
+
+typedef struct {
+  int64_t work_groups;           /* grid size of the call's kernel                         */
+  int32_t head_tile;             /* decode: query heads per work-group                     */
+  int32_t head_tiles;            /* decode: G / head_tile                                  */
+  int32_t chunk;                 /* decode: tokens per work-group                          */
+  int32_t n_chunks;              /* decode: work-groups per (sequence, kv head, head tile) */
+  int32_t wave_tokens;           /* decode: tokens of one wave superblock (64; fp16: 32)   */
+  int32_t superblocks_per_wave;  /* decode: ceil(chunk / (4 * wave_tokens))                */
+  int64_t blocks;                /* quantize: 16-vector blocks of the call                 */
+  int64_t blocks_per_work_group; /* quantize: largest block range of one work-group        */
+} kvq_plan;
+
+kvq_status kvq_launch_plan(const kvq_layout* layout, kvq_call call, int32_t n, kvq_plan* out);
 
 #ifdef __cplusplus
 }

@@ -363,4 +363,44 @@ kvq_status kvq_decode_attn_fp16(const kvq_layout* L, const void* q_f16, const vo
   return hip_status(kvq_impl::launch_decode_f16(a, p, static_cast<hipStream_t>(stream)), fn);
 }
 
+kvq_status kvq_launch_plan(const kvq_layout* L, kvq_call call, int32_t n, kvq_plan* out) {
+  const char* fn = "kvq_launch_plan";
+  KVQ_TRY(check_layout(L, fn));
+  if (!out) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: out is NULL", fn);
+  kvq_plan r{};
+  if (call == KVQ_CALL_QUANTIZE) {
+    KVQ_TRY(check_range(L, 0, n, fn));
+    const kvq_impl::QuantPlan q = kvq_impl::plan_quantize(L->head_dim, int64_t(L->batch) * L->kv_heads * n);
+    r.work_groups = q.grid;
+    r.blocks = q.blocks;
+    r.blocks_per_work_group = (q.blocks + q.grid - 1) / q.grid;
+    *out = r;
+    return ok();
+  }
+  if (call < KVQ_CALL_DECODE || call > KVQ_CALL_DECODE_FP16)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: unknown call %d", fn, int(call));
+  if (L->q_heads < 1 || L->q_heads % L->kv_heads != 0)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: q_heads (%d) must be a positive multiple of kv_heads (%d)", fn,
+                L->q_heads, L->kv_heads);
+  if (L->q_heads / L->kv_heads > 64)
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: GQA ratio %d (supported: <= 64)", fn, L->q_heads / L->kv_heads);
+  if (n < 1 || n > L->capacity)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: seq_len %d must lie in [1, capacity=%d]", fn, n, L->capacity);
+  const bool f16 = call == KVQ_CALL_DECODE_FP16;
+  const bool append = call == KVQ_CALL_DECODE_APPEND || call == KVQ_CALL_DECODE_PAGED_APPEND;
+  const bool paged = call == KVQ_CALL_DECODE_PAGED || call == KVQ_CALL_DECODE_PAGED_APPEND;
+  const kvq_impl::DecodePlan p =
+      kvq_impl::plan_decode(L->batch, L->kv_heads, L->q_heads, L->head_dim, n, n, f16, append, paged);
+  const int64_t units = int64_t(L->batch) * L->kv_heads * p.head_tiles;
+  r.work_groups = units * p.n_chunks;
+  r.head_tile = p.head_tile;
+  r.head_tiles = p.head_tiles;
+  r.chunk = p.chunk;
+  r.n_chunks = p.n_chunks;
+  r.wave_tokens = f16 ? 32 : 64;
+  r.superblocks_per_wave = (p.chunk + 4 * r.wave_tokens - 1) / (4 * r.wave_tokens);
+  *out = r;
+  return ok();
+}
+
 }  // extern "C"

@@ -120,7 +120,15 @@ __host__ __device__ inline WsLayout ws_layout(int units, int head_tile, int head
   return w;
 }
 
+// Grid of the write path: 16-vector blocks, each work-group a contiguous range of them.
+struct QuantPlan {
+  int grid;          // work-groups
+  int64_t blocks;    // 16-vector blocks in the call
+};
+constexpr int kQuantVecs = 16;  // vectors per block (MFMA columns)
+
 // Host-side planning (pure host code, no HIP call).
+QuantPlan plan_quantize(int head_dim, int64_t n_vec);
 DecodePlan plan_decode(int batch, int kv_heads, int q_heads, int head_dim, int seq_len, int max_seq_len, bool f16,
                        bool append = false, bool paged = false);
 size_t decode_workspace_bytes(int batch, int kv_heads, int q_heads, int head_dim, int max_seq_len);

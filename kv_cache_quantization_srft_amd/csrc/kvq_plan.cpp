@@ -16,6 +16,15 @@ int token_align(bool f16) { return f16 ? 4 * 32 : 4 * 64; }  // 4 waves x superb
 
 }  // namespace
 
+QuantPlan plan_quantize(int head_dim, int64_t n_vec) {
+  QuantPlan q;
+  q.blocks = (n_vec + kQuantVecs - 1) / kQuantVecs;
+  // resident work-groups: 3 per CU at d = 128 (256 threads), 1 at d = 256 (512 threads)
+  const int64_t resident = head_dim == 128 ? 3 * 256 : 256;
+  q.grid = int(std::max<int64_t>(1, std::min<int64_t>(q.blocks, resident)));
+  return q;
+}
+
 DecodePlan plan_decode(int batch, int kv_heads, int q_heads, int head_dim, int seq_len, int max_seq_len, bool f16,
                        bool append, bool paged) {
   DecodePlan p{};

@@ -47,7 +47,7 @@ namespace mq {
 using dec::v8h;
 using dec::v4f;
 
-constexpr int kVecs = 16;  // vectors per block (MFMA columns)
+constexpr int kVecs = kQuantVecs;  // vectors per block (MFMA columns)
 
 // max over the four 16-lane rows for every lane position (v_permlane32_swap, v_permlane16_swap)
 // of a non-negative float given as its bit pattern (non-negative floats order like their bits)
@@ -304,10 +304,7 @@ template <int D, int BITS, bool PT>
 hipError_t quantize_mfma_dispatch(const QuantArgs& a, hipStream_t s) {
   const uint32_t n_vec = uint32_t(a.batch) * uint32_t(a.kv_heads) * uint32_t(a.n_tok);  // < 2^31 (validated)
   const FastDiv fd_tok = FastDiv::make(uint32_t(a.n_tok)), fd_heads = FastDiv::make(uint32_t(a.kv_heads));
-  const int64_t blocks = (n_vec + mq::kVecs - 1) / mq::kVecs;
-  // resident work-groups per CU: 3 (d = 128, 256 threads), 1 (d = 256, 512 threads)
-  const int64_t resident = D == 128 ? 3 * 256 : 256;
-  const int grid = int(std::min<int64_t>(blocks, resident));
+  const int grid = plan_quantize(D, n_vec).grid;
   auto* x = static_cast<const uint16_t*>(a.x);
   auto* codes = static_cast<uint8_t*>(a.codes);
   auto* scales = static_cast<uint16_t*>(a.scales);

@@ -23,6 +23,7 @@ EXPORTS = (
     "kvq_version", "kvq_status_string", "kvq_last_error_message", "kvq_codes_bytes", "kvq_scales_bytes",
     "kvq_quantize", "kvq_dequantize", "kvq_calibrate_lambda", "kvq_decode_attn_workspace_bytes",
     "kvq_decode_attn", "kvq_decode_attn_append", "kvq_decode_attn_paged", "kvq_decode_attn_fp16",
+    "kvq_launch_plan",
 )
 
 
@@ -46,6 +47,17 @@ def make_layout(batch, kv_heads, q_heads, head_dim, capacity, k_bits=4, v_bits=4
     """transform: "srft" (KVQ_TRANSFORM_SRFT) or "srht" (KVQ_TRANSFORM_SRHT), or the enum value."""
     tr = TRANSFORMS[transform] if isinstance(transform, str) else int(transform)
     return kvq_layout(batch, kv_heads, q_heads, head_dim, group_size, k_bits, v_bits, capacity, tr)
+
+
+CALLS = {"quantize": 0, "decode": 1, "decode_append": 2, "decode_paged": 3, "decode_paged_append": 4,
+         "decode_fp16": 5}
+
+
+class kvq_plan(ctypes.Structure):
+    _fields_ = [("work_groups", ctypes.c_int64), ("head_tile", ctypes.c_int32), ("head_tiles", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("n_chunks", ctypes.c_int32), ("wave_tokens", ctypes.c_int32),
+                ("superblocks_per_wave", ctypes.c_int32), ("blocks", ctypes.c_int64),
+                ("blocks_per_work_group", ctypes.c_int64)]
 
 
 _lib = None
@@ -90,6 +102,8 @@ def lib() -> ctypes.CDLL:
                                             _P, _I64, _P, _P, _I64, ctypes.c_float, _P, _SZ, _P, _P]
         L.kvq_decode_attn_fp16.restype = ctypes.c_int
         L.kvq_decode_attn_fp16.argtypes = [_LP, _P, _P, _P, _I32, _P, ctypes.c_float, _P, _SZ, _P, _P]
+        L.kvq_launch_plan.restype = ctypes.c_int
+        L.kvq_launch_plan.argtypes = [_LP, ctypes.c_int, _I32, ctypes.POINTER(kvq_plan)]
         _lib = L
     return _lib
 
@@ -268,3 +282,11 @@ def kvq_decode_attn_fp16(layout, q, k, v, seq_len, seq_lens, sm_scale, workspace
         _ptr(seq_lens, torch.int32, "seq_lens", layout.batch), float(sm_scale), _ptr(workspace, None, "workspace"),
         workspace.numel() * workspace.element_size(), _ptr(out, _f32(), "out", layout.batch * layout.q_heads * d),
         _stream(stream)))
+
+
+def kvq_launch_plan(layout, call, n) -> kvq_plan:
+    """call: a key of CALLS ("quantize", "decode", ...) or its enum value; returns the plan struct."""
+    c = CALLS[call] if isinstance(call, str) else int(call)
+    out = kvq_plan()
+    _check(lib().kvq_launch_plan(ctypes.byref(layout), c, n, ctypes.byref(out)))
+    return out

@@ -159,3 +159,66 @@ def torch_kv(w: Workload, layer: int, tensor: int, device, seq_len: int | None =
     else:
         raise ValueError(dist)
     return x.clamp_(-65504.0, 65504.0).to(torch.float16)
+
+
+# ----------------------------------------------------------------------------------------------
+# Random cache planes: in-range code bytes and positive fp16 scales drawn directly (no vector is
+# quantized to make them), so a large cache costs only random-number generation.  A code plane
+# row holds d*bits/8 bytes per token; every int4 nibble and every int8 byte is a two's-complement
+# value in [-qmax, qmax] (-8 and -128, which the write path never produces, are replaced by 0).
+# ----------------------------------------------------------------------------------------------
+def random_code_bytes(rng: np.random.Generator, shape: tuple, bits: int) -> np.ndarray:
+    """uint8 array of `shape` (the last axis counts bytes) holding random in-range codes."""
+    b = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    if bits == 8:
+        b[b == 0x80] = 0
+        return b
+    lo = b & 0x0F
+    hi = b >> 4
+    lo[lo == 8] = 0
+    hi[hi == 8] = 0
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def random_scales(rng: np.random.Generator, shape: tuple, lo: float, hi: float) -> np.ndarray:
+    """float16 array of `shape`, log-uniform in [lo, hi]."""
+    return np.exp(rng.uniform(np.log(lo), np.log(hi), size=shape)).astype(np.float16)
+
+
+def random_lambda(rng: np.random.Generator, shape: tuple, lo: float = 0.5, hi: float = 8.0) -> np.ndarray:
+    """float32 array of `shape`, log-uniform in [lo, hi] (per-channel factors)."""
+    return np.exp(rng.uniform(np.log(lo), np.log(hi), size=shape)).astype(np.float32)
+
+
+def torch_random_code_bytes(gen, numel: int, bits: int, device, chunk: int = 1 << 28):
+    """random_code_bytes on a torch device (flat uint8 tensor of `numel` bytes), drawn in chunks
+    with the seeded generator `gen`; same recipe, not the same numbers as the NumPy version."""
+    import torch
+
+    out = torch.empty(numel, dtype=torch.uint8, device=device)
+    for i in range(0, numel, chunk):
+        n = min(chunk, numel - i)
+        b = torch.randint(0, 256, (n,), generator=gen, device=device, dtype=torch.uint8)
+        if bits == 8:
+            b[b == 0x80] = 0
+        else:
+            lo = b & 0x0F
+            hi = b >> 4
+            lo[lo == 8] = 0
+            hi[hi == 8] = 0
+            b = lo | (hi << 4)
+        out[i:i + n] = b
+    return out
+
+
+def torch_random_scales(gen, numel: int, lo: float, hi: float, device, chunk: int = 1 << 28):
+    """random_scales on a torch device: flat fp16 tensor, log-uniform in [lo, hi]."""
+    import torch
+
+    out = torch.empty(numel, dtype=torch.float16, device=device)
+    a, b = float(np.log(lo)), float(np.log(hi))
+    for i in range(0, numel, chunk):
+        n = min(chunk, numel - i)
+        u = torch.rand((n,), generator=gen, device=device, dtype=torch.float32)
+        out[i:i + n] = torch.exp(a + (b - a) * u).to(torch.float16)
+    return out

@@ -7,7 +7,7 @@ Tolerances (fixed by the requirements of the method's port, restated here):
   * in groups whose scales agree, at most 0.1% of codes differ from the oracle's, each by +-1,
     and only where u/scale is within 1e-3 of a rounding tie;
   * in groups whose scales differ by one ulp, codes are valid for the GPU's scale
-    (|u/scale - code| <= 0.5 + 1e-3, |code| <= qmax);
+    (|u/scale - code| <= 0.5 + 1e-3, or u/scale beyond qmax clamped to qmax of its sign);
   * dequantized vectors (from the oracle's planes) within 1e-3 x the vector's max-abs;
   * attention outputs (from the oracle's planes) within 2e-3 max-abs.
 """
@@ -93,7 +93,10 @@ def check_quantize(gpu_bytes, gpu_scales, u, bits, label="", group=16):
         sc = np.repeat(gs.astype(np.float64), group, axis=-1).reshape(u.shape)
         r = u[~same] / np.where(sc[~same] > 0, sc[~same], 1.0)
         err = np.abs(r - gc[~same])
-        ok = (sc[~same] == 0) | (err <= 0.5 + TIE_WINDOW) | (np.abs(gc[~same]) == qmax)
+        # a code is valid for the GPU's scale if it is the rounding of u / scale (within the tie
+        # window), or the clamp of a ratio beyond qmax to the qmax of the same sign
+        clamped = (np.abs(r) > qmax) & (gc[~same] == np.sign(r) * qmax)
+        ok = ((sc[~same] == 0) & (gc[~same] == 0)) | (err <= 0.5 + TIE_WINDOW) | clamped
         assert ok.all(), f"{label}: invalid codes in 1-ulp scale groups"
     return n_diff, int((ulp > 0).sum())
 
@@ -136,3 +139,47 @@ def gpu_decode_fp16(q16, k16, v16, seq_len, seq_lens=None, sm_scale=0.0, ws=None
     kvq.kvq_decode_attn_fp16(lay, dev(q16), dev(k16), dev(v16), seq_len, sl, sm_scale, ws, out)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64)
+
+
+def plan(layout, call, n):
+    """The launch plan of a call (kvq_launch_plan) as a dict."""
+    p = kvq.kvq_launch_plan(layout, call, n)
+    return {f: getattr(p, f) for f, _ in p._fields_}
+
+
+def gpu_decode_planes(lay, q16, kb, ks16, vb, vs16, seq_len, seq_lens, s_k, s_v, lam_k, lam_v, lambda_bs,
+                      sm_scale=0.0, page=None):
+    """kvq_decode_attn (or kvq_decode_attn_paged when page = (table [B, pps], page_size, num_pages))
+    on packed planes given as numpy arrays; returns the output [B, Hq, d] as float64."""
+    B, Hq, d = lay.batch, lay.q_heads, lay.head_dim
+    ws = torch.zeros(kvq.kvq_decode_attn_workspace_bytes(lay, seq_len), dtype=torch.uint8, device="cuda")
+    out = torch.full((B, Hq, d), float("nan"), dtype=torch.float32, device="cuda")
+    args = (dev(kb), dev(ks16.view(np.int16)), dev(vb), dev(vs16.view(np.int16)))
+    sl = None if seq_lens is None else dev(np.asarray(seq_lens, np.int32))
+    lk = None if lam_k is None else dev(np.asarray(lam_k, np.float32))
+    lv = None if lam_v is None else dev(np.asarray(lam_v, np.float32))
+    if page is None:
+        kvq.kvq_decode_attn(lay, dev(q16), *args, seq_len, sl, dev(s_k), dev(s_v), 0, lk, lv, lambda_bs, sm_scale, ws,
+                            out)
+    else:
+        table, page_size, num_pages = page
+        kvq.kvq_decode_attn_paged(lay, dev(q16), None, None, *args, dev(np.asarray(table, np.int32)), table.shape[1],
+                                  page_size, num_pages, seq_len, sl, dev(s_k), dev(s_v), 0, lk, lv, lambda_bs,
+                                  sm_scale, ws, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def oracle_unit(q16, kb, ks16, vb, vs16, k_bits, v_bits, s_k, s_v, lk_row, lv_row, L, sm_scale=None,
+                transform="srft"):
+    """The oracle's decode attention of one (sequence, kv head): q16 [G, d]; kb, vb packed code rows
+    [>= L, bytes]; ks16, vs16 [>= L, d/16]; lk_row, lv_row [d] or None.  Returns [G, d] float64."""
+    G, d = q16.shape
+    if L == 0:
+        return np.zeros((G, d))
+    kc = O.unpack_codes(kb[:L], k_bits)[None, None]
+    vc = O.unpack_codes(vb[:L], v_bits)[None, None]
+    lk = 1.0 if lk_row is None else np.asarray(lk_row, np.float64)[None, None, None, :]
+    lv = 1.0 if lv_row is None else np.asarray(lv_row, np.float64)[None, None, None, :]
+    return O.decode_attention_quantized(q16[None], kc, ks16[:L][None, None], vc, vs16[:L][None, None], s_k, s_v,
+                                        lk, lv, L, sm_scale=sm_scale, transform=transform)[0]

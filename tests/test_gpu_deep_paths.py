@@ -1,0 +1,243 @@
+"""GPU parity of the decode kernels on the code paths that long rows and large batches take:
+many 64-token superblocks per wave (the next superblock's loads issued during the current
+one, the online-softmax rescale of a running sum and accumulator, paged lookups of the k-th
+superblock's page, the append patch of a later superblock), several chunks per row (the
+cross-work-group merge) and GQA ratios above the head tile.
+
+Each test asks the library for its launch plan (kvq_launch_plan) and asserts the depth it
+claims to reach.  The caches are random in-range code bytes and fp16 scales (synth's random
+planes), so no vector needs quantizing; sampled (sequence, kv head) units are compared element
+by element with the oracle's attention over the same planes, 2e-3 max-abs."""
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_quantization_srft_amd import kvq, synth
+from oracle import kvq_oracle as O
+
+from gpu_parity import ATTN_ATOL, check_quantize, dev, gpu_decode_planes, oracle_unit, plan, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _cache(rng, B, Hkv, S, d, kb, vb, k_scales=(0.15, 0.8), v_scales=(0.15, 0.8), lam=(0.5, 2.0)):
+    kbytes = synth.random_code_bytes(rng, (B, Hkv, S, d * kb // 8), kb)
+    vbytes = synth.random_code_bytes(rng, (B, Hkv, S, d * vb // 8), vb)
+    ks = synth.random_scales(rng, (B, Hkv, S, d // 16), *k_scales)
+    vs = synth.random_scales(rng, (B, Hkv, S, d // 16), *v_scales)
+    lk = None if lam is None else synth.random_lambda(rng, (B, Hkv, d), *lam)
+    lv = None if lam is None else synth.random_lambda(rng, (B, Hkv, d), *lam)
+    return kbytes, ks, vbytes, vs, lk, lv
+
+
+def _lengths(rng, B, S):
+    """Ragged lengths: full rows, empty rows, one token, superblock and chunk edges +-1, random."""
+    special = [S, 0, 1, 63, 64, 65, 255, 256, 257, S - 1]
+    lens = rng.integers(1, S + 1, size=B)
+    lens[: min(B, len(special))] = [min(max(x, 0), S) for x in special[:B]]
+    return lens
+
+
+def _units(rng, B, Hkv, n, lens):
+    """Sampled (sequence, kv head) pairs: the first and last rows, every special-length row, random."""
+    picks = {(0, 0), (B - 1, Hkv - 1)}
+    picks |= {(b, int(rng.integers(Hkv))) for b in range(min(B, 10))}
+    while len(picks) < n:
+        picks.add((int(rng.integers(B)), int(rng.integers(Hkv))))
+    return sorted(picks)
+
+
+def _compare(lay, q, cache, S, lens, sk, sv, units, label, page=None, sm_scale=0.0, transform="srft"):
+    kbytes, ks, vbytes, vs, lk, lv = cache
+    d, Hkv = lay.head_dim, lay.kv_heads
+    G = lay.q_heads // Hkv
+    lbs = 0 if lk is None else Hkv * d
+    if page is None:
+        got = gpu_decode_planes(lay, q, kbytes, ks, vbytes, vs, S, lens, sk, sv, lk, lv, lbs, sm_scale)
+    else:
+        got = gpu_decode_planes(lay, q, *page[3], S, lens, sk, sv, lk, lv, lbs, sm_scale, page=page[:3])
+    assert np.isfinite(got).all(), label
+    L_of = (lambda b: S) if lens is None else (lambda b: int(np.clip(lens[b], 0, S)))
+    worst = 0.0
+    for b, j in units:
+        ref = oracle_unit(q[b, j * G:(j + 1) * G], kbytes[b, j], ks[b, j], vbytes[b, j], vs[b, j], lay.k_bits,
+                          lay.v_bits, sk, sv, None if lk is None else lk[b, j], None if lv is None else lv[b, j],
+                          L_of(b), sm_scale=None if sm_scale <= 0 else sm_scale, transform=transform)
+        err = float(np.abs(got[b, j * G:(j + 1) * G] - ref).max())
+        worst = max(worst, err)
+        assert err <= ATTN_ATOL, f"{label}: unit ({b}, {j}) L={L_of(b)} max-abs {err:.3g}"
+    say(label, "worst max-abs over", len(units), "units:", f"{worst:.3g}")
+    return got
+
+
+# d, k_bits, v_bits, B, Hkv, G, S, ragged, scale ranges (K, V), lambda range, min superblocks/wave, min chunks
+# scale ranges that give outputs of order 1 (moderately peaked softmax, values of order 1), so the
+# absolute bar is a tight relative one
+K4, K8, V4, V8 = (0.15, 0.8), (0.01, 0.06), (0.15, 0.8), (0.01, 0.06)
+DEEP = [
+    (128, 4, 4, 64, 8, 4, 1100, True, K4, V4, (0.5, 2.0), 5, 1),
+    (128, 4, 4, 16, 4, 6, 8192, True, K4, V4, (0.5, 2.0), 4, 8),
+    (128, 4, 4, 64, 8, 4, 2048, False, (0.2, 2.0), (0.2, 2.0), (1.0, 8.0), 8, 1),   # sharply peaked softmax
+    (256, 8, 4, 64, 4, 4, 1500, True, K8, V4, None, 6, 1),
+    (128, 4, 8, 128, 4, 2, 900, True, K4, V8, (0.5, 2.0), 4, 1),
+    (128, 8, 8, 512, 1, 1, 700, True, K8, V8, (0.5, 2.0), 3, 1),
+    (256, 4, 8, 32, 2, 8, 4096, True, K4, V8, (0.5, 2.0), 4, 2),
+    (128, 4, 4, 128, 2, 32, 1000, True, K4, V4, (0.5, 2.0), 4, 1),  # G 32: two head tiles
+    (256, 8, 4, 32, 1, 24, 2000, True, K8, V4, None, 3, 3),          # G 24: three head tiles
+]
+
+
+@pytest.mark.parametrize("d,kb,vb,B,Hkv,G,S,ragged,ksr,vsr,lam,min_sb,min_ch", DEEP)
+def test_decode_deep(d, kb, vb, B, Hkv, G, S, ragged, ksr, vsr, lam, min_sb, min_ch):
+    rng = np.random.default_rng(d * 7 + kb * 3 + vb + B + G + S)
+    lay = kvq.make_layout(B, Hkv, Hkv * G, d, S, k_bits=kb, v_bits=vb)
+    pl = plan(lay, "decode", S)
+    say("deep decode", (d, kb, vb, B, Hkv, G, S), pl)
+    assert pl["superblocks_per_wave"] >= min_sb and pl["n_chunks"] >= min_ch, pl
+    cache = _cache(rng, B, Hkv, S, d, kb, vb, ksr, vsr, lam)
+    q = synth.to_fp16(rng.standard_normal((B, Hkv * G, d)))
+    sk = synth.random_signs(int(rng.integers(1 << 30)), d)
+    sv = synth.random_signs(int(rng.integers(1 << 30)), d)
+    lens = _lengths(rng, B, S) if ragged else None
+    _compare(lay, q, cache, S, lens, sk, sv, _units(rng, B, Hkv, 20, lens), f"deep K{kb}V{vb} d{d} G{G} S{S}")
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_decode_deep_large_int8_value_scales(d):
+    """int8 V with scales above 512 in some superblocks of a row and not in others (the
+    range-safe form is chosen per superblock), over several superblocks per wave."""
+    rng = np.random.default_rng(91 + d)
+    B, Hkv, G, S = (64, 8, 2, 1100) if d == 128 else (64, 4, 2, 1300)
+    lay = kvq.make_layout(B, Hkv, Hkv * G, d, S, k_bits=4, v_bits=8)
+    pl = plan(lay, "decode", S)
+    say("deep decode big V scales", d, pl)
+    assert pl["superblocks_per_wave"] >= 4
+    kbytes, ks, vbytes, vs, lk, lv = _cache(rng, B, Hkv, S, d, 4, 8, K4, V8, (0.5, 2.0))
+    big = rng.random((B, Hkv, S)) < 0.02
+    vs[big] = synth.random_scales(rng, (int(big.sum()), d // 16), 600.0, 4000.0)
+    lv = lv * 1e-4
+    q = synth.to_fp16(rng.standard_normal((B, Hkv * G, d)))
+    sk = synth.random_signs(3, d)
+    sv = synth.random_signs(4, d)
+    lens = _lengths(rng, B, S)
+    _compare(lay, q, (kbytes, ks, vbytes, vs, lk, lv), S, lens, sk, sv, _units(rng, B, Hkv, 20, lens),
+             f"deep big V scales d{d}")
+
+
+@pytest.mark.parametrize("d,kb,page_size", [(128, 4, 64), (256, 8, 128), (128, 4, 192)])
+def test_paged_deep(d, kb, page_size):
+    """Paged cache, shuffled pages, several superblocks per wave: the page of superblock k >= 1
+    comes from lane k of the wave's page list.  The output equals the contiguous call's bit for
+    bit (same plan) and matches the oracle."""
+    rng = np.random.default_rng(17 + d + page_size)
+    B, Hkv, G = (64, 8, 4) if d == 128 else (64, 4, 4)
+    S = 1100 if d == 128 else 1500
+    lay_c = kvq.make_layout(B, Hkv, Hkv * G, d, S, k_bits=kb, v_bits=4)
+    pps = -(-S // page_size)
+    lay = kvq.make_layout(B, Hkv, Hkv * G, d, pps * page_size, k_bits=kb, v_bits=4)
+    pl = plan(lay, "decode_paged", S)
+    say("paged deep", d, kb, page_size, pl)
+    assert pl["superblocks_per_wave"] >= 4 and pl == plan(lay_c, "decode", S)
+    kbytes, ks, vbytes, vs, lk, lv = _cache(rng, B, Hkv, S, d, kb, 4, K8 if kb == 8 else K4, V4)
+    q = synth.to_fp16(rng.standard_normal((B, Hkv * G, d)))
+    sk = synth.random_signs(5, d)
+    sv = synth.random_signs(6, d)
+    lens = _lengths(rng, B, S)
+    # pages: logical page p of sequence b lives at physical page perm[b * pps + p]
+    n_pages = B * pps
+    perm = rng.permutation(n_pages)
+    table = perm.reshape(B, pps).astype(np.int32)
+
+    def paged(a):
+        w = a.shape[-1]
+        pad = np.zeros((B, Hkv, pps * page_size - S, w), a.dtype)
+        nat = np.concatenate([a, pad], 2).reshape(B, Hkv, pps, page_size, w).transpose(0, 2, 1, 3, 4)
+        out = np.empty_like(nat.reshape(n_pages, Hkv, page_size, w))
+        out[perm] = nat.reshape(n_pages, Hkv, page_size, w)
+        return out
+
+    pages = tuple(paged(a) for a in (kbytes, ks, vbytes, vs))
+    units = _units(rng, B, Hkv, 16, lens)
+    got = _compare(lay, q, (kbytes, ks, vbytes, vs, lk, lv), S, lens, sk, sv, units, f"paged deep d{d}",
+                   page=(table, page_size, n_pages, pages))
+    ref = gpu_decode_planes(lay_c, q, kbytes, ks, vbytes, vs, S, lens, sk, sv, lk, lv, Hkv * d)
+    assert np.array_equal(got, ref), "paged output differs from the contiguous call"
+
+
+@pytest.mark.parametrize("d,kb", [(128, 4), (256, 8)])
+def test_append_deep(d, kb):
+    """Fused append with position L - 1 in a later superblock of its wave: the new token's bytes
+    meet the write path's bar, nothing else changes, the output matches the oracle over the planes
+    the call left."""
+    rng = np.random.default_rng(23 + d)
+    B, Hkv, G, S = (64, 8, 4, 1100) if d == 128 else (64, 4, 4, 1500)
+    lay = kvq.make_layout(B, Hkv, Hkv * G, d, S, k_bits=kb, v_bits=4)
+    pl = plan(lay, "decode_append", S)
+    say("append deep", d, kb, pl)
+    assert pl["superblocks_per_wave"] >= 4
+    kbytes, ks, vbytes, vs, lk, lv = _cache(rng, B, Hkv, S, d, kb, 4, K8 if kb == 8 else K4, V4)
+    q = synth.to_fp16(rng.standard_normal((B, Hkv * G, d)))
+    k_new = synth.to_fp16(rng.standard_normal((B, Hkv, d)) * 2)
+    v_new = synth.to_fp16(rng.standard_normal((B, Hkv, d)))
+    sk = synth.random_signs(7, d)
+    sv = synth.random_signs(8, d)
+    lens = _lengths(rng, B, S)
+    lens[10:20] = [S, 300, 600, 700, 1000, 767, 768, 769, 513, 1023][: min(10, B - 10)]
+    before = [a.copy() for a in (kbytes, ks, vbytes, vs)]
+    t = [dev(a) for a in (kbytes, ks.view(np.int16), vbytes, vs.view(np.int16))]
+    ws = torch.zeros(kvq.kvq_decode_attn_workspace_bytes(lay, S), dtype=torch.uint8, device="cuda")
+    out = torch.full((B, Hkv * G, d), float("nan"), dtype=torch.float32, device="cuda")
+    kvq.kvq_decode_attn_append(lay, dev(q), dev(k_new), dev(v_new), *t, S, dev(lens.astype(np.int32)), dev(sk),
+                               dev(sv), 0, dev(lk), dev(lv), Hkv * d, 0.0, ws, out)
+    torch.cuda.synchronize()
+    got = (t[0].cpu().numpy(), t[1].cpu().numpy().view(np.float16), t[2].cpu().numpy(),
+           t[3].cpu().numpy().view(np.float16))
+    out = out.cpu().numpy().astype(np.float64)
+    live = np.nonzero(lens >= 1)[0]
+    for g_, bf in zip(got, before):
+        chg = (g_.view(np.uint8) != bf.view(np.uint8)).any(axis=-1)  # [B, Hkv, S]
+        chg[live, :, lens[live] - 1] = False
+        assert not chg.any(), "bytes changed outside position L - 1"
+    sel = lambda a: np.stack([a[b][:, lens[b] - 1:lens[b]] for b in live])
+    uk = O.rotated_scaled(k_new[live][:, :, None, :], sk, lk[live][:, :, None, :])
+    uv = O.rotated_scaled(v_new[live][:, :, None, :], sv, lv[live][:, :, None, :])
+    check_quantize(sel(got[0]), sel(got[1]), uk, kb, label="deep append K")
+    check_quantize(sel(got[2]), sel(got[3]), uv, 4, label="deep append V")
+    worst = 0.0
+    for b, j in _units(rng, B, Hkv, 20, lens):
+        ref = oracle_unit(q[b, j * G:(j + 1) * G], got[0][b, j], got[1][b, j], got[2][b, j], got[3][b, j], kb, 4, sk,
+                          sv, lk[b, j], lv[b, j], int(lens[b]))
+        err = float(np.abs(out[b, j * G:(j + 1) * G] - ref).max())
+        worst = max(worst, err)
+        assert err <= ATTN_ATOL, f"unit ({b}, {j}) L={lens[b]}: {err:.3g}"
+    say("append deep worst", f"{worst:.3g}")
+
+
+@pytest.mark.parametrize("d,B,Hkv,G,S,min_sb,min_ch", [(128, 64, 8, 1, 1000, 8, 1), (256, 64, 4, 4, 2000, 16, 1),
+                                                       (128, 8, 4, 2, 8192, 4, 8)])
+def test_fp16_decode_deep(d, B, Hkv, G, S, min_sb, min_ch):
+    """The fp16 comparator over several 32-token superblocks per wave and several chunks."""
+    rng = np.random.default_rng(d + B + S)
+    lay = kvq.make_layout(B, Hkv, Hkv * G, d, S)
+    pl = plan(lay, "decode_fp16", S)
+    say("fp16 deep", (d, B, Hkv, G, S), pl)
+    assert pl["superblocks_per_wave"] >= min_sb and pl["n_chunks"] >= min_ch, pl
+    k = synth.to_fp16(rng.standard_normal((B, Hkv, S, d)) * 1.5)
+    v = synth.to_fp16(rng.standard_normal((B, Hkv, S, d)))
+    q = synth.to_fp16(rng.standard_normal((B, Hkv * G, d)))
+    lens = _lengths(rng, B, S)
+    ws = torch.zeros(kvq.kvq_decode_attn_workspace_bytes(lay, S), dtype=torch.uint8, device="cuda")
+    out = torch.full((B, Hkv * G, d), float("nan"), dtype=torch.float32, device="cuda")
+    kvq.kvq_decode_attn_fp16(lay, dev(q), dev(k), dev(v), S, dev(lens.astype(np.int32)), 0.0, ws, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    worst = 0.0
+    for b, j in _units(rng, B, Hkv, 20, lens):
+        hs = slice(j * G, (j + 1) * G)
+        L = int(lens[b])
+        ref = np.zeros((G, d)) if L == 0 else O.decode_attention(q[b:b + 1, hs], k[b:b + 1, j:j + 1],
+                                                                 v[b:b + 1, j:j + 1], L)[0]
+        err = float(np.abs(got[b, hs] - ref).max())
+        worst = max(worst, err)
+        assert err <= ATTN_ATOL, f"fp16 unit ({b}, {j}) L={L}: {err:.3g}"
+    say("fp16 deep worst", f"{worst:.3g}")
