@@ -329,13 +329,17 @@ def main():
         for i in range(20):
             decode(planes[i % len(planes)])
         torch.cuda.synchronize()
+        for i in range(20):
+            kvq.kvq_decode_attn_fp16(lay, q, kv16[i % len(kv16)][0], kv16[i % len(kv16)][1], S, None, 0.0, ws, out16)
+        torch.cuda.synchronize()
         src = torch.empty(PMC_COPY_BYTES, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         src.fill_(1)
         for _ in range(4):
             dst.copy_(src)
         torch.cuda.synchronize()
-        print(json.dumps({"pmc_run": w.name, "decode_launches": 20, "copy_bytes": PMC_COPY_BYTES,
+        print(json.dumps({"pmc_run": w.name, "decode_launches": 20, "fp16_decode_launches": 20,
+                          "copy_bytes": PMC_COPY_BYTES,
                           "decode_algorithmic_bytes": q_bytes, "decode_sources_sha": decode_sources_sha()}))
         return
 

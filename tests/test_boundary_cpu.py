@@ -285,3 +285,40 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     line = r.stdout.strip().splitlines()[-1]
     assert "one GPU" in line and line.startswith("{")
+
+
+def test_launch_plan_shapes(L):
+    """kvq_launch_plan describes the split the calls launch with (host only)."""
+    # serving shard folded into the batch: 2048 units cover the GPU, one chunk of 32768 tokens each
+    p = kvq.kvq_launch_plan(kvq.make_layout(256, 8, 32, 128, 32768), "decode", 32768)
+    assert (p.work_groups, p.head_tile, p.head_tiles, p.chunk, p.n_chunks) == (2048, 4, 1, 32768, 1)
+    assert (p.wave_tokens, p.superblocks_per_wave) == (64, 128)
+    # few units: the sequence is split into chunks, every chunk a multiple of 4 waves x 64 tokens
+    p = kvq.kvq_launch_plan(kvq.make_layout(1, 2, 12, 128, 4096), "decode", 4096)
+    assert p.head_tile == 6 and p.chunk % 256 == 0 and p.n_chunks * p.chunk >= 4096 and p.n_chunks > 1
+    # G above the largest head tile: several head tiles per kv head
+    p = kvq.kvq_launch_plan(kvq.make_layout(2, 2, 64, 128, 1000), "decode", 1000)
+    assert (p.head_tile, p.head_tiles) == (16, 2)
+    p = kvq.kvq_launch_plan(kvq.make_layout(2, 2, 64, 128, 1000), "decode_append", 1000)
+    assert p.head_tile * p.head_tiles == 32 and p.head_tile <= 14
+    # fp16 comparator: 32-token wave superblocks
+    p = kvq.kvq_launch_plan(kvq.make_layout(64, 8, 8, 128, 1000), "decode_fp16", 1000)
+    assert p.wave_tokens == 32 and p.superblocks_per_wave == p.chunk // 128
+    # write path: 16-vector blocks in contiguous ranges over at most 3 x 256 work-groups (d 128)
+    p = kvq.kvq_launch_plan(kvq.make_layout(3, 9, 9, 128, 5000), "quantize", 5000)
+    assert (p.work_groups, p.blocks) == (768, (3 * 9 * 5000 + 15) // 16)
+    assert p.blocks_per_work_group == -(-p.blocks // 768)
+    p = kvq.kvq_launch_plan(kvq.make_layout(1, 1, 1, 256, 40), "quantize", 40)
+    assert (p.work_groups, p.blocks, p.blocks_per_work_group) == (3, 3, 1)
+
+
+def test_launch_plan_errors(L):
+    out = kvq.kvq_plan()
+    lay = kvq.make_layout(2, 2, 12, 128, 64)
+    assert L.kvq_launch_plan(ctypes.byref(lay), 1, 65, ctypes.byref(out)) == 1   # seq_len > capacity
+    assert L.kvq_launch_plan(ctypes.byref(lay), 0, 0, ctypes.byref(out)) == 1    # n_tok < 1
+    assert L.kvq_launch_plan(ctypes.byref(lay), 9, 8, ctypes.byref(out)) == 1    # unknown call
+    assert L.kvq_launch_plan(ctypes.byref(lay), 1, 8, None) == 1
+    bad = kvq.make_layout(2, 2, 5, 128, 64)
+    assert L.kvq_launch_plan(ctypes.byref(bad), 1, 8, ctypes.byref(out)) == 1    # q_heads % kv_heads
+    assert L.kvq_launch_plan(ctypes.byref(kvq.make_layout(2, 2, 2, 96, 64)), 0, 8, ctypes.byref(out)) == 2
