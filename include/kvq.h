@@ -186,6 +186,30 @@ kvq_status kvq_decode_attn(const kvq_layout* layout, const void* q_f16, const vo
                            void* workspace, size_t workspace_bytes, float* out, void* stream);
 
 /*
+ * kvq_decode_attn_noalloc -- kvq_decode_attn without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the call makes no allocation of any kind.  Its completion counters and chunk
+ * partials live in a device array built into the library, 32 MiB (33554432 bytes) per GPU, held
+ * until the process ends; the first call on a device looks up that device's copy and clears its
+ * counters (a fill kernel on `stream`), and every call that runs to completion leaves them zero.
+ * All calls on one GPU share the array: calls whose execution overlaps on one GPU (different
+ * streams, or host threads) race and give wrong results; serialize them.  After a call that did not
+ * complete, the counters are stale and later calls of this entry point give wrong results.
+ * Computation, precision, plan and result are those of kvq_decode_attn (the same kernels).
+ * Arguments as kvq_decode_attn without workspace/workspace_bytes.
+ * Errors: those of kvq_decode_attn; KVQ_ERR_WORKSPACE_TOO_SMALL when the call would need more than
+ * the built-in 32 MiB (kvq_decode_attn_workspace_bytes(layout, seq_len) > 33554432, e.g. very many
+ * chunks of many units); KVQ_ERR_HIP if the scratch cannot be set up.
+ */
+kvq_status kvq_decode_attn_noalloc(const kvq_layout* layout, const void* q_f16, const void* k_codes,
+                                   const void* k_scales, const void* v_codes, const void* v_scales,
+                                   int32_t seq_len, const int32_t* seq_lens, const float* sign_k,
+                                   const float* sign_v, int64_t sign_batch_stride,
+                                   const float* lambda_k, const float* lambda_v,
+                                   int64_t lambda_batch_stride, float sm_scale, float* out,
+                                   void* stream);
+
+/*
  * kvq_decode_attn_append -- one decode step in one launch: the write path ([QF] Methodology 2,
  * the steps of the fused kernel) on the step's new K and V vectors, then kvq_decode_attn over
  * the cache that now holds them ([QF] Key results: one vector written per head and step, the

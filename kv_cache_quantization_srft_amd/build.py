@@ -23,7 +23,7 @@ OUT = os.path.join(PKG, "libkvq.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 SOURCES = ["kvq_dequant.hip", "kvq_quant.hip", "kvq_decode_q128.hip", "kvq_decode_q256.hip", "kvq_decode_f16.hip",
-           "kvq_plan.cpp", "kvq_api.cpp"]
+           "kvq_noalloc.hip", "kvq_plan.cpp", "kvq_api.cpp"]
 ARCH = "gfx950"
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

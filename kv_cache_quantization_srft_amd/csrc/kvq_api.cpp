@@ -99,9 +99,11 @@ kvq_status check_decode_group(const kvq_layout* L, const char* fn) {
   return KVQ_OK;
 }
 
+// workspace == nullptr with workspace_bytes == 0 and noalloc: the built-in scratch of the
+// allocation-free call, checked against its size instead
 kvq_status check_decode_common(const kvq_layout* L, const void* q, int32_t seq_len, const int32_t* seq_lens,
                                float sm_scale, void* workspace, size_t workspace_bytes, float* out,
-                               const char* fn, bool append = false) {
+                               const char* fn, bool append = false, bool noalloc = false) {
   if (L->q_heads < 1 || L->q_heads % L->kv_heads != 0)
     return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: q_heads (%d) must be a positive multiple of kv_heads (%d)", fn,
                 L->q_heads, L->kv_heads);
@@ -121,8 +123,16 @@ kvq_status check_decode_common(const kvq_layout* L, const void* q, int32_t seq_l
       return fail(KVQ_ERR_UNSUPPORTED, "%s: batch x kv_heads x head tiles = %ld exceeds %d", fn, units,
                   kvq_impl::kMaxDecodeUnits);
   }
-  KVQ_TRY(check_ptr(workspace, 256, fn, "workspace"));
   const size_t need = kvq_impl::decode_workspace_bytes(L->batch, L->kv_heads, L->q_heads, L->head_dim, seq_len);
+  if (noalloc) {
+    if (need > kvq_impl::kNoAllocScratchBytes)
+      return fail(KVQ_ERR_WORKSPACE_TOO_SMALL,
+                  "%s: the call needs %zu bytes of scratch, the built-in scratch holds %zu (use kvq_decode_attn "
+                  "with a caller workspace)",
+                  fn, need, kvq_impl::kNoAllocScratchBytes);
+    return KVQ_OK;
+  }
+  KVQ_TRY(check_ptr(workspace, 256, fn, "workspace"));
   if (workspace_bytes < need)
     return fail(KVQ_ERR_WORKSPACE_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need);
   return KVQ_OK;
@@ -252,6 +262,40 @@ kvq_status kvq_decode_attn(const kvq_layout* L, const void* q_f16, const void* k
                          L->capacity, seq_len,    seq_lens,   q_f16,       k_codes,     k_scales,
                          v_codes,    v_scales,    sign_k,     sign_v,      sign_batch_stride, lambda_k,
                          lambda_v,   lambda_batch_stride,     scale,       workspace,   out};
+  a.transform = L->transform;
+  return hip_status(kvq_impl::launch_decode(a, p, static_cast<hipStream_t>(stream)), fn);
+}
+
+kvq_status kvq_decode_attn_noalloc(const kvq_layout* L, const void* q_f16, const void* k_codes,
+                                   const void* k_scales, const void* v_codes, const void* v_scales, int32_t seq_len,
+                                   const int32_t* seq_lens, const float* sign_k, const float* sign_v,
+                                   int64_t sign_batch_stride, const float* lambda_k, const float* lambda_v,
+                                   int64_t lambda_batch_stride, float sm_scale, float* out, void* stream) {
+  const char* fn = "kvq_decode_attn_noalloc";
+  KVQ_TRY(check_layout(L, fn));
+  KVQ_TRY(check_bits(L->k_bits, fn, "k_bits"));
+  KVQ_TRY(check_bits(L->v_bits, fn, "v_bits"));
+  KVQ_TRY(check_decode_group(L, fn));
+  KVQ_TRY(check_decode_common(L, q_f16, seq_len, seq_lens, sm_scale, nullptr, 0, out, fn, false, true));
+  KVQ_TRY(check_ptr(k_codes, 16, fn, "k_codes"));
+  KVQ_TRY(check_ptr(k_scales, 16, fn, "k_scales"));
+  KVQ_TRY(check_ptr(v_codes, 16, fn, "v_codes"));
+  KVQ_TRY(check_ptr(v_scales, 16, fn, "v_scales"));
+  KVQ_TRY(check_ptr(sign_k, 4, fn, "sign_k"));
+  KVQ_TRY(check_ptr(sign_v, 4, fn, "sign_v"));
+  KVQ_TRY(check_opt_ptr(lambda_k, 4, fn, "lambda_k"));
+  KVQ_TRY(check_opt_ptr(lambda_v, 4, fn, "lambda_v"));
+  KVQ_TRY(check_strides(sign_batch_stride, lambda_batch_stride, fn));
+  void* ws = nullptr;
+  const hipError_t e = kvq_impl::noalloc_scratch(static_cast<hipStream_t>(stream), &ws);
+  if (e != hipSuccess) return fail(KVQ_ERR_HIP, "%s: scratch set-up: %s", fn, hipGetErrorString(e));
+  const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt(float(L->head_dim));
+  const kvq_impl::DecodePlan p =
+      kvq_impl::plan_decode(L->batch, L->kv_heads, L->q_heads, L->head_dim, seq_len, seq_len, false);
+  kvq_impl::DecodeArgs a{L->batch,   L->kv_heads, L->q_heads, L->head_dim, L->k_bits,   L->v_bits,
+                         L->capacity, seq_len,    seq_lens,   q_f16,       k_codes,     k_scales,
+                         v_codes,    v_scales,    sign_k,     sign_v,      sign_batch_stride, lambda_k,
+                         lambda_v,   lambda_batch_stride,     scale,       ws,          out};
   a.transform = L->transform;
   return hip_status(kvq_impl::launch_decode(a, p, static_cast<hipStream_t>(stream)), fn);
 }

@@ -102,6 +102,11 @@ struct DecodeF16Args {
 constexpr int kMaxDecodeUnits = 16384;
 constexpr size_t kDecodeCounterBytes = size_t(kMaxDecodeUnits) * sizeof(uint32_t);
 
+// Workspace of the allocation-free decode (kvq_decode_attn_noalloc): a device array of this
+// many bytes per GPU, resolved on the first call on each device.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+hipError_t noalloc_scratch(hipStream_t stream, void** out);
+
 struct WsLayout {
   size_t counters;  // uint32 per unit
   size_t pml;       // per (unit, head, chunk): m, l

@@ -23,7 +23,7 @@ EXPORTS = (
     "kvq_version", "kvq_status_string", "kvq_last_error_message", "kvq_codes_bytes", "kvq_scales_bytes",
     "kvq_quantize", "kvq_dequantize", "kvq_calibrate_lambda", "kvq_decode_attn_workspace_bytes",
     "kvq_decode_attn", "kvq_decode_attn_append", "kvq_decode_attn_paged", "kvq_decode_attn_fp16",
-    "kvq_launch_plan",
+    "kvq_launch_plan", "kvq_decode_attn_noalloc",
 )
 
 
@@ -102,6 +102,9 @@ def lib() -> ctypes.CDLL:
                                             _P, _I64, _P, _P, _I64, ctypes.c_float, _P, _SZ, _P, _P]
         L.kvq_decode_attn_fp16.restype = ctypes.c_int
         L.kvq_decode_attn_fp16.argtypes = [_LP, _P, _P, _P, _I32, _P, ctypes.c_float, _P, _SZ, _P, _P]
+        L.kvq_decode_attn_noalloc.restype = ctypes.c_int
+        L.kvq_decode_attn_noalloc.argtypes = [_LP, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _I64, _P, _P, _I64,
+                                              ctypes.c_float, _P, _P]
         L.kvq_launch_plan.restype = ctypes.c_int
         L.kvq_launch_plan.argtypes = [_LP, ctypes.c_int, _I32, ctypes.POINTER(kvq_plan)]
         _lib = L
@@ -220,6 +223,22 @@ def kvq_decode_attn(layout, q, k_codes, k_scales, v_codes, v_scales, seq_len, se
         _ptr(sign_v, _f32(), "sign_v"), sign_batch_stride, _ptr(lambda_k, _f32(), "lambda_k"),
         _ptr(lambda_v, _f32(), "lambda_v"), lambda_batch_stride, float(sm_scale),
         _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(out, _f32(), "out", layout.batch * layout.q_heads * d), _stream(stream)))
+
+
+def kvq_decode_attn_noalloc(layout, q, k_codes, k_scales, v_codes, v_scales, seq_len, seq_lens, sign_k, sign_v,
+                            sign_batch_stride, lambda_k, lambda_v, lambda_batch_stride, sm_scale, out, stream=None):
+    import torch
+    d = layout.head_dim
+    _check(lib().kvq_decode_attn_noalloc(
+        ctypes.byref(layout), _ptr(q, _f16(), "q", layout.batch * layout.q_heads * d),
+        _ptr(k_codes, _u8(), "k_codes", min_bytes=kvq_codes_bytes(layout, layout.k_bits)),
+        _ptr(k_scales, _scale_t(), "k_scales", min_bytes=kvq_scales_bytes(layout)),
+        _ptr(v_codes, _u8(), "v_codes", min_bytes=kvq_codes_bytes(layout, layout.v_bits)),
+        _ptr(v_scales, _scale_t(), "v_scales", min_bytes=kvq_scales_bytes(layout)), seq_len,
+        _ptr(seq_lens, torch.int32, "seq_lens", layout.batch), _ptr(sign_k, _f32(), "sign_k"),
+        _ptr(sign_v, _f32(), "sign_v"), sign_batch_stride, _ptr(lambda_k, _f32(), "lambda_k"),
+        _ptr(lambda_v, _f32(), "lambda_v"), lambda_batch_stride, float(sm_scale),
         _ptr(out, _f32(), "out", layout.batch * layout.q_heads * d), _stream(stream)))
 
 
