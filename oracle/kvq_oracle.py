@@ -41,6 +41,17 @@ Readings taken where the pages are silent (each also listed in the design notes)
       SRHT): SRHT(x) = d^-1/2 H_d diag(s) x with H_d the Sylvester-ordered Walsh-Hadamard
       matrix, H[i][j] = (-1)^popcount(i & j); everything downstream (lambda, quantizer,
       decode) is unchanged.  Functions take transform="srft" (default) or "srht".
+  R14 Several query tokens per sequence (chunked prefill, speculative verification; [GM]
+      "Flash Attention 与 Metal 内核融合"): the T new tokens are the last T positions of the
+      cache (already written); query i of a sequence of length L sits at position
+      p = L - T + i and attends causally, positions t <= p.  A query whose position would be
+      negative (L < T) has a zero output.
+  R15 Sliding window ([GM] "KV 缓存分片与内存管理": keep the latest tokens): with a window W >= 1
+      a query at position p attends the W most recent positions up to its own, t in
+      [max(0, p - W + 1), p]; W = 0 means no window.
+  R16 Ring buffer: logical position t of a row is stored at plane slot t mod capacity.  This is a
+      storage convention only; attention is defined on logical positions (tests lay the planes
+      out from the logical rows).
 """
 from __future__ import annotations
 
@@ -292,6 +303,52 @@ def decode_attention_quantized(q16, k_codes, k_scales, v_codes, v_scales, s_k, s
     k_hat = dequantize(k_codes, k_scales, s_k, lam_k, transform=transform)
     v_hat = dequantize(v_codes, v_scales, s_v, lam_v, transform=transform)
     return decode_attention(np.asarray(q16).astype(np.float64), k_hat, v_hat, seq_lens, sm_scale)
+
+
+def prefix_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_lens, n_query: int, window: int = 0,
+                     sm_scale=None):
+    """Attention of the last n_query positions of every sequence over its cache (readings R14,
+    R15), float64, by definition with explicit loops over sequences, query tokens and heads.
+
+    q: [B, T, Hq, d] (T = n_query); k, v: [B, Hkv, >= max(seq_lens), d] in the original domain.
+    Query i of sequence b (length L) sits at p = L - T + i and attends positions
+    t in [lo, p] with lo = max(0, p - window + 1) if window >= 1 else 0; p < 0 gives zeros.
+    Query head h reads kv head h // (Hq // Hkv).  Returns o: [B, T, Hq, d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, T, Hq, d = q.shape
+    assert T == n_query
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(d)
+    lens = np.broadcast_to(np.asarray(seq_lens), (B,))
+    o = np.zeros((B, T, Hq, d))
+    for b in range(B):
+        L = int(lens[b])
+        for i in range(T):
+            p = L - T + i
+            if p < 0:
+                continue
+            lo = max(0, p - window + 1) if window >= 1 else 0
+            for h in range(Hq):
+                j = h // G
+                logits = sm_scale * (k[b, j, lo:p + 1] @ q[b, i, h])
+                w = np.exp(logits - logits.max())
+                w /= w.sum()
+                o[b, i, h] = w @ v[b, j, lo:p + 1]
+    return o
+
+
+def prefix_attention_quantized(q16, k_codes, k_scales, v_codes, v_scales, s_k, s_v, lam_k, lam_v, seq_lens,
+                               n_query: int, window: int = 0, sm_scale=None, transform: str = "srft"):
+    """prefix_attention over a quantized cache: dequantize every K/V vector, then attend
+    (codes unpacked int8 [B, Hkv, S, d], scales float16 [B, Hkv, S, d/16])."""
+    k_hat = dequantize(k_codes, k_scales, s_k, lam_k, transform=transform)
+    v_hat = dequantize(v_codes, v_scales, s_v, lam_v, transform=transform)
+    return prefix_attention(np.asarray(q16).astype(np.float64), k_hat, v_hat, seq_lens, n_query, window, sm_scale)
 
 
 # ----------------------------------------------------------------------------------------
