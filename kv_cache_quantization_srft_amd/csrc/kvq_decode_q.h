@@ -64,7 +64,7 @@ struct QGeom {
   static constexpr int LDS_V = kSB * VRB;
   static constexpr int LDS_S = NG * kSB * 2;
   static constexpr int LDS_K = kSB * NG * 2;
-  static constexpr int LDS_P = 16 * kSB * 4;
+  static constexpr int LDS_P = 32 * kSB * 2;  // p as fp16 hi and lo parts, 16 heads each
   static constexpr int LDS_WAVE = LDS_V + LDS_S + LDS_K + LDS_P + 16 * 4;
   static constexpr int LDS_EPI = (kWaves * 16 * 2 + 16 * kWaves + 32 + kWaves * (D == 128 ? 16 : 8) * D) * 4;
   static constexpr int LDS_Q = 4 * NS * 3 * 1024 + 256;  // prologue: digit operands + head maxima
@@ -80,16 +80,25 @@ __device__ __forceinline__ v4i widen_int4(uint32_t w0, uint32_t w1) {
              int(w1 & 0xf0f0f0f0u)};
 }
 
-// 8 nibbles (tokens r = 0..7 of one channel) -> 4 fp16 pairs of code values,
-// pairs hold tokens (0,4), (1,5), (2,6), (3,7).  mask = 0x000f000f and magic = 0x64006400 come
-// in VGPRs so that the extraction is one v_and_or_b32 per pair (VOP3 takes no literals here).
-__device__ __forceinline__ void nibbles_to_half_pairs(uint32_t x, uint32_t mask, uint32_t magic, uint32_t (&p)[4]) {
-  x ^= 0x88888888u;  // offset binary: nibble = code + 8
-  const v2h off = {static_cast<_Float16>(-1032.0f), static_cast<_Float16>(-1032.0f)};
+// 8 nibbles (tokens r = 0..7 of one channel) -> 4 fp16 pairs of code / 16, pairs holding tokens
+// (0,4), (1,5), (2,6), (3,7).  After the offset-binary flip (nibble n = code + 8), nibbles 0 and 4
+// sit in mantissa bits 0-3 of the two halves (magic 0x6400: 1024 + n) and nibbles 1 and 5 in bits
+// 4-7 (1024 + 16 n); one shift by 8 brings nibbles 2, 6 and 3, 7 to the same places.  One packed
+// FMA per pair then gives code / 16 exactly: (1024 + n) / 16 - 64.5 and (1024 + 16 n) / 256 - 4.5.
+// The masks and the magic come in VGPRs (VOP3 takes no literal here), so each pair costs one
+// v_and_or_b32 and one v_pk_fma_f16.
+__device__ __forceinline__ void nibbles_to_half16(uint32_t x, uint32_t m_lo, uint32_t m_hi, uint32_t magic,
+                                                  uint32_t (&p)[4]) {
+  x ^= 0x88888888u;
+  const uint32_t y = x >> 8;
+  const v2h f_lo = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
+  const v2h o_lo = {static_cast<_Float16>(-64.5f), static_cast<_Float16>(-64.5f)};
+  const v2h f_hi = {static_cast<_Float16>(0.00390625f), static_cast<_Float16>(0.00390625f)};
+  const v2h o_hi = {static_cast<_Float16>(-4.5f), static_cast<_Float16>(-4.5f)};
+  const uint32_t t[4] = {(x & m_lo) | magic, (x & m_hi) | magic, (y & m_lo) | magic, (y & m_hi) | magic};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t t = ((x >> (4 * i)) & mask) | magic;  // halves 1024 + code + 8
-    const v2h c = __builtin_bit_cast(v2h, t) + off;
+    const v2h c = __builtin_elementwise_fma(__builtin_bit_cast(v2h, t[i]), (i & 1) ? f_hi : f_lo, (i & 1) ? o_hi : o_lo);
     p[i] = __builtin_bit_cast(uint32_t, c);
   }
 }
@@ -231,15 +240,28 @@ __host__ __device__ constexpr int kinv16(int p) {
   return (p < 8 ? 0 : 8) + ((p & 7) % 2 == 0 ? (p & 7) / 2 : (p & 7) / 2 + 4);
 }
 
+// One value MFMA step: acc += P * B for B = code * scale split into fp16 hi + lo.
+//   TWO (head tile <= 8): the A rows are (head, part) -- rows 0-7 the hi parts of p of heads 0-7,
+//       rows 8-15 the lo parts -- so two products (A b_hi, A b_lo) cover hi*hi, lo*hi, hi*lo (and
+//       the negligible lo*lo); the hi and lo rows of a head are added once, at the chunk's end.
+//   otherwise the rows are heads: three products (a_hi b_hi, a_hi b_lo, a_lo b_hi).
+template <bool TWO>
+__device__ __forceinline__ v4f value_mfma(const v8h& a0, const v8h& a1, const v8h& b_hi, const v8h& b_lo, v4f acc) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b_hi, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b_lo, acc, 0, 0, 0);
+  if constexpr (!TWO) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b_hi, acc, 0, 0, 0);
+  return acc;
+}
+
 // Value accumulation over int8 V codes staged in LDS (rows swizzled as in the staging).
 // ds_read_b64_tr_b8 hands lane c + 8 h of each 16-lane group byte c of the rows that lanes
 // 2 j + h supplied, j = 0..7; so lane 2 j + h points at channel half h of group g of the token
 // in k slot j, and lane n16 receives channel n16 of the 8 tokens of its k slots.  Bytes become
 // fp16 pairs with one v_perm_b32 (exponent byte 0x64 beside each offset-binary code) and one
 // packed add; B = code * (staged scale) split exactly into fp16 hi + lo.
-template <int D, int KB, int VB>
-__device__ __forceinline__ void values_int8(int lane, const v8h (&a_hi)[2], const v8h (&a_lo)[2],
-                                            v4f (&acc)[D / 16], const uint8_t* vtile, const uint16_t* stile) {
+template <int D, int KB, int VB, bool TWO>
+__device__ __forceinline__ void values_int8(int lane, const v8h (&a0)[2], const v8h (&a1)[2], v4f (&acc)[D / 16],
+                                            const uint8_t* vtile, const uint16_t* stile) {
   using Gm = QGeom<D, KB, VB>;
   constexpr int NG = Gm::NG;
   const int n16 = lane & 15, r4 = lane >> 4;
@@ -272,30 +294,50 @@ __device__ __forceinline__ void values_int8(int lane, const v8h (&a_hi)[2], cons
         bh[i] = __builtin_bit_cast(uint32_t, hi);
         bl[i] = __builtin_bit_cast(uint32_t, lo);
       }
-      const v8h b_hi = as_v8h(bh[0], bh[1], bh[2], bh[3]);
-      const v8h b_lo = as_v8h(bl[0], bl[1], bl[2], bl[3]);
-      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[hblk], b_hi, acc[g], 0, 0, 0);
-      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[hblk], b_lo, acc[g], 0, 0, 0);
-      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo[hblk], b_hi, acc[g], 0, 0, 0);
+      acc[g] = value_mfma<TWO>(a0[hblk], a1[hblk], as_v8h(bh[0], bh[1], bh[2], bh[3]), as_v8h(bl[0], bl[1], bl[2], bl[3]),
+                               acc[g]);
     }
   }
 }
 
+// Sum over the four 16-lane rows for every lane position (v_permlane32_swap, v_permlane16_swap).
+__device__ __forceinline__ float rows_sum4(float a) {
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  a = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  return __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+}
+
+// 65536 hi + 256 mid + lo of three exact int32 digit dots, as two v_lshl_add_u32 (the empty asm
+// keeps the compiler from reassociating it into two shifts and an add3)
+__device__ __forceinline__ int digit_dot(int hi, int mid, int lo) {
+  uint32_t t = (uint32_t(hi) << 8) + uint32_t(mid);
+  asm volatile("" : "+v"(t));
+  return int((t << 8) + uint32_t(lo));
+}
+
 // Everything one wave does with one superblock already in registers.
-template <int D, int KB, int VB, int NRB>
+//   aop: score MFMA A operands.  G1 (head tile 1): one operand per step s whose rows are
+//        (group slot, digit): the three digits of the query, so one MFMA gives every digit's dot
+//        of four groups and the lanes of a slot combine them.  Otherwise aop[rb][s][digit] with
+//        rows (head, group slot).
+//   ptile: p of the superblock as fp16 hi and lo parts, row part * 16 + head, 64 tokens in the
+//        value MFMA's k order.
+template <int D, int KB, int VB, int NRB, bool G1>
 __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int base, int t_end, int lane,
-                                                   const v4i (&aop)[NRB][D / 64][3], const float (&sig)[NRB],
-                                                   float (&m_run)[NRB], float (&l_run)[NRB], v4f (&acc)[D / 16],
-                                                   uint8_t* vtile, uint16_t* stile, uint16_t* ktile, float* ptile,
-                                                   float* atile, const uint8_t* __restrict__ kc,
-                                                   const uint16_t* __restrict__ ks, const uint8_t* __restrict__ vc,
-                                                   const uint16_t* __restrict__ vs, int next_base, int64_t next_t0,
-                                                   int next_nrem) {
+                                                   const v4i (&aop)[G1 ? 1 : NRB][D / 64][G1 ? 1 : 3],
+                                                   const float (&sig)[NRB], float (&m_run)[NRB], float (&l_run)[NRB],
+                                                   v4f (&acc)[D / 16], uint8_t* vtile, uint16_t* stile,
+                                                   uint16_t* ktile, uint16_t* ptile, float* atile,
+                                                   const uint8_t* __restrict__ kc, const uint16_t* __restrict__ ks,
+                                                   const uint8_t* __restrict__ vc, const uint16_t* __restrict__ vs,
+                                                   int next_base, int64_t next_t0, int next_nrem) {
   using Gm = QGeom<D, KB, VB>;
   constexpr int NS = Gm::NS, NG = Gm::NG;
+  constexpr bool TWO = NRB <= 2;
   const int n16 = lane & 15, r4 = lane >> 4;
 
-  // ---------------- stage V codes, V scales (k order, pre-scaled) and K scales in LDS ----------------
+  // ---------------- stage V codes, V scales (k order) and K scales in LDS ----------------
   bool vbig = false;
   if constexpr (VB == 8) {
     uint32_t mx = 0;
@@ -303,7 +345,6 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int bas
     for (int i = 0; i < Gm::SLW; ++i) mx = max(mx, max(r.vsw[i] & 0x7fffu, (r.vsw[i] >> 16) & 0x7fffu));
     vbig = __builtin_amdgcn_ballot_w64(mx > 0x6000u) != 0ull;  // 0x6000 = 512 in fp16
   }
-  const float vpre = VB == 4 ? 0.0625f : (vbig ? 0.0078125f : 1.0f);
 #pragma unroll
   for (int i = 0; i < Gm::VLU; ++i) {
     const int u = i * 64 + lane;  // 16-byte unit of the superblock, token-major
@@ -318,20 +359,25 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int bas
     }
   }
   {
-    // int4: scale / 16 keeps code * scale inside the fp16 range (undone by the merge).  int8:
-    // the scale as it is (scales of calibrated values are small, and a pre-factor would push
-    // them into fp16 subnormals), unless a scale of this superblock exceeds 512, where
-    // code * scale could overflow: then B takes scale / 128 and A takes p * 128.  No mask is
-    // needed: a superblock never crosses a chunk end (chunks are whole multiples of the
-    // work-group stride), so its tokens past t_end are past the row end, where the loads
-    // returned zero.  (Kept in float: a packed-half multiply here was miscompiled, both
+    // V scales, transposed to [group][k order].  int4: the scale as stored (the codes come out of
+    // the conversion as code / 16, which keeps code * scale inside the fp16 range; the merge undoes
+    // the 1/16).  int8: the scale as it is (scales of calibrated values are small, and a
+    // pre-factor would push them into fp16 subnormals), unless a scale of this superblock exceeds
+    // 512, where code * scale could overflow: then B takes scale / 128 and A takes p * 128.  No
+    // mask is needed: a superblock never crosses a chunk end (chunks are whole multiples of the
+    // work-group stride), so its tokens past t_end are past the row end, where the loads returned
+    // zero.  (The int8 factor stays in float: a packed-half multiply here was miscompiled, both
     // halves stored from the low-half product.)
     const int pos = 16 * (lane >> 4) + kpos16(lane & 15);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const uint32_t bits = (r.vsw[g >> 1] >> (16 * (g & 1))) & 0xffffu;
-      const float sv = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(bits))) * vpre;
-      stile[g * kSB + pos] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(sv));
+      if constexpr (VB == 4) {
+        stile[g * kSB + pos] = uint16_t(bits);
+      } else {
+        const float sv = static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(bits))) * (vbig ? 0.0078125f : 1.0f);
+        stile[g * kSB + pos] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(sv));
+      }
     }
     uint32_t* kt = reinterpret_cast<uint32_t*>(ktile + lane * NG);
 #pragma unroll
@@ -343,6 +389,9 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int bas
   wave_sync_lds();
 
   // ---------------- scores (int8 MFMA, exact integer group dots) ----------------
+  // A group dot of the 21-bit (int8 keys: 20-bit) query digits, hi * 65536 + mid * 256 + lo, is
+  // exact in int32 (|hi| <= 16, or 8; 16 channels of codes up to 112 = 16 * 7, or 127).
+  const bool tail = base + kSB > t_end;  // wave-uniform: only the last superblock has masked tokens
   float sc[4][NRB];
 #pragma unroll
   for (int sb = 0; sb < 4; ++sb) {
@@ -355,68 +404,102 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int bas
         bop[s] = v4i{int(r.kw[sb][4 * s]), int(r.kw[sb][4 * s + 1]), int(r.kw[sb][4 * s + 2]),
                      int(r.kw[sb][4 * s + 3])};
     }
-    uint32_t kraw[Gm::SLW];
-    {
-      const uint32_t* kt = reinterpret_cast<const uint32_t*>(ktile + (16 * sb + n16) * NG);
-#pragma unroll
-      for (int i = 0; i < Gm::SLW; i += 4) {
-        const uint4 v = *reinterpret_cast<const uint4*>(kt + i);
-        kraw[i] = v.x;
-        kraw[i + 1] = v.y;
-        kraw[i + 2] = v.z;
-        kraw[i + 3] = v.w;
+    const v4i zero = {0, 0, 0, 0};
+    if constexpr (G1) {
+      // lane (token n16, slot r4): the scales of groups r4 * NS + s, s = 0..NS-1, are adjacent
+      const uint16_t* kt = ktile + (16 * sb + n16) * NG + r4 * NS;
+      uint32_t kr[(NS + 1) / 2];
+      if constexpr (NS == 2) {
+        kr[0] = *reinterpret_cast<const uint32_t*>(kt);
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(kt);
+        kr[0] = v.x;
+        kr[1] = v.y;
       }
-    }
-    // the fp16 group scales stay packed; the FMA takes them as fp16 operands (v_fma_mix_f32)
-    const bool valid = base + 16 * sb + n16 < t_end;
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
       float s_acc = 0.0f;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const v4i zero = {0, 0, 0, 0};
-        const v4i chi = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[rb][s][0], bop[s], zero, 0, 0, 0);
-        const v4i cmi = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[rb][s][1], bop[s], zero, 0, 0, 0);
-        const v4i clo = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[rb][s][2], bop[s], zero, 0, 0, 0);
+        const v4i c = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[0][s][0], bop[s], zero, 0, 0, 0);
+        const int dot = digit_dot(c[0], c[1], c[2]);
+        s_acc = (s & 1) ? fma_mix_f16<1>(static_cast<float>(dot), kr[s >> 1], s_acc)
+                        : fma_mix_f16<0>(static_cast<float>(dot), kr[s >> 1], s_acc);
+      }
+      s_acc = rows_sum4(s_acc) * sig[0];
+      sc[sb][0] = (tail && base + 16 * sb + n16 >= t_end) ? -INFINITY : s_acc;
+    } else {
+      uint32_t kraw[Gm::SLW];
+      {
+        const uint32_t* kt = reinterpret_cast<const uint32_t*>(ktile + (16 * sb + n16) * NG);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // 256 hi + mid exactly in int32 (|.| < 2^26), the lo digit's dot added in fp32
-          const int dot = chi[i] * 256 + cmi[i];
-          const float f = fmaf(static_cast<float>(clo[i]), 1.0f / 256.0f, static_cast<float>(dot));
-          const int gi = i * NS + s;
-          s_acc = (gi & 1) ? fma_mix_f16<1>(f, kraw[gi >> 1], s_acc) : fma_mix_f16<0>(f, kraw[gi >> 1], s_acc);
+        for (int i = 0; i < Gm::SLW; i += 4) {
+          const uint4 v = *reinterpret_cast<const uint4*>(kt + i);
+          kraw[i] = v.x;
+          kraw[i + 1] = v.y;
+          kraw[i + 2] = v.z;
+          kraw[i + 3] = v.w;
         }
       }
-      sc[sb][rb] = valid ? s_acc * sig[rb] : -INFINITY;
+      // the fp16 group scales stay packed; the FMA takes them as fp16 operands (v_fma_mix_f32)
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        float s_acc = 0.0f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const v4i chi = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[rb][s][0], bop[s], zero, 0, 0, 0);
+          const v4i cmi = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[rb][s][1], bop[s], zero, 0, 0, 0);
+          const v4i clo = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop[rb][s][2], bop[s], zero, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int dot = digit_dot(chi[i], cmi[i], clo[i]);
+            const int gi = i * NS + s;
+            s_acc = (gi & 1) ? fma_mix_f16<1>(static_cast<float>(dot), kraw[gi >> 1], s_acc)
+                             : fma_mix_f16<0>(static_cast<float>(dot), kraw[gi >> 1], s_acc);
+          }
+        }
+        s_acc *= sig[rb];
+        sc[sb][rb] = (tail && base + 16 * sb + n16 >= t_end) ? -INFINITY : s_acc;
+      }
     }
   }
 
   // the K codes of this superblock are consumed: the next one's load during softmax + values
   if (next_base < t_end) load_sb_kcodes<D, KB, VB>(r, kc, next_t0, next_nrem, lane);
 
-  // ---------------- online softmax per head (16-lane rows) ----------------
+  // ---------------- online softmax per head (16-lane rows); p as fp16 hi + lo in LDS ----------------
+  // The running maximum of a head is finite after its first superblock (every superblock holds a
+  // valid token of its chunk), so exp2 needs no guard: exp2(-inf) = 0.
   bool rescale = false;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     float mb = fmaxf(fmaxf(sc[0][rb], sc[1][rb]), fmaxf(sc[2][rb], sc[3][rb]));
     mb = row_max16(mb);
     const float mn = fmaxf(m_run[rb], mb);
-    const float alpha = exp2_guard(m_run[rb], mn);
+    const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - mn);
     rescale |= mn != m_run[rb];
     m_run[rb] = mn;
-    float psum = 0.0f;
+    float p[4];
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-      const float p = exp2_guard(sc[sb][rb], mn);
-      psum += p;
-      ptile[(4 * rb + r4) * kSB + 16 * sb + kpos16(n16)] = p;
+    for (int sb = 0; sb < 4; ++sb) p[sb] = __builtin_amdgcn_exp2f(sc[sb][rb] - mn);
+    l_run[rb] = l_run[rb] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    const int head = 4 * rb + r4;
+    uint16_t* prow = ptile + head * kSB + kpos16(n16);
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const auto hi = __builtin_amdgcn_cvt_pkrtz(p[2 * q2], p[2 * q2 + 1]);
+      const auto lo = __builtin_amdgcn_cvt_pkrtz(p[2 * q2] - static_cast<float>(hi[0]),
+                                                 p[2 * q2 + 1] - static_cast<float>(hi[1]));
+      const uint32_t hb = __builtin_bit_cast(uint32_t, hi), lb = __builtin_bit_cast(uint32_t, lo);
+      prow[16 * (2 * q2)] = uint16_t(hb);
+      prow[16 * (2 * q2 + 1)] = uint16_t(hb >> 16);
+      prow[16 * kSB + 16 * (2 * q2)] = uint16_t(lb);
+      prow[16 * kSB + 16 * (2 * q2 + 1)] = uint16_t(lb >> 16);
     }
-    l_run[rb] = l_run[rb] * alpha + psum;
-    if (n16 == 0) atile[4 * rb + r4] = alpha;
+    if (n16 == 0) atile[head] = alpha;
   }
   wave_sync_lds();
   if (__builtin_amdgcn_ballot_w64(rescale) != 0ull) {
-    const float4 al = *reinterpret_cast<const float4*>(atile + 4 * r4);
+    // acc rows: heads 4 r4 + i, or with TWO (head, part) rows, heads 4 (r4 & 1) + i
+    const float4 al = *reinterpret_cast<const float4*>(atile + 4 * (TWO ? (r4 & 1) : r4));
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       acc[g][0] *= al.x;
@@ -426,38 +509,43 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int bas
     }
   }
 
-  // ---------------- A operands: p of head n16 for tokens 16*r4 + (0..15), hi + lo ----------------
-  uint32_t ahi[2][4], alo[2][4];
+  // ---------------- A operands from the staged p parts, tokens 16 r4 + (0..15) ----------------
+  v8h a0[2], a1[2];
   {
-    const float* pr = ptile + n16 * kSB + 16 * r4;
-    const float pa = vbig ? 128.0f : 1.0f;
+    const int row0 = TWO ? (n16 >> 3) * 16 + (n16 & 7) : n16;
 #pragma unroll
     for (int hblk = 0; hblk < 2; ++hblk) {
-      float4 p0 = *reinterpret_cast<const float4*>(pr + 8 * hblk);
-      float4 p1 = *reinterpret_cast<const float4*>(pr + 8 * hblk + 4);
-      if constexpr (VB == 8) {
-        p0 = make_float4(p0.x * pa, p0.y * pa, p0.z * pa, p0.w * pa);
-        p1 = make_float4(p1.x * pa, p1.y * pa, p1.z * pa, p1.w * pa);
+      const uint4 x = *reinterpret_cast<const uint4*>(ptile + row0 * kSB + 16 * r4 + 8 * hblk);
+      a0[hblk] = as_v8h(x.x, x.y, x.z, x.w);
+      if constexpr (!TWO) {
+        const uint4 y = *reinterpret_cast<const uint4*>(ptile + (16 + n16) * kSB + 16 * r4 + 8 * hblk);
+        a1[hblk] = as_v8h(y.x, y.y, y.z, y.w);
+      } else {
+        a1[hblk] = a0[hblk];
       }
-      split_pair(p0.x, p0.y, ahi[hblk][0], alo[hblk][0]);
-      split_pair(p0.z, p0.w, ahi[hblk][1], alo[hblk][1]);
-      split_pair(p1.x, p1.y, ahi[hblk][2], alo[hblk][2]);
-      split_pair(p1.z, p1.w, ahi[hblk][3], alo[hblk][3]);
+    }
+    if constexpr (VB == 8) {
+      if (vbig) {
+        const v8h k128 = {static_cast<_Float16>(128.0f), static_cast<_Float16>(128.0f), static_cast<_Float16>(128.0f),
+                          static_cast<_Float16>(128.0f), static_cast<_Float16>(128.0f), static_cast<_Float16>(128.0f),
+                          static_cast<_Float16>(128.0f), static_cast<_Float16>(128.0f)};
+#pragma unroll
+        for (int hblk = 0; hblk < 2; ++hblk) {
+          a0[hblk] *= k128;
+          a1[hblk] *= k128;
+        }
+      }
     }
   }
-  const v8h a_hi[2] = {as_v8h(ahi[0][0], ahi[0][1], ahi[0][2], ahi[0][3]),
-                       as_v8h(ahi[1][0], ahi[1][1], ahi[1][2], ahi[1][3])};
-  const v8h a_lo[2] = {as_v8h(alo[0][0], alo[0][1], alo[0][2], alo[0][3]),
-                       as_v8h(alo[1][0], alo[1][1], alo[1][2], alo[1][3])};
 
   // ---------------- values (fp16 MFMA over LDS-transposed codes) ----------------
   if constexpr (VB == 8) {
-    values_int8<D, KB, VB>(lane, a_hi, a_lo, acc, vtile, stile);
+    values_int8<D, KB, VB, TWO>(lane, a0, a1, acc, vtile, stile);
     wave_sync_lds();
     return;
   }
-  uint32_t nmask = 0x000f000fu, nmagic = 0x64006400u;
-  asm volatile("" : "+v"(nmask), "+v"(nmagic));
+  uint32_t m_lo = 0x000f000fu, m_hi = 0x00f000f0u, nmagic = 0x64006400u;
+  asm volatile("" : "+v"(m_lo), "+v"(m_hi), "+v"(nmagic));
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     // lane r of each 16-lane group points at token 16*r4 + r, group g
@@ -469,7 +557,7 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int bas
 #pragma unroll
     for (int hblk = 0; hblk < 2; ++hblk) {
       uint32_t cp[4];
-      nibbles_to_half_pairs(uint32_t(hblk == 0 ? tr.x : tr.y), nmask, nmagic, cp);
+      nibbles_to_half16(uint32_t(hblk == 0 ? tr.x : tr.y), m_lo, m_hi, nmagic, cp);
       uint32_t bh[4], bl[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -480,11 +568,8 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int bas
         bh[i] = __builtin_bit_cast(uint32_t, hi);
         bl[i] = __builtin_bit_cast(uint32_t, lo);
       }
-      const v8h b_hi = as_v8h(bh[0], bh[1], bh[2], bh[3]);
-      const v8h b_lo = as_v8h(bl[0], bl[1], bl[2], bl[3]);
-      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[hblk], b_hi, acc[g], 0, 0, 0);
-      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi[hblk], b_lo, acc[g], 0, 0, 0);
-      acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo[hblk], b_hi, acc[g], 0, 0, 0);
+      acc[g] = value_mfma<TWO>(a0[hblk], a1[hblk], as_v8h(bh[0], bh[1], bh[2], bh[3]), as_v8h(bl[0], bl[1], bl[2], bl[3]),
+                               acc[g]);
     }
   }
   // the next superblock overwrites this wave's tiles
@@ -520,8 +605,9 @@ struct QDecodeParams {
 };
 
 // APP: the appending variant (kvq_decode_attn_append), a separate instance so that the plain
-// decode carries none of its code.
-template <int D, int KB, int VB, int NRB, bool APP>
+// decode carries none of its code.  G1: the head tile is one query head (the score MFMA rows carry
+// the query's three digits instead of heads).
+template <int D, int KB, int VB, int NRB, bool APP, bool G1>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1))) void decode_kernel(
     const QDecodeParams P) {
   using Gm = QGeom<D, KB, VB>;
@@ -623,7 +709,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   if (base < t_end) load_superblock<D, KB, VB>(ra, kc, ks, vc, vs, sb_slot(base, 0), L - base, lane);
 
   // LDS of the prologue (aliases the main-loop tiles): digit operands, per-wave head maxima
-  constexpr int kDigBytes = NRB * NS * 3 * 1024;
+  constexpr int kDigBytes = (G1 ? 1 : NRB * 3) * NS * 1024;
   uint8_t* dig = smem;
   float* pmax = reinterpret_cast<float*>(smem + kDigBytes);  // [kWaves][16]
   for (int i = threadIdx.x; i < kDigBytes / 16; i += kThreads)
@@ -739,9 +825,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
           *reinterpret_cast<const uint4*>(appbuf + Gm::APP_VS + 16 * u);
     }
   }
-  // per-head step: the largest |q_hat| maps to 32639 * 256 so all three digits fit int8 (two
-  // digits, 16 bits relative to the largest channel, left score errors up to ~1e-2 when lambda_K
-  // spans a decade and keys exceed the calibration range)
+  // per-head step: the largest |q_hat| maps to QTOT = 2^20 (int8 keys: 2^19), so the digits
+  // hi, mid, lo of Q = 65536 hi + 256 mid + lo fit int8 with |hi| <= 16 (8) and a group dot of Q
+  // with 16 codes stays exact in int32 (two 8-bit digits, 16 bits relative to the largest
+  // channel, left score errors up to ~1e-2 when lambda_K spans a decade and keys exceed the
+  // calibration range)
+  constexpr float QTOT = KB == 4 ? 1048576.0f : 524288.0f;
   float sgm[4];
   {
     float4 mx = *reinterpret_cast<const float4*>(pmax + 4 * r4);
@@ -752,24 +841,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
     }
     const float m4[4] = {mx.x, mx.y, mx.z, mx.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sgm[i] = m4[i] > 0.0f ? m4[i] / (32639.0f * 256.0f) : 1.0f;
+    for (int i = 0; i < 4; ++i) sgm[i] = m4[i] > 0.0f ? m4[i] / QTOT : 1.0f;
   }
-  // score multiplier of the rows this lane's scores belong to: heads 4 rb + r4
+  // score multiplier of the rows this lane's scores belong to: heads 4 rb + r4 (G1: head 0 in
+  // every lane)
   float sig[NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
+    const int hr = G1 ? 0 : 4 * rb + r4;
     float mxh = 0.0f;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) mxh = fmaxf(mxh, pmax[ww * 16 + 4 * rb + r4]);
-    const float sg = mxh > 0.0f ? mxh / 32639.0f : 1.0f;
-    // step of the combined dot (256 hi + mid + lo / 256), times 1/16 for int4 codes widened as
-    // 16*code
-    sig[rb] = (4 * rb + r4 < GT ? sg : 0.0f) * (KB == 4 ? 0.0625f : 1.0f);
+    for (int ww = 0; ww < kWaves; ++ww) mxh = fmaxf(mxh, pmax[ww * 16 + hr]);
+    const float sg = mxh > 0.0f ? mxh / QTOT : 1.0f;
+    // step of the exact dot of Q, times 1/16 for int4 codes widened as 16 * code
+    sig[rb] = (hr < GT ? sg : 0.0f) * (KB == 4 ? 0.0625f : 1.0f);
   }
   // the three int8 digits of every channel (Q = 65536 hi + 256 mid + lo), scattered into the score
   // MFMA's A operands: for (row block rb, step s, digit dg) lane l holds row r = l%16 = (head
   // 4rb + r/4, slot r%4) and the k bytes of lane group l/16; it is non-zero only when
-  // l/16 == r%4, where the 16 bytes are the digits of group g = (r%4) NS + s
+  // l/16 == r%4, where the 16 bytes are the digits of group g = (r%4) NS + s.  G1: one operand
+  // per step s, row r = 4 slot + digit (row 4 slot + 3 zero), non-zero where l/16 == slot.
   {
     int bt_of_c = 0;  // byte of the widened K codes that holds channel n16 of a group
 #pragma unroll
@@ -783,30 +874,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
       for (int i = 0; i < 4; ++i) {
         const int h = 4 * r4 + i;
         if (h < GT) {
+          constexpr int QI = int(QTOT);
           int Q = static_cast<int>(rintf(qv_[j][i] * (1.0f / sgm[i])));
-          Q = min(max(Q, -32639 * 256), 32639 * 256);
-          const int t1 = (Q + 128) >> 8;  // in [-32639, 32639]
+          Q = min(max(Q, -QI), QI);
+          const int t1 = (Q + 128) >> 8;  // in [-QI / 256, QI / 256]
           const int lo = Q - 256 * t1;     // in [-128, 127]
-          const int hi = (t1 + 128) >> 8;  // in [-127, 127]
+          const int hi = (t1 + 128) >> 8;  // in [-16, 16] (int8 keys: [-8, 8])
           const int mid = t1 - 256 * hi;   // in [-128, 127]
-          const int rb = h >> 2, row = (h & 3) * 4 + slot;
-          const int off = ((rb * NS + s) * 3) * 1024 + (row + 16 * slot) * 16 + bt_of_c;
-          dig[off] = uint8_t(hi & 0xff);
-          dig[off + 1024] = uint8_t(mid & 0xff);
-          dig[off + 2048] = uint8_t(lo & 0xff);
+          if constexpr (G1) {
+            const int off = s * 1024 + (4 * slot + 16 * slot) * 16 + bt_of_c;
+            dig[off] = uint8_t(hi & 0xff);
+            dig[off + 16] = uint8_t(mid & 0xff);
+            dig[off + 32] = uint8_t(lo & 0xff);
+          } else {
+            const int rb = h >> 2, row = (h & 3) * 4 + slot;
+            const int off = ((rb * NS + s) * 3) * 1024 + (row + 16 * slot) * 16 + bt_of_c;
+            dig[off] = uint8_t(hi & 0xff);
+            dig[off + 1024] = uint8_t(mid & 0xff);
+            dig[off + 2048] = uint8_t(lo & 0xff);
+          }
         }
       }
     }
   }
   __syncthreads();
-  v4i aop[NRB][NS][3];
+  v4i aop[G1 ? 1 : NRB][NS][G1 ? 1 : 3];
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb)
+  for (int rb = 0; rb < (G1 ? 1 : NRB); ++rb)
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int dg = 0; dg < 3; ++dg) {
-        const uint4 v = *reinterpret_cast<const uint4*>(dig + ((rb * NS + s) * 3 + dg) * 1024 + lane * 16);
+      for (int dg = 0; dg < (G1 ? 1 : 3); ++dg) {
+        const uint4 v = *reinterpret_cast<const uint4*>(dig + ((rb * NS + s) * (G1 ? 1 : 3) + dg) * 1024 + lane * 16);
         aop[rb][s][dg] = v4i{int(v.x), int(v.y), int(v.z), int(v.w)};
       }
   __syncthreads();  // the main loop's tiles overwrite the prologue's LDS
@@ -815,11 +914,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   uint8_t* vtile = wbase;
   uint16_t* stile = reinterpret_cast<uint16_t*>(wbase + Gm::LDS_V);
   uint16_t* ktile = reinterpret_cast<uint16_t*>(wbase + Gm::LDS_V + Gm::LDS_S);
-  float* ptile = reinterpret_cast<float*>(wbase + Gm::LDS_V + Gm::LDS_S + Gm::LDS_K);
+  uint16_t* ptile = reinterpret_cast<uint16_t*>(wbase + Gm::LDS_V + Gm::LDS_S + Gm::LDS_K);
   float* atile = reinterpret_cast<float*>(wbase + Gm::LDS_V + Gm::LDS_S + Gm::LDS_K + Gm::LDS_P);
 
   // P rows never produced by a score row block and alpha of such heads stay neutral
-  for (int i = lane; i < 16 * kSB; i += 64) ptile[i] = 0.0f;
+  for (int i = lane; i < 32 * kSB / 2; i += 64) reinterpret_cast<uint32_t*>(ptile)[i] = 0u;
   if (lane < 16) atile[lane] = 1.0f;
 
   float m_run[NRB], l_run[NRB];
@@ -834,10 +933,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
 
   for (int k = 0; base < t_end; ++k) {
     if (app && t_app >= base && t_app < base + kSB) patch_superblock<D, KB, VB>(ra, t_app - base, appbuf, lane);
-    process_superblock<D, KB, VB, NRB>(ra, base, t_end, lane, aop, sig, m_run, l_run, acc, vtile, stile, ktile, ptile,
+    process_superblock<D, KB, VB, NRB, G1>(ra, base, t_end, lane, aop, sig, m_run, l_run, acc, vtile, stile, ktile, ptile,
                                    atile, kc, ks, vc, vs, base + kStride, sb_slot(base + kStride, k + 1),
                                    L - (base + kStride));
     base += kStride;
+  }
+  if constexpr (NRB <= 2) {
+    // (head, part) rows: add the lo rows of a head (lanes 32-63) to its hi rows (lanes 0-31)
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[g][i]), __float_as_uint(acc[g][i]), false,
+                                                        false);
+        acc[g][i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      }
   }
 
   if (P.n_chunks == 1) {
@@ -899,23 +1009,27 @@ hipError_t launch_q(const DecodeArgs& a, const DecodePlan& p, const WsLayout& w,
   P.num_pages = a.num_pages;
   const dim3 grid(units * p.n_chunks), block(kThreads);
   const bool app = a.k_new != nullptr;
-#define KVQ_DLAUNCH(NRB)                                                              \
+#define KVQ_DLAUNCH(NRB, G1)                                                          \
   if (app)                                                                            \
-    hipLaunchKernelGGL((decode_kernel<D, KB, VB, NRB, true>), grid, block, 0, s, P);      \
+    hipLaunchKernelGGL((decode_kernel<D, KB, VB, NRB, true, G1>), grid, block, 0, s, P);  \
   else                                                                                \
-    hipLaunchKernelGGL((decode_kernel<D, KB, VB, NRB, false>), grid, block, 0, s, P);
+    hipLaunchKernelGGL((decode_kernel<D, KB, VB, NRB, false, G1>), grid, block, 0, s, P);
   switch ((p.head_tile + 3) / 4) {
     case 1:
-      KVQ_DLAUNCH(1);
+      if (p.head_tile == 1) {
+        KVQ_DLAUNCH(1, true);
+      } else {
+        KVQ_DLAUNCH(1, false);
+      }
       break;
     case 2:
-      KVQ_DLAUNCH(2);
+      KVQ_DLAUNCH(2, false);
       break;
     case 3:
-      KVQ_DLAUNCH(3);
+      KVQ_DLAUNCH(3, false);
       break;
     case 4:
-      KVQ_DLAUNCH(4);
+      KVQ_DLAUNCH(4, false);
       break;
     default:
       return hipErrorInvalidValue;
