@@ -442,6 +442,29 @@ def main():
     paged_diff = float((out_pg - out).abs().max())
     del paged_planes
 
+    # kvq_attn: several query tokens (speculative verification of 4 drafted tokens: the last 4
+    # positions attend causally) and a sliding window of 4096 positions, over the same cache
+    n_spec = 4
+    q_spec = torch.from_numpy(np.concatenate(
+        [np.random.default_rng(l).standard_normal((B, n_spec, Hq, d)).astype(np.float16) for l in range(L)])).cuda()
+    opts_spec = kvq.make_attn_opts(n_spec, 0)
+    ws_spec = torch.zeros(kvq.kvq_attn_workspace_bytes(lay, opts_spec, S), dtype=torch.uint8, device="cuda")
+    out_spec = torch.empty(LB * n_spec * Hq * d, dtype=torch.float32, device="cuda")
+    win = min(4096, S)
+    opts_win = kvq.make_attn_opts(1, win)
+    ws_win = torch.zeros(kvq.kvq_attn_workspace_bytes(lay, opts_win, S), dtype=torch.uint8, device="cuda")
+
+    def attn(i, opts, qq, wsp, o):
+        p = planes[i]
+        kvq.kvq_attn(lay, opts, qq, p[0], p[1], p[2], p[3], None, 0, 0, 0, S, None, s, s, 0, lam_k, lam_v, lbs, 0.0, wsp,
+                     o)
+
+    res_spec = timer.run(lambda i: attn(i, opts_spec, q_spec.view(-1), ws_spec, out_spec), R, steps, args.warmup)
+    res_win = timer.run(lambda i: attn(i, opts_win, q, ws_win, out), R, steps, args.warmup)
+    pl_spec = kvq.kvq_attn_launch_plan(lay, opts_spec, S)
+    win_bytes = q_bytes // S * win
+    del q_spec, out_spec, ws_spec, ws_win
+
     # one scale per vector (group = d), the per-token comparison mode of the write path: bulk
     # quantize of K and V, all layers, and the round-trip error of both modes on layer 0's K
     lay_pt = kvq.make_layout(LB, H, Hq, d, S, k_bits=w.k_bits, v_bits=w.v_bits, transform=args.transform,
@@ -522,6 +545,17 @@ def main():
                           "GBps_moved": round(bq_bytes / (res_bq["ms_mean"] * 1e-3) / 1e9, 2),
                           "frac_hbm_peak": round(bq_bytes / (res_bq["ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                           "vectors": n_vec, "ms": round(res_bq["ms_mean"], 5)},
+        "attn_speculative_4": {
+            "GBps": round(q_bytes / (res_spec["ms_mean"] * 1e-3) / 1e9, 2), "ms": round(res_spec["ms_mean"], 5),
+            "query_tokens": n_spec, "rows_per_work_group": pl_spec.head_tile * pl_spec.query_tile,
+            "query_tiles": pl_spec.query_tiles,
+            "note": "kvq_attn, 4 query tokens per sequence (the last 4 positions, causal), every layer; bytes = the "
+                    "whole cache, read once per tile of query tokens"},
+        "attn_window": {
+            "GBps": round(win_bytes / (res_win["ms_mean"] * 1e-3) / 1e9, 2), "ms": round(res_win["ms_mean"], 5),
+            "window": win, "bytes_per_step": win_bytes,
+            "note": "kvq_attn, one query token, sliding window of the latest positions; bytes = the window's codes "
+                    "and scales"},
         "decode_paged": {
             "GBps": round(dec_bytes / (res_pg["ms_mean"] * 1e-3) / 1e9, 2), "ms": round(res_pg["ms_mean"], 5),
             "page_tokens": page, "pages": LB * pps, "max_abs_diff_vs_contiguous": paged_diff,

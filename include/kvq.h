@@ -311,9 +311,70 @@ typedef struct {
   int32_t superblocks_per_wave;  /* decode: ceil(chunk / (4 * wave_tokens))                */
   int64_t blocks;                /* quantize: 16-vector blocks of the call                 */
   int64_t blocks_per_work_group; /* quantize: largest block range of one work-group        */
+  int32_t query_tile;            /* kvq_attn: query tokens per work-group (decode calls: 1) */
+  int32_t query_tiles;           /* kvq_attn: ceil(n_query / query_tile) (decode calls: 1)  */
 } kvq_plan;
 
 kvq_status kvq_launch_plan(const kvq_layout* layout, kvq_call call, int32_t n, kvq_plan* out);
+
+/*
+ * kvq_attn -- attention of several query tokens per sequence over the quantized cache, with an
+ * optional sliding window, on contiguous rows, a ring buffer or a paged cache.
+ *   Several query tokens: the step before single-token decode (chunked prefill, speculative
+ *   verification: [GM] "Flash Attention 与 Metal 内核融合", tiled attention with an online
+ *   softmax).  The n_query new tokens are the last n_query positions of every sequence's cache
+ *   (already written with kvq_quantize); query i of a sequence of length L sits at position
+ *   p = L - n_query + i and attends positions t <= p (causal).  A query with p < 0 gets a zero
+ *   output.
+ *   Sliding window ([GM] "KV 缓存分片与内存管理": keep the latest tokens): with window W >= 1 a
+ *   query at p attends only t in [max(0, p - W + 1), p].
+ *   Ring buffer: position t of a row is stored at slot t % capacity (contiguous rows) or at
+ *   page_table[b * pages_per_seq + (t % capacity) / page_size], offset t % page_size (paged), so a
+ *   row of `capacity` slots holds the latest `capacity` positions of an unbounded sequence.
+ * For every sequence b, query token i and query head h (kv head h / G):
+ *   out[b, i, h] = sum_t softmax_t(sm_scale * q[b, i, h] . x_hat_K[b, j, t]) x_hat_V[b, j, t]
+ * over the positions above; computed in the rotated domain as kvq_decode_attn does (same kernel
+ * family; n_query = 1 with no window gives kvq_decode_attn's result).
+ *   opts         : host struct (n_query >= 1, window >= 0 with 0 = none, ring 0 or 1)
+ *   q_f16        : fp16 [batch, n_query, q_heads, head_dim] contiguous
+ *   page_table   : NULL for contiguous rows (planes [batch, kv_heads, capacity, .]); otherwise
+ *                  device int32 [batch, pages_per_seq] with the page rules of
+ *                  kvq_decode_attn_paged (page_size a multiple of 64, capacity = pages_per_seq x
+ *                  page_size, entries clamped to [0, num_pages))
+ *   seq_len      : the largest length; without a ring 1 <= seq_len <= capacity; with a ring any
+ *                  seq_len >= 1, capacity a multiple of 64, window >= 1 and
+ *                  window + n_query - 1 <= capacity (the attended positions of a unit are
+ *                  still in the ring)
+ *   seq_lens     : device int32 [batch] or NULL, clamped to [0, seq_len]
+ *   workspace    : >= kvq_attn_workspace_bytes(layout, opts, seq_len) bytes, 256-byte aligned,
+ *                  first 65536 bytes zeroed counters, as kvq_decode_attn's
+ *   out          : float [batch, n_query, q_heads, head_dim]
+ * Other arguments and errors as kvq_decode_attn / kvq_decode_attn_paged.
+ */
+typedef struct {
+  int32_t n_query; /* query tokens per sequence, >= 1                              */
+  int32_t window;  /* 0: no window; W >= 1: the W latest positions up to the query */
+  int32_t ring;    /* 0: position t at slot t; 1: at slot t % capacity             */
+} kvq_attn_opts;
+
+kvq_status kvq_attn(const kvq_layout* layout, const kvq_attn_opts* opts, const void* q_f16,
+                    const void* k_codes, const void* k_scales, const void* v_codes,
+                    const void* v_scales, const int32_t* page_table, int32_t pages_per_seq,
+                    int32_t page_size, int32_t num_pages, int32_t seq_len, const int32_t* seq_lens,
+                    const float* sign_k, const float* sign_v, int64_t sign_batch_stride,
+                    const float* lambda_k, const float* lambda_v, int64_t lambda_batch_stride,
+                    float sm_scale, void* workspace, size_t workspace_bytes, float* out,
+                    void* stream);
+
+/* Workspace bytes kvq_attn needs for any seq_len <= max_seq_len with these options (contiguous or
+ * paged).  0 if the layout or options are invalid. */
+size_t kvq_attn_workspace_bytes(const kvq_layout* layout, const kvq_attn_opts* opts,
+                                int32_t max_seq_len);
+
+/* The launch shape of kvq_attn (host only), as kvq_launch_plan describes the other calls; paged:
+ * nonzero for a paged cache.  query_tile / query_tiles give the split of the query tokens. */
+kvq_status kvq_attn_launch_plan(const kvq_layout* layout, const kvq_attn_opts* opts, int32_t seq_len,
+                                int32_t paged, kvq_plan* out);
 
 #ifdef __cplusplus
 }

@@ -443,8 +443,133 @@ kvq_status kvq_launch_plan(const kvq_layout* L, kvq_call call, int32_t n, kvq_pl
   r.n_chunks = p.n_chunks;
   r.wave_tokens = f16 ? 32 : 64;
   r.superblocks_per_wave = (p.chunk + 4 * r.wave_tokens - 1) / (4 * r.wave_tokens);
+  r.query_tile = r.query_tiles = 1;
   *out = r;
   return ok();
+}
+
+// Shared checks of the multi-token / windowed attention (kvq_attn and its sizing calls).
+static kvq_status check_attn_opts(const kvq_layout* L, const kvq_attn_opts* o, int32_t seq_len, const char* fn) {
+  if (!o) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: opts is NULL", fn);
+  if (o->n_query < 1 || o->window < 0 || (o->ring != 0 && o->ring != 1))
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: need n_query >= 1 (%d), window >= 0 (%d), ring 0 or 1 (%d)", fn,
+                o->n_query, o->window, o->ring);
+  if (L->q_heads < 1 || L->q_heads % L->kv_heads != 0)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: q_heads (%d) must be a positive multiple of kv_heads (%d)", fn,
+                L->q_heads, L->kv_heads);
+  if (L->q_heads / L->kv_heads > 64)
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: GQA ratio %d (supported: <= 64)", fn, L->q_heads / L->kv_heads);
+  if (seq_len < 1) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: seq_len %d must be >= 1", fn, seq_len);
+  if (o->ring) {
+    if (L->capacity % 64 != 0)
+      return fail(KVQ_ERR_UNSUPPORTED, "%s: a ring buffer needs capacity (%d) a multiple of 64", fn, L->capacity);
+    if (o->window < 1 || (long long)o->window + o->n_query - 1 > L->capacity)
+      return fail(KVQ_ERR_INVALID_ARGUMENT,
+                  "%s: a ring buffer needs 1 <= window and window + n_query - 1 <= capacity (window %d, n_query %d, "
+                  "capacity %d)",
+                  fn, o->window, o->n_query, L->capacity);
+  } else if (seq_len > L->capacity) {
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: seq_len %d must lie in [1, capacity=%d] without a ring buffer", fn,
+                seq_len, L->capacity);
+  }
+  return KVQ_OK;
+}
+
+size_t kvq_attn_workspace_bytes(const kvq_layout* L, const kvq_attn_opts* o, int32_t max_seq_len) {
+  if (check_layout(L, "kvq_attn_workspace_bytes") != KVQ_OK) return 0;
+  if (check_attn_opts(L, o, max_seq_len, "kvq_attn_workspace_bytes") != KVQ_OK) return 0;
+  return kvq_impl::attn_workspace_bytes(L->batch, L->kv_heads, L->q_heads, L->head_dim, max_seq_len, o->n_query,
+                                        o->window);
+}
+
+kvq_status kvq_attn_launch_plan(const kvq_layout* L, const kvq_attn_opts* o, int32_t seq_len, int32_t paged,
+                                kvq_plan* out) {
+  const char* fn = "kvq_attn_launch_plan";
+  KVQ_TRY(check_layout(L, fn));
+  KVQ_TRY(check_attn_opts(L, o, seq_len, fn));
+  if (!out) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: out is NULL", fn);
+  const kvq_impl::DecodePlan p = kvq_impl::plan_decode(L->batch, L->kv_heads, L->q_heads, L->head_dim, seq_len,
+                                                       seq_len, false, false, paged != 0, o->n_query, o->window);
+  kvq_plan r{};
+  r.work_groups = int64_t(L->batch) * L->kv_heads * p.head_tiles * p.tok_tiles * p.n_chunks;
+  r.head_tile = p.head_tile;
+  r.head_tiles = p.head_tiles;
+  r.chunk = p.chunk;
+  r.n_chunks = p.n_chunks;
+  r.wave_tokens = 64;
+  r.superblocks_per_wave = (p.chunk + 255) / 256;
+  r.query_tile = p.tok_tile;
+  r.query_tiles = p.tok_tiles;
+  *out = r;
+  return ok();
+}
+
+kvq_status kvq_attn(const kvq_layout* L, const kvq_attn_opts* o, const void* q_f16, const void* k_codes,
+                    const void* k_scales, const void* v_codes, const void* v_scales, const int32_t* page_table,
+                    int32_t pages_per_seq, int32_t page_size, int32_t num_pages, int32_t seq_len,
+                    const int32_t* seq_lens, const float* sign_k, const float* sign_v, int64_t sign_batch_stride,
+                    const float* lambda_k, const float* lambda_v, int64_t lambda_batch_stride, float sm_scale,
+                    void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  const char* fn = "kvq_attn";
+  KVQ_TRY(check_layout(L, fn));
+  KVQ_TRY(check_bits(L->k_bits, fn, "k_bits"));
+  KVQ_TRY(check_bits(L->v_bits, fn, "v_bits"));
+  KVQ_TRY(check_decode_group(L, fn));
+  KVQ_TRY(check_attn_opts(L, o, seq_len, fn));
+  if (!std::isfinite(sm_scale)) return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: sm_scale is not finite", fn);
+  const bool paged = page_table != nullptr;
+  if (paged) {
+    if (page_size < 64 || page_size % 64 != 0)
+      return fail(KVQ_ERR_UNSUPPORTED, "%s: page_size %d (supported: a positive multiple of 64)", fn, page_size);
+    if (pages_per_seq < 1 || num_pages < 1)
+      return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: pages_per_seq (%d) and num_pages (%d) must be >= 1", fn,
+                  pages_per_seq, num_pages);
+    if ((long long)pages_per_seq * page_size != L->capacity)
+      return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: capacity (%d) must equal pages_per_seq x page_size (%lld)", fn,
+                  L->capacity, (long long)pages_per_seq * page_size);
+    if ((long long)num_pages * L->kv_heads * page_size > (1LL << 40))
+      return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: num_pages*kv_heads*page_size too large", fn);
+    KVQ_TRY(check_ptr(page_table, 4, fn, "page_table"));
+  }
+  KVQ_TRY(check_ptr(q_f16, 16, fn, "q"));
+  KVQ_TRY(check_ptr(out, 16, fn, "out"));
+  KVQ_TRY(check_opt_ptr(seq_lens, 4, fn, "seq_lens"));
+  KVQ_TRY(check_ptr(k_codes, 16, fn, "k_codes"));
+  KVQ_TRY(check_ptr(k_scales, 16, fn, "k_scales"));
+  KVQ_TRY(check_ptr(v_codes, 16, fn, "v_codes"));
+  KVQ_TRY(check_ptr(v_scales, 16, fn, "v_scales"));
+  KVQ_TRY(check_ptr(sign_k, 4, fn, "sign_k"));
+  KVQ_TRY(check_ptr(sign_v, 4, fn, "sign_v"));
+  KVQ_TRY(check_opt_ptr(lambda_k, 4, fn, "lambda_k"));
+  KVQ_TRY(check_opt_ptr(lambda_v, 4, fn, "lambda_v"));
+  KVQ_TRY(check_strides(sign_batch_stride, lambda_batch_stride, fn));
+  const kvq_impl::DecodePlan p = kvq_impl::plan_decode(L->batch, L->kv_heads, L->q_heads, L->head_dim, seq_len,
+                                                       seq_len, false, false, paged, o->n_query, o->window);
+  const long long units = (long long)L->batch * L->kv_heads * p.head_tiles * p.tok_tiles;
+  if (units > kvq_impl::kMaxDecodeUnits)
+    return fail(KVQ_ERR_UNSUPPORTED, "%s: batch x kv_heads x head tiles x query tiles = %lld exceeds %d", fn, units,
+                kvq_impl::kMaxDecodeUnits);
+  if ((long long)L->batch * o->n_query * L->q_heads > 0x7fffffffLL)
+    return fail(KVQ_ERR_INVALID_ARGUMENT, "%s: batch x n_query x q_heads exceeds 2^31 - 1 rows", fn);
+  KVQ_TRY(check_ptr(workspace, 256, fn, "workspace"));
+  const size_t need = kvq_impl::attn_workspace_bytes(L->batch, L->kv_heads, L->q_heads, L->head_dim, seq_len,
+                                                     o->n_query, o->window);
+  if (workspace_bytes < need)
+    return fail(KVQ_ERR_WORKSPACE_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", fn, workspace_bytes, need);
+  const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / std::sqrt(float(L->head_dim));
+  kvq_impl::DecodeArgs a{L->batch,   L->kv_heads, L->q_heads, L->head_dim, L->k_bits,   L->v_bits,
+                         L->capacity, seq_len,    seq_lens,   q_f16,       k_codes,     k_scales,
+                         v_codes,    v_scales,    sign_k,     sign_v,      sign_batch_stride, lambda_k,
+                         lambda_v,   lambda_batch_stride,     scale,       workspace,   out};
+  a.transform = L->transform;
+  a.page_table = page_table;
+  a.page_size = page_size;
+  a.pages_per_seq = pages_per_seq;
+  a.num_pages = num_pages;
+  a.n_query = o->n_query;
+  a.window = o->window;
+  a.ring = o->ring;
+  return hip_status(kvq_impl::launch_decode(a, p, static_cast<hipStream_t>(stream)), fn);
 }
 
 }  // extern "C"

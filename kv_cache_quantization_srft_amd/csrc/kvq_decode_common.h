@@ -339,10 +339,14 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, int n_chunks, int
 // lambda_V and inverse-rotated with MFMAs against generated operands (A = y split into fp16
 // hi + lo):  x[h][n] = s_n sum_c y[h][c] Q[c][n].
 // ------------------------------------------------------------------------------------------
+// A unit is ((sequence b, kv head) x head tile ht) x query-token tile tt; it owns `rows` (head_tile
+// below) query rows, row r = (token tt * tok_tile + r / gt, head ht * gt + r % gt).  Single-token
+// decode has tok_tile = tok_tiles = n_query = 1 and rows = gt.
 struct MergeArgs {
   const float* pml;
   const float* pacc;
   int n_chunks, max_chunks, head_tile, head_tiles, q_heads, kv_heads;
+  int gt, tok_tile, tok_tiles, n_query;
   float acc_scale;
   const float* sign;
   int64_t sign_bs;
@@ -367,12 +371,23 @@ struct RotOps {
   float sg[NBW];
 };
 
+// Sequence and kv head of a unit; orow0 = output row of the unit's row 0, tt = its token tile.
 __device__ __forceinline__ void unit_coords(const MergeArgs& a, int unit, int& b, int& kvh, int64_t& orow0) {
-  const int ht = unit % a.head_tiles;
-  const int bk = unit / a.head_tiles;
+  const int tt = unit % a.tok_tiles;
+  const int hu = unit / a.tok_tiles;
+  const int ht = hu % a.head_tiles;
+  const int bk = hu / a.head_tiles;
   kvh = bk % a.kv_heads;
   b = bk / a.kv_heads;
-  orow0 = int64_t(b) * a.q_heads + kvh * (a.q_heads / a.kv_heads) + ht * a.head_tile;
+  orow0 = (int64_t(b) * a.n_query + tt * a.tok_tile) * a.q_heads + kvh * (a.q_heads / a.kv_heads) + ht * a.gt;
+}
+
+// Output row of row r of the unit whose row 0 is orow0, or -1 past the last query token.
+__device__ __forceinline__ int64_t out_row(const MergeArgs& a, int unit, int64_t orow0, int r) {
+  if (a.tok_tiles == 1 && a.tok_tile == 1) return orow0 + r;
+  const int i = r / a.gt;
+  if ((unit % a.tok_tiles) * a.tok_tile + i >= a.n_query) return -1;
+  return orow0 + int64_t(i) * a.q_heads + (r - i * a.gt);
 }
 
 template <int D>
@@ -443,7 +458,8 @@ __device__ __forceinline__ void rotate_store(const MergeArgs& a, int unit, const
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * r4 + i;
-      if (h < GT) a.out[(orow0 + h) * D + n] = acc[i] * sg;
+      const int64_t orow = out_row(a, unit, orow0, h);
+      if (h < GT && orow >= 0) a.out[orow * D + n] = acc[i] * sg;
     }
   }
 }
@@ -543,7 +559,7 @@ __device__ __forceinline__ void merge_unit(const MergeArgs& a, int unit, float* 
       }
       const float li = linv[h];
       v = make_float4(v.x * li * lam4[k].x, v.y * li * lam4[k].y, v.z * li * lam4[k].z, v.w * li * lam4[k].w);
-      if constexpr (!ROT) *reinterpret_cast<float4*>(a.out + (orow0 + h) * D + c) = v;
+      if constexpr (!ROT) *reinterpret_cast<float4*>(a.out + out_row(a, unit, orow0, h) * D + c) = v;
     }
     yv[k] = v;
   }
@@ -645,7 +661,7 @@ __device__ __forceinline__ void finish_direct(float (&m_run)[NSLOT], float (&l_r
       }
       const float li = hml[2 * h];
       s = make_float4(s.x * li * lam4[k].x, s.y * li * lam4[k].y, s.z * li * lam4[k].z, s.w * li * lam4[k].w);
-      if constexpr (!ROT) *reinterpret_cast<float4*>(a.out + (orow0 + h) * D + c) = s;
+      if constexpr (!ROT) *reinterpret_cast<float4*>(a.out + out_row(a, unit, orow0, h) * D + c) = s;
     }
     yv[k] = s;
   }

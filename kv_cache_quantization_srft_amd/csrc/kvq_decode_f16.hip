@@ -220,9 +220,19 @@ hipError_t launch_f16(const DecodeF16Args& a, const DecodePlan& p, const WsLayou
   auto* pacc = reinterpret_cast<float*>(ws + w.pacc);
   const int units = a.batch * a.kv_heads * p.head_tiles;
   auto* counters = reinterpret_cast<uint32_t*>(ws + w.counters);
-  const MergeArgs m{pml,       pacc,       p.n_chunks, p.max_chunks, p.head_tile, p.head_tiles, a.q_heads,
-                    a.kv_heads, 1.0f,      nullptr,    0,            nullptr,     0,            a.out,
-                    0};
+  MergeArgs m{};
+  m.pml = pml;
+  m.pacc = pacc;
+  m.n_chunks = p.n_chunks;
+  m.max_chunks = p.max_chunks;
+  m.head_tile = p.head_tile;
+  m.head_tiles = p.head_tiles;
+  m.q_heads = a.q_heads;
+  m.kv_heads = a.kv_heads;
+  m.gt = p.head_tile;
+  m.tok_tile = m.tok_tiles = m.n_query = 1;
+  m.acc_scale = 1.0f;
+  m.out = a.out;
   hipLaunchKernelGGL((decode_f16_kernel<D>), dim3(units * p.n_chunks), dim3(kThreads), 0, s,
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.q), a.seq_lens, a.seq_len, a.kv_heads, a.q_heads, a.capacity,

@@ -326,7 +326,8 @@ __device__ __forceinline__ int digit_dot(int hi, int mid, int lo) {
 template <int D, int KB, int VB, int NRB, bool G1>
 __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int base, int t_end, int lane,
                                                    const v4i (&aop)[G1 ? 1 : NRB][D / 64][G1 ? 1 : 3],
-                                                   const float (&sig)[NRB], float (&m_run)[NRB], float (&l_run)[NRB],
+                                                   const float (&sig)[NRB], const int (&rlo)[NRB], const int (&rhi)[NRB],
+                                                   int lo_max, int hi_min, float (&m_run)[NRB], float (&l_run)[NRB],
                                                    v4f (&acc)[D / 16], uint8_t* vtile, uint16_t* stile,
                                                    uint16_t* ktile, uint16_t* ptile, float* atile,
                                                    const uint8_t* __restrict__ kc, const uint16_t* __restrict__ ks,
@@ -391,7 +392,9 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int bas
   // ---------------- scores (int8 MFMA, exact integer group dots) ----------------
   // A group dot of the 21-bit (int8 keys: 20-bit) query digits, hi * 65536 + mid * 256 + lo, is
   // exact in int32 (|hi| <= 16, or 8; 16 channels of codes up to 112 = 16 * 7, or 127).
-  const bool tail = base + kSB > t_end;  // wave-uniform: only the last superblock has masked tokens
+  // wave-uniform: only the chunk's last superblock and those at a row's causal end or window start
+  // hold masked tokens
+  const bool tail = base + kSB > min(t_end, hi_min) || base < lo_max;
   float sc[4][NRB];
 #pragma unroll
   for (int sb = 0; sb < 4; ++sb) {
@@ -425,7 +428,8 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int bas
                         : fma_mix_f16<0>(static_cast<float>(dot), kr[s >> 1], s_acc);
       }
       s_acc = rows_sum4(s_acc) * sig[0];
-      sc[sb][0] = (tail && base + 16 * sb + n16 >= t_end) ? -INFINITY : s_acc;
+      const int tok = base + 16 * sb + n16;
+      sc[sb][0] = (tail && (tok >= t_end || tok < rlo[0] || tok >= rhi[0])) ? -INFINITY : s_acc;
     } else {
       uint32_t kraw[Gm::SLW];
       {
@@ -457,7 +461,8 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int bas
           }
         }
         s_acc *= sig[rb];
-        sc[sb][rb] = (tail && base + 16 * sb + n16 >= t_end) ? -INFINITY : s_acc;
+        const int tok = base + 16 * sb + n16;
+        sc[sb][rb] = (tail && (tok >= t_end || tok < rlo[rb] || tok >= rhi[rb])) ? -INFINITY : s_acc;
       }
     }
   }
@@ -466,20 +471,21 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int bas
   if (next_base < t_end) load_sb_kcodes<D, KB, VB>(r, kc, next_t0, next_nrem, lane);
 
   // ---------------- online softmax per head (16-lane rows); p as fp16 hi + lo in LDS ----------------
-  // The running maximum of a head is finite after its first superblock (every superblock holds a
-  // valid token of its chunk), so exp2 needs no guard: exp2(-inf) = 0.
+  // A row whose tokens so far are all masked keeps m = -inf; the exponent's reference is then 0, so
+  // exp2(-inf - 0) = 0 and no NaN arises.
   bool rescale = false;
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     float mb = fmaxf(fmaxf(sc[0][rb], sc[1][rb]), fmaxf(sc[2][rb], sc[3][rb]));
     mb = row_max16(mb);
     const float mn = fmaxf(m_run[rb], mb);
-    const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - mn);
+    const float mref = mn == -INFINITY ? 0.0f : mn;
+    const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - mref);
     rescale |= mn != m_run[rb];
     m_run[rb] = mn;
     float p[4];
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) p[sb] = __builtin_amdgcn_exp2f(sc[sb][rb] - mn);
+    for (int sb = 0; sb < 4; ++sb) p[sb] = __builtin_amdgcn_exp2f(sc[sb][rb] - mref);
     l_run[rb] = l_run[rb] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
     const int head = 4 * rb + r4;
     uint16_t* prow = ptile + head * kSB + kpos16(n16);
@@ -602,6 +608,10 @@ struct QDecodeParams {
   // planes, page = page_table[b * pages_per_seq + t / page_size] clamped to [0, num_pages)
   const int32_t* page_table;
   int page_size, pages_per_seq, num_pages;
+  // rows of a unit: tok_tile query tokens x head_tile heads; query i of a sequence of length L
+  // sits at position L - n_query + i and attends positions [max(0, p - window + 1) if window,
+  // else 0; p]; ring: token t at plane position t % capacity
+  int tok_tile, tok_tiles, rows, n_query, window, ring;
 };
 
 // APP: the appending variant (kvq_decode_attn_append), a separate instance so that the plain
@@ -621,16 +631,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   const int n16 = lane & 15, r4 = lane >> 4;
   const int ch = blockIdx.x % P.n_chunks;
   const int unit = blockIdx.x / P.n_chunks;
-  const int ht = unit % P.head_tiles;
-  const int bk = unit / P.head_tiles;
+  const int tti = unit % P.tok_tiles;
+  const int hu = unit / P.tok_tiles;
+  const int ht = hu % P.head_tiles;
+  const int bk = hu / P.head_tiles;
   const int kvh = bk % P.kv_heads;
   const int b = bk / P.kv_heads;
-  const int GT = P.head_tile;
+  const int GT = P.head_tile;  // query heads of the unit
+  const int ROWS = P.rows;     // rows: query tokens x heads
   const int h0 = kvh * (P.q_heads / P.kv_heads) + ht * GT;
   int L = P.seq_len;
   if (P.seq_lens) L = min(max(P.seq_lens[b], 0), P.seq_len);
-  const int t_begin = ch * P.chunk;
-  const int t_end = min(L, t_begin + P.chunk);
+  // the unit's query tokens i0 .. i_last sit at positions L - n_query + i; it attends from the
+  // window start of its first query (aligned down to a superblock) to its last query's position
+  const int i0 = tti * P.tok_tile;
+  const int i_last = min(i0 + P.tok_tile, P.n_query) - 1;
+  const int p0 = L - P.n_query + i0, p_last = L - P.n_query + i_last;
+  const int u_end = max(p_last + 1, 0);
+  const int u_start = P.window > 0 ? max(p0 + 1 - P.window, 0) : 0;
+  const int t_begin = (u_start / kSB) * kSB + ch * P.chunk;
+  const int t_end = min(u_end, t_begin + P.chunk);
+  // tokens that some row of the unit masks: below lo_max or from hi_min on (wave-uniform)
+  const int hi_min = max(p0 + 1, 0);
+  const int lo_max = P.window > 0 ? max(p_last + 1 - P.window, 0) : 0;
   const int64_t rowbase = (int64_t(b) * P.kv_heads + kvh) * P.capacity;
   // not restrict: an appending call writes one token of these planes
   const uint8_t* kc = P.kc;
@@ -644,17 +667,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   // of 64).  Issued first, so the first superblock's address waits only for this load.  Entries
   // past the row's tokens read a valid entry and are not used; pages are clamped to the planes.
   const bool paged = P.page_table != nullptr;
-  int pg_v = 0;
+  int pg_v = 0, po_v = 0;  // lane k: page of superblock k and its first token's offset in the page
   if (paged) {
-    const int tb = min(t_begin + w * kSB + lane * kStride, max(L - 1, 0));
+    int tb = min(t_begin + w * kSB + lane * kStride, max(L - 1, 0));
+    if (P.ring) tb %= P.capacity;
     const int e = min(tb / P.page_size, P.pages_per_seq - 1);
     pg_v = min(max(P.page_table[int64_t(b) * P.pages_per_seq + e], 0), P.num_pages - 1);
+    po_v = tb - e * P.page_size;
   }
-  // plane slot of superblock k of this wave (first token bs)
-  auto sb_slot = [&](int bs, int k) -> int64_t {
-    if (!paged) return rowbase + bs;
-    const int pg = __builtin_amdgcn_readlane(pg_v, min(k, 63));
-    return (int64_t(pg) * P.kv_heads + kvh) * P.page_size + bs % P.page_size;
+  // plane slot of superblock k of this wave from its row position ls (the first token's position,
+  // taken modulo the capacity in a ring; a multiple of 64, and a ring's capacity is a multiple of
+  // 64, so a superblock never wraps).  The position advances by the wave stride per superblock:
+  // by one compare and subtract in a ring (step_ring = stride % capacity), no division per step.
+  auto sb_slot = [&](int ls, int k) -> int64_t {
+    if (!paged) return rowbase + ls;
+    const int kk = min(k, 63);
+    const int pg = __builtin_amdgcn_readlane(pg_v, kk);
+    return (int64_t(pg) * P.kv_heads + kvh) * P.page_size + __builtin_amdgcn_readlane(po_v, kk);
+  };
+  const int step_ring = P.ring ? kWaves * kSB % P.capacity : 0;
+  auto next_pos = [&](int ls) -> int {
+    if (!P.ring) return ls + kWaves * kSB;
+    const int n = ls + step_ring;
+    return n >= P.capacity ? n - P.capacity : n;
   };
 
   // ---------------- prologue: rotated query -> int8 digit operands ----------------
@@ -667,10 +702,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   const int t_app = L - 1;
   const bool app = APP && t_app >= t_begin && t_app < t_end;  // work-group uniform
   const bool nrow = app && n16 >= 14;
-  const bool live = n16 < GT || nrow;
+  // row n16 = (query token i0 + n16 / GT, head h0 + n16 % GT)
+  const int qr = min(n16, ROWS - 1);
+  const int qi = min(i0 + qr / GT, P.n_query - 1);
+  const bool live = (n16 < ROWS && i0 + n16 / GT < P.n_query) || nrow;
   const float* srow_k = P.sign_k + b * P.sign_bs;
   const uint16_t* qrow = nrow ? (n16 == 14 ? P.k_new : P.v_new) + (int64_t(b) * P.kv_heads + kvh) * D
-                              : P.q + (int64_t(b) * P.q_heads + h0 + min(n16, GT - 1)) * D;
+                              : P.q + ((int64_t(b) * P.n_query + qi) * P.q_heads + h0 + qr % GT) * D;
   const float* srow = nrow && n16 == 15 ? P.merge.sign + b * P.sign_bs : srow_k;
   uint4 qv[NSTEP];
   float4 sv0[NSTEP], sv1[NSTEP];
@@ -706,7 +744,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
 
   SBRegs<D, KB, VB> ra;
   int base = t_begin + w * kSB;
-  if (base < t_end) load_superblock<D, KB, VB>(ra, kc, ks, vc, vs, sb_slot(base, 0), L - base, lane);
+  int pos = P.ring ? base % P.capacity : base;  // row position of this wave's superblock
+  if (base < t_end) load_superblock<D, KB, VB>(ra, kc, ks, vc, vs, sb_slot(pos, 0), min(L - base, kSB), lane);
 
   // LDS of the prologue (aliases the main-loop tiles): digit operands, per-wave head maxima
   constexpr int kDigBytes = (G1 ? 1 : NRB * 3) * NS * 1024;
@@ -854,7 +893,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
     for (int ww = 0; ww < kWaves; ++ww) mxh = fmaxf(mxh, pmax[ww * 16 + hr]);
     const float sg = mxh > 0.0f ? mxh / QTOT : 1.0f;
     // step of the exact dot of Q, times 1/16 for int4 codes widened as 16 * code
-    sig[rb] = (hr < GT ? sg : 0.0f) * (KB == 4 ? 0.0625f : 1.0f);
+    sig[rb] = (hr < ROWS ? sg : 0.0f) * (KB == 4 ? 0.0625f : 1.0f);
+  }
+  // positions the rows of this lane's scores attend, [rlo, rhi) (rows past the unit's query
+  // tokens and phantom rows: unmasked, their results are never stored)
+  int rlo[NRB], rhi[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int hr = G1 ? 0 : 4 * rb + r4;
+    const int qt = i0 + hr / GT;
+    const bool real = hr < ROWS && qt < P.n_query;
+    const int pr = L - P.n_query + qt;
+    rhi[rb] = real ? max(pr + 1, 0) : 0x7fffffff;
+    rlo[rb] = real && P.window > 0 ? max(pr + 1 - P.window, 0) : 0;
   }
   // the three int8 digits of every channel (Q = 65536 hi + 256 mid + lo), scattered into the score
   // MFMA's A operands: for (row block rb, step s, digit dg) lane l holds row r = l%16 = (head
@@ -873,7 +924,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int h = 4 * r4 + i;
-        if (h < GT) {
+        if (h < ROWS) {
           constexpr int QI = int(QTOT);
           int Q = static_cast<int>(rintf(qv_[j][i] * (1.0f / sgm[i])));
           Q = min(max(Q, -QI), QI);
@@ -933,10 +984,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
 
   for (int k = 0; base < t_end; ++k) {
     if (app && t_app >= base && t_app < base + kSB) patch_superblock<D, KB, VB>(ra, t_app - base, appbuf, lane);
-    process_superblock<D, KB, VB, NRB, G1>(ra, base, t_end, lane, aop, sig, m_run, l_run, acc, vtile, stile, ktile, ptile,
-                                   atile, kc, ks, vc, vs, base + kStride, sb_slot(base + kStride, k + 1),
-                                   L - (base + kStride));
+    process_superblock<D, KB, VB, NRB, G1>(ra, base, t_end, lane, aop, sig, rlo, rhi, lo_max, hi_min, m_run, l_run, acc,
+                                           vtile, stile, ktile, ptile, atile, kc, ks, vc, vs, base + kStride,
+                                           sb_slot(next_pos(pos), k + 1), min(L - (base + kStride), kSB));
     base += kStride;
+    pos = next_pos(pos);
   }
   if constexpr (NRB <= 2) {
     // (head, part) rows: add the lo rows of a head (lanes 32-63) to its hi rows (lanes 0-31)
@@ -956,7 +1008,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
     return;
   }
   PartialArgs e;
-  e.head_tile = GT;
+  e.head_tile = ROWS;
   e.max_chunks = P.max_chunks;
   e.chunk_index = ch;
   e.unit = unit;
@@ -971,7 +1023,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
 template <int D, int KB, int VB>
 hipError_t launch_q(const DecodeArgs& a, const DecodePlan& p, const WsLayout& w, hipStream_t s) {
   char* ws = static_cast<char*>(a.workspace);
-  const int units = a.batch * a.kv_heads * p.head_tiles;
+  const int units = a.batch * a.kv_heads * p.head_tiles * p.tok_tiles;
   QDecodeParams P;
   P.kc = static_cast<const uint8_t*>(a.k_codes);
   P.ks = static_cast<const uint16_t*>(a.k_scales);
@@ -998,9 +1050,33 @@ hipError_t launch_q(const DecodeArgs& a, const DecodePlan& p, const WsLayout& w,
   P.pacc = reinterpret_cast<float*>(ws + w.pacc);
   // int4: code * scale was staged as code * scale / 16 in fp16, acc_scale 16 undoes it (int8
   // keeps the product's scale)
-  P.merge = MergeArgs{P.pml,      P.pacc,     p.n_chunks, p.max_chunks, p.head_tile, p.head_tiles,
-                      a.q_heads,  a.kv_heads, VB == 4 ? 16.0f : 1.0f, a.sign_v, a.sign_bs, a.lambda_v,
-                      a.lambda_bs, a.out,     a.transform};
+  MergeArgs& m = P.merge;
+  m = MergeArgs{};
+  m.pml = P.pml;
+  m.pacc = P.pacc;
+  m.n_chunks = p.n_chunks;
+  m.max_chunks = p.max_chunks;
+  m.head_tile = p.rows;
+  m.head_tiles = p.head_tiles;
+  m.q_heads = a.q_heads;
+  m.kv_heads = a.kv_heads;
+  m.gt = p.head_tile;
+  m.tok_tile = p.tok_tile;
+  m.tok_tiles = p.tok_tiles;
+  m.n_query = a.n_query;
+  m.acc_scale = VB == 4 ? 16.0f : 1.0f;
+  m.sign = a.sign_v;
+  m.sign_bs = a.sign_bs;
+  m.lambda = a.lambda_v;
+  m.lambda_bs = a.lambda_bs;
+  m.out = a.out;
+  m.transform = a.transform;
+  P.tok_tile = p.tok_tile;
+  P.tok_tiles = p.tok_tiles;
+  P.rows = p.rows;
+  P.n_query = a.n_query;
+  P.window = a.window;
+  P.ring = a.ring;
   P.k_new = static_cast<const uint16_t*>(a.k_new);
   P.v_new = static_cast<const uint16_t*>(a.v_new);
   P.page_table = a.page_table;
@@ -1014,9 +1090,9 @@ hipError_t launch_q(const DecodeArgs& a, const DecodePlan& p, const WsLayout& w,
     hipLaunchKernelGGL((decode_kernel<D, KB, VB, NRB, true, G1>), grid, block, 0, s, P);  \
   else                                                                                \
     hipLaunchKernelGGL((decode_kernel<D, KB, VB, NRB, false, G1>), grid, block, 0, s, P);
-  switch ((p.head_tile + 3) / 4) {
+  switch ((p.rows + 3) / 4) {
     case 1:
-      if (p.head_tile == 1) {
+      if (p.rows == 1) {
         KVQ_DLAUNCH(1, true);
       } else {
         KVQ_DLAUNCH(1, false);
@@ -1043,7 +1119,7 @@ hipError_t launch_q(const DecodeArgs& a, const DecodePlan& p, const WsLayout& w,
 // The instances of one head dimension (each is built in a translation unit of its own).
 template <int D>
 hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
-  const WsLayout w = ws_layout(a.batch * a.kv_heads * p.head_tiles, p.head_tile, a.head_dim, p.max_chunks);
+  const WsLayout w = ws_layout(a.batch * a.kv_heads * p.head_tiles * p.tok_tiles, p.rows, a.head_dim, p.max_chunks);
   switch (a.k_bits * 10 + a.v_bits) {
     case 44: return launch_q<D, 4, 4>(a, p, w, s);
     case 84: return launch_q<D, 8, 4>(a, p, w, s);

@@ -46,12 +46,17 @@ struct CalibArgs {
   int transform;
 };
 
-// Split of a decode call into work-groups (shared by the quantized and the fp16 kernels).
+// Split of a decode / attention call into work-groups (shared by the quantized and the fp16
+// kernels).  A unit is (sequence, kv head, head tile, query-token tile); its rows are
+// tok_tile x head_tile (query token, head) pairs, at most 16 (8 at d = 256).
 struct DecodePlan {
-  int head_tile;   // query heads handled by one work-group (a divisor of G, <= 16)
+  int head_tile;   // query heads handled by one work-group (a divisor of G)
   int head_tiles;  // G / head_tile
+  int tok_tile;    // query tokens handled by one work-group (1 for single-token decode)
+  int tok_tiles;   // ceil(n_query / tok_tile)
+  int rows;        // head_tile * tok_tile
   int chunk;       // tokens per work-group
-  int n_chunks;    // ceil(seq_len / chunk)
+  int n_chunks;    // work-groups per unit
   int max_chunks;  // chunk count the workspace layout is laid out for
 };
 
@@ -82,6 +87,10 @@ struct DecodeArgs {
   // planes [num_pages, kv_heads, page_size, .]; page_size a multiple of 64
   const int32_t* page_table = nullptr;
   int page_size = 0, pages_per_seq = 0, num_pages = 0;
+  // several query tokens (q and out [batch, n_query, q_heads, d]; query i of a sequence of
+  // length L sits at position L - n_query + i and attends causally), a sliding window (0: none)
+  // and ring-buffer slots (token t at slot t % capacity)
+  int n_query = 1, window = 0, ring = 0;
 };
 
 struct DecodeF16Args {
@@ -135,8 +144,11 @@ constexpr int kQuantVecs = 16;  // vectors per block (MFMA columns)
 // Host-side planning (pure host code, no HIP call).
 QuantPlan plan_quantize(int head_dim, int64_t n_vec);
 DecodePlan plan_decode(int batch, int kv_heads, int q_heads, int head_dim, int seq_len, int max_seq_len, bool f16,
-                       bool append = false, bool paged = false);
+                       bool append = false, bool paged = false, int n_query = 1, int window = 0);
 size_t decode_workspace_bytes(int batch, int kv_heads, int q_heads, int head_dim, int max_seq_len);
+// workspace of the multi-token / windowed attention (both the contiguous and the paged call)
+size_t attn_workspace_bytes(int batch, int kv_heads, int q_heads, int head_dim, int max_seq_len, int n_query,
+                            int window);
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);

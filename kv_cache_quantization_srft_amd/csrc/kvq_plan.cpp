@@ -26,23 +26,41 @@ QuantPlan plan_quantize(int head_dim, int64_t n_vec) {
 }
 
 DecodePlan plan_decode(int batch, int kv_heads, int q_heads, int head_dim, int seq_len, int max_seq_len, bool f16,
-                       bool append, bool paged) {
+                       bool append, bool paged, int n_query, int window) {
   DecodePlan p{};
   const int G = q_heads / kv_heads;
-  // epilogue LDS holds 4 x tile x d floats; an appending call rotates the new K and V vectors
+  const int T = std::max(n_query, 1);
+  // epilogue LDS holds 4 x rows x d floats; an appending call rotates the new K and V vectors
   // in rows 14 and 15 of the query rotation
-  const int max_tile = head_dim == 128 ? (append ? 14 : 16) : 8;
-  int tile = 1;
-  for (int t = std::min(G, max_tile); t >= 1; --t)
-    if (G % t == 0) {
-      tile = t;
-      break;
+  const int max_rows = head_dim == 128 ? (append ? 14 : 16) : 8;
+  // (head tile, token tile) with rows <= max_rows and the fewest tiles per kv head (each tile reads
+  // the kv head's cache once); ties go to the larger head tile
+  int best_gt = 1, best_tt = 1;
+  long best_tiles = -1;
+  for (int gt = std::min(G, max_rows); gt >= 1; --gt) {
+    if (G % gt) continue;
+    const int tt = std::min(T, max_rows / gt);
+    const long tiles = long(G / gt) * ((T + tt - 1) / tt);
+    if (best_tiles < 0 || tiles < best_tiles) {
+      best_tiles = tiles;
+      best_gt = gt;
+      best_tt = tt;
     }
-  p.head_tile = tile;
-  p.head_tiles = G / tile;
-  const long units = long(batch) * kv_heads * p.head_tiles;
+  }
+  p.head_tile = best_gt;
+  p.head_tiles = G / best_gt;
+  p.tok_tile = best_tt;
+  p.tok_tiles = (T + best_tt - 1) / best_tt;
+  p.rows = best_gt * best_tt;
+  const long units = long(batch) * kv_heads * p.head_tiles * p.tok_tiles;
   const long cap_chunks = std::max(1L, (target_workgroups(head_dim) + units - 1) / units);
   const int align = token_align(f16);
+  // tokens one unit attends: its queries' prefix, or with a window the window of its first query
+  // through its last query, plus up to 63 tokens before the window's start (superblocks start at
+  // multiples of 64)
+  auto span = [&](int len) {
+    return window > 0 ? int(std::min<long>(len, long(window) + p.tok_tile - 1 + 63)) : len;
+  };
   auto chunk_for = [&](int len) {
     long per = (std::max(len, 1) + cap_chunks - 1) / cap_chunks;
     per = ((per + align - 1) / align) * align;
@@ -50,10 +68,10 @@ DecodePlan plan_decode(int batch, int kv_heads, int q_heads, int head_dim, int s
     if (paged) per = std::min<long>(per, 64L * align);
     return int(std::max<long>(align, per));
   };
-  p.chunk = chunk_for(seq_len);
-  p.n_chunks = (std::max(seq_len, 1) + p.chunk - 1) / p.chunk;
-  const int mc = chunk_for(max_seq_len);
-  p.max_chunks = std::max(p.n_chunks, (std::max(max_seq_len, 1) + mc - 1) / mc);
+  p.chunk = chunk_for(span(seq_len));
+  p.n_chunks = (std::max(span(seq_len), 1) + p.chunk - 1) / p.chunk;
+  const int mc = chunk_for(span(max_seq_len));
+  p.max_chunks = std::max(p.n_chunks, (std::max(span(max_seq_len), 1) + mc - 1) / mc);
   return p;
 }
 
@@ -63,7 +81,19 @@ size_t decode_workspace_bytes(int batch, int kv_heads, int q_heads, int head_dim
   for (int variant = 0; variant < 5; ++variant) {
     const DecodePlan p = plan_decode(batch, kv_heads, q_heads, head_dim, max_seq_len, max_seq_len, variant == 1,
                                      variant == 2 || variant == 4, variant >= 3);
-    const WsLayout w = ws_layout(batch * kv_heads * p.head_tiles, p.head_tile, head_dim, p.max_chunks);
+    const WsLayout w = ws_layout(batch * kv_heads * p.head_tiles * p.tok_tiles, p.rows, head_dim, p.max_chunks);
+    need = std::max(need, w.total);
+  }
+  return need;
+}
+
+size_t attn_workspace_bytes(int batch, int kv_heads, int q_heads, int head_dim, int max_seq_len, int n_query,
+                            int window) {
+  size_t need = 0;
+  for (int paged = 0; paged < 2; ++paged) {
+    const DecodePlan p = plan_decode(batch, kv_heads, q_heads, head_dim, max_seq_len, max_seq_len, false, false,
+                                     paged != 0, n_query, window);
+    const WsLayout w = ws_layout(batch * kv_heads * p.head_tiles * p.tok_tiles, p.rows, head_dim, p.max_chunks);
     need = std::max(need, w.total);
   }
   return need;

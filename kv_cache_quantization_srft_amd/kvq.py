@@ -23,7 +23,7 @@ EXPORTS = (
     "kvq_version", "kvq_status_string", "kvq_last_error_message", "kvq_codes_bytes", "kvq_scales_bytes",
     "kvq_quantize", "kvq_dequantize", "kvq_calibrate_lambda", "kvq_decode_attn_workspace_bytes",
     "kvq_decode_attn", "kvq_decode_attn_append", "kvq_decode_attn_paged", "kvq_decode_attn_fp16",
-    "kvq_launch_plan", "kvq_decode_attn_noalloc",
+    "kvq_launch_plan", "kvq_decode_attn_noalloc", "kvq_attn", "kvq_attn_workspace_bytes", "kvq_attn_launch_plan",
 )
 
 
@@ -57,7 +57,12 @@ class kvq_plan(ctypes.Structure):
     _fields_ = [("work_groups", ctypes.c_int64), ("head_tile", ctypes.c_int32), ("head_tiles", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("n_chunks", ctypes.c_int32), ("wave_tokens", ctypes.c_int32),
                 ("superblocks_per_wave", ctypes.c_int32), ("blocks", ctypes.c_int64),
-                ("blocks_per_work_group", ctypes.c_int64)]
+                ("blocks_per_work_group", ctypes.c_int64), ("query_tile", ctypes.c_int32),
+                ("query_tiles", ctypes.c_int32)]
+
+
+class kvq_attn_opts(ctypes.Structure):
+    _fields_ = [("n_query", ctypes.c_int32), ("window", ctypes.c_int32), ("ring", ctypes.c_int32)]
 
 
 _lib = None
@@ -105,6 +110,13 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_attn_noalloc.restype = ctypes.c_int
         L.kvq_decode_attn_noalloc.argtypes = [_LP, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _I64, _P, _P, _I64,
                                               ctypes.c_float, _P, _P]
+        L.kvq_attn.restype = ctypes.c_int
+        L.kvq_attn.argtypes = [_LP, ctypes.POINTER(kvq_attn_opts), _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P,
+                               _P, _P, _I64, _P, _P, _I64, ctypes.c_float, _P, _SZ, _P, _P]
+        L.kvq_attn_workspace_bytes.restype = _SZ
+        L.kvq_attn_workspace_bytes.argtypes = [_LP, ctypes.POINTER(kvq_attn_opts), _I32]
+        L.kvq_attn_launch_plan.restype = ctypes.c_int
+        L.kvq_attn_launch_plan.argtypes = [_LP, ctypes.POINTER(kvq_attn_opts), _I32, _I32, ctypes.POINTER(kvq_plan)]
         L.kvq_launch_plan.restype = ctypes.c_int
         L.kvq_launch_plan.argtypes = [_LP, ctypes.c_int, _I32, ctypes.POINTER(kvq_plan)]
         _lib = L
@@ -309,3 +321,45 @@ def kvq_launch_plan(layout, call, n) -> kvq_plan:
     out = kvq_plan()
     _check(lib().kvq_launch_plan(ctypes.byref(layout), c, n, ctypes.byref(out)))
     return out
+
+
+def make_attn_opts(n_query=1, window=0, ring=False) -> kvq_attn_opts:
+    return kvq_attn_opts(n_query, window, 1 if ring else 0)
+
+
+def kvq_attn_workspace_bytes(layout, opts, max_seq_len) -> int:
+    return lib().kvq_attn_workspace_bytes(ctypes.byref(layout), ctypes.byref(opts), max_seq_len)
+
+
+def kvq_attn_launch_plan(layout, opts, seq_len, paged=False) -> kvq_plan:
+    out = kvq_plan()
+    _check(lib().kvq_attn_launch_plan(ctypes.byref(layout), ctypes.byref(opts), seq_len, 1 if paged else 0,
+                                      ctypes.byref(out)))
+    return out
+
+
+def kvq_attn(layout, opts, q, k_codes, k_scales, v_codes, v_scales, page_table, pages_per_seq, page_size, num_pages,
+             seq_len, seq_lens, sign_k, sign_v, sign_batch_stride, lambda_k, lambda_v, lambda_batch_stride, sm_scale,
+             workspace, out, stream=None):
+    """page_table None: contiguous rows (planes sized by the layout); otherwise paged planes of
+    num_pages pages."""
+    import torch
+    d = layout.head_dim
+    rows = layout.batch * opts.n_query * layout.q_heads * d
+    if page_table is None:
+        kcb, vcb = kvq_codes_bytes(layout, layout.k_bits), kvq_codes_bytes(layout, layout.v_bits)
+        scb = kvq_scales_bytes(layout)
+    else:
+        kcb = _page_plane_bytes(layout, layout.k_bits, num_pages, page_size)
+        vcb = _page_plane_bytes(layout, layout.v_bits, num_pages, page_size)
+        scb = _page_plane_bytes(layout, 0, num_pages, page_size, scales=True)
+    _check(lib().kvq_attn(
+        ctypes.byref(layout), ctypes.byref(opts), _ptr(q, _f16(), "q", rows),
+        _ptr(k_codes, _u8(), "k_codes", min_bytes=kcb), _ptr(k_scales, _scale_t(), "k_scales", min_bytes=scb),
+        _ptr(v_codes, _u8(), "v_codes", min_bytes=vcb), _ptr(v_scales, _scale_t(), "v_scales", min_bytes=scb),
+        _ptr(page_table, torch.int32, "page_table", None if page_table is None else layout.batch * pages_per_seq),
+        pages_per_seq, page_size, num_pages, seq_len, _ptr(seq_lens, torch.int32, "seq_lens", layout.batch),
+        _ptr(sign_k, _f32(), "sign_k"), _ptr(sign_v, _f32(), "sign_v"), sign_batch_stride,
+        _ptr(lambda_k, _f32(), "lambda_k"), _ptr(lambda_v, _f32(), "lambda_v"), lambda_batch_stride,
+        float(sm_scale), _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(out, _f32(), "out", rows), _stream(stream)))

@@ -322,3 +322,47 @@ def test_launch_plan_errors(L):
     bad = kvq.make_layout(2, 2, 5, 128, 64)
     assert L.kvq_launch_plan(ctypes.byref(bad), 1, 8, ctypes.byref(out)) == 1    # q_heads % kv_heads
     assert L.kvq_launch_plan(ctypes.byref(kvq.make_layout(2, 2, 2, 96, 64)), 0, 8, ctypes.byref(out)) == 2
+
+
+def attn(L, lay, opts, seq_len=64, table=NULL, pps=0, ps=0, npg=0, ws=GOOD, ws_bytes=1 << 30, q=GOOD):
+    return L.kvq_attn(ctypes.byref(lay), opts if opts is None else ctypes.byref(opts), q, GOOD, GOOD, GOOD, GOOD, table,
+                      pps, ps, npg, seq_len, NULL, GOOD, GOOD, 0, NULL, NULL, 0, 0.0, ws, ws_bytes, GOOD, NULL)
+
+
+def test_attn_validation(L):
+    """kvq_attn rejects bad options on the host (status codes from kvq.h), before any HIP call."""
+    lay = layout(capacity=640)
+    ok_opts = kvq.make_attn_opts(4, 0)
+    assert attn(L, lay, None) == 1                                          # opts NULL
+    assert attn(L, lay, kvq.make_attn_opts(0, 0)) == 1                      # n_query < 1
+    assert attn(L, lay, kvq.make_attn_opts(2, -1)) == 1                     # window < 0
+    assert attn(L, lay, ok_opts, seq_len=641) == 1                          # beyond capacity, no ring
+    assert attn(L, lay, kvq.make_attn_opts(1, 0, ring=True), seq_len=5000) == 1   # ring needs a window
+    assert attn(L, lay, kvq.make_attn_opts(4, 638, ring=True), seq_len=5000) == 1  # W + T - 1 > capacity
+    assert attn(L, layout(capacity=600), kvq.make_attn_opts(1, 100, ring=True), seq_len=5000) == 2  # capacity % 64
+    assert attn(L, lay, ok_opts, table=GOOD, pps=10, ps=100, npg=8) == 2     # page size
+    assert attn(L, lay, ok_opts, table=GOOD, pps=4, ps=128, npg=8) == 1      # capacity != pps x page size
+    assert attn(L, lay, ok_opts, q=MIS) == 3
+    assert attn(L, lay, ok_opts, ws_bytes=1024) == 4
+    assert b"workspace" in L.kvq_last_error_message()
+    assert attn(L, layout(capacity=640, group_size=128), ok_opts) == 2       # decode reads groups of 16
+
+
+def test_attn_sizing_and_plan(L):
+    lay = kvq.make_layout(8, 2, 8, 128, 65536)
+    o = kvq.make_attn_opts(4, 0)
+    sizes = [kvq.kvq_attn_workspace_bytes(lay, o, s) for s in (64, 4096, 65536)]
+    assert all(s > 0 for s in sizes) and sizes == sorted(sizes)
+    # a window bounds the tokens a unit attends, and so the chunks and the workspace
+    ow = kvq.make_attn_opts(4, 512)
+    assert kvq.kvq_attn_workspace_bytes(lay, ow, 65536) == kvq.kvq_attn_workspace_bytes(lay, ow, 8192)
+    assert kvq.kvq_attn_workspace_bytes(lay, kvq.make_attn_opts(0, 0), 64) == 0
+    p = kvq.kvq_attn_launch_plan(lay, o, 4096)
+    assert (p.head_tile, p.query_tile, p.query_tiles) == (4, 4, 1)            # G 4 x 4 tokens = 16 rows
+    p = kvq.kvq_attn_launch_plan(kvq.make_layout(2, 2, 12, 128, 4096), kvq.make_attn_opts(3, 0), 4096)
+    assert (p.head_tile, p.query_tile, p.query_tiles) == (6, 2, 2)
+    p = kvq.kvq_attn_launch_plan(kvq.make_layout(2, 2, 8, 256, 4096), kvq.make_attn_opts(5, 0), 4096)
+    assert p.head_tile * p.query_tile <= 8
+    p1 = kvq.kvq_attn_launch_plan(lay, kvq.make_attn_opts(1, 0), 4096)
+    p2 = kvq.kvq_launch_plan(lay, "decode", 4096)
+    assert (p1.work_groups, p1.chunk, p1.n_chunks, p1.head_tile) == (p2.work_groups, p2.chunk, p2.n_chunks, p2.head_tile)

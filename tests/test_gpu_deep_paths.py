@@ -40,6 +40,7 @@ def _lengths(rng, B, S):
 
 def _units(rng, B, Hkv, n, lens):
     """Sampled (sequence, kv head) pairs: the first and last rows, every special-length row, random."""
+    n = min(n, B * Hkv)
     picks = {(0, 0), (B - 1, Hkv - 1)}
     picks |= {(b, int(rng.integers(Hkv))) for b in range(min(B, 10))}
     while len(picks) < n:
