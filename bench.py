@@ -402,6 +402,13 @@ def main():
     nb = max(R, Rf)
     res_bq = timer.run(lambda i: quantize_all(planes[i % R], *kv16[i % Rf]), nb, 2 * nb, args.warmup)
 
+    # the same write path with the rotation as an in-register FFT (one lane per vector)
+    def quantize_all_fft(p, xk, xv):
+        kvq.kvq_quantize_fft(lay, w.k_bits, xk, 0, S, s, 0, lam_k, lbs, p[0], p[1])
+        kvq.kvq_quantize_fft(lay, w.v_bits, xv, 0, S, s, 0, lam_v, lbs, p[2], p[3])
+
+    res_bqf = timer.run(lambda i: quantize_all_fft(planes[i % R], *kv16[i % Rf]), nb, 2 * nb, args.warmup)
+
     # paged cache: every copy cut into pages of PAGE tokens, stored in a shuffled page order and
     # addressed through a page table (kvq_decode_attn_paged); same tokens, same bytes read
     page = 256 if S % 256 == 0 else 64
@@ -544,7 +551,13 @@ def main():
         "quantize_bulk": {"Mvectors_per_s": round(n_vec / (res_bq["ms_mean"] * 1e-3) / 1e6, 2),
                           "GBps_moved": round(bq_bytes / (res_bq["ms_mean"] * 1e-3) / 1e9, 2),
                           "frac_hbm_peak": round(bq_bytes / (res_bq["ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                          "vectors": n_vec, "ms": round(res_bq["ms_mean"], 5)},
+                          "vectors": n_vec, "ms": round(res_bq["ms_mean"], 5),
+                          "kernel": "quantize_mfma_kernel (rotation as a matrix product on MFMA)"},
+        "quantize_bulk_fft": {"Mvectors_per_s": round(n_vec / (res_bqf["ms_mean"] * 1e-3) / 1e6, 2),
+                              "GBps_moved": round(bq_bytes / (res_bqf["ms_mean"] * 1e-3) / 1e9, 2),
+                              "frac_hbm_peak": round(bq_bytes / (res_bqf["ms_mean"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                              "ms": round(res_bqf["ms_mean"], 5),
+                              "kernel": "quantize_fft_kernel (kvq_quantize_fft: in-register FFT, one lane per vector)"},
         "attn_speculative_4": {
             "GBps": round(q_bytes / (res_spec["ms_mean"] * 1e-3) / 1e9, 2), "ms": round(res_spec["ms_mean"], 5),
             "query_tokens": n_spec, "rows_per_work_group": pl_spec.head_tile * pl_spec.query_tile,

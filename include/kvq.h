@@ -123,6 +123,19 @@ kvq_status kvq_quantize(const kvq_layout* layout, int32_t bits, const void* x_f1
                         void* scales, void* stream);
 
 /*
+ * kvq_quantize_fft -- the same write path as kvq_quantize, with the rotation computed as an
+ * in-register radix-2 FFT of length head_dim/2 plus the Hermitian unpack ([QF] Methodology 1 and
+ * 2: the FFT, the Hermitian pack and the rest of the fused write kernel's steps), one GPU lane per vector,
+ * instead of as a matrix product on the matrix cores.  Same arguments, validation, outputs and
+ * error codes as kvq_quantize; its codes and scales meet the write path's bar against the same
+ * definition (they may differ from kvq_quantize's on float32 near-ties of the rounding).
+ */
+kvq_status kvq_quantize_fft(const kvq_layout* layout, int32_t bits, const void* x_f16, int32_t pos,
+                            int32_t n_tok, const float* sign, int64_t sign_batch_stride,
+                            const float* lambda, int64_t lambda_batch_stride, void* codes,
+                            void* scales, void* stream);
+
+/*
  * kvq_dequantize -- inverse of the write path ([QF] Methodology 2 run backwards: unpack, times
  * scale and lambda, inverse rotation, sign), for inspection and tests.
  *   out[b, h, t, :] = s * SRFT^-1(lambda * code * scale) for tokens pos .. pos+n_tok-1,

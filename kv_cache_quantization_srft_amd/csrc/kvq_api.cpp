@@ -194,6 +194,26 @@ kvq_status kvq_quantize(const kvq_layout* L, int32_t bits, const void* x_f16, in
   return hip_status(kvq_impl::launch_quantize(a, static_cast<hipStream_t>(stream)), fn);
 }
 
+kvq_status kvq_quantize_fft(const kvq_layout* L, int32_t bits, const void* x_f16, int32_t pos, int32_t n_tok,
+                            const float* sign, int64_t sign_batch_stride, const float* lambda,
+                            int64_t lambda_batch_stride, void* codes, void* scales, void* stream) {
+  const char* fn = "kvq_quantize_fft";
+  KVQ_TRY(check_layout(L, fn));
+  KVQ_TRY(check_bits(bits, fn, "bits"));
+  KVQ_TRY(check_range(L, pos, n_tok, fn));
+  KVQ_TRY(check_ptr(x_f16, 16, fn, "x"));
+  KVQ_TRY(check_ptr(sign, 4, fn, "sign"));
+  KVQ_TRY(check_opt_ptr(lambda, 4, fn, "lambda"));
+  KVQ_TRY(check_ptr(codes, 16, fn, "codes"));
+  KVQ_TRY(check_ptr(scales, 16, fn, "scales"));
+  KVQ_TRY(check_strides(sign_batch_stride, lambda_batch_stride, fn));
+  kvq_impl::QuantArgs a{L->batch, L->kv_heads, L->head_dim, bits, L->capacity, pos, n_tok, x_f16, sign,
+                        sign_batch_stride, lambda, lambda_batch_stride, codes, scales};
+  a.transform = L->transform;
+  a.group = L->group_size;
+  return hip_status(kvq_impl::launch_quantize_fft(a, static_cast<hipStream_t>(stream)), fn);
+}
+
 kvq_status kvq_dequantize(const kvq_layout* L, int32_t bits, const void* codes, const void* scales, int32_t pos,
                           int32_t n_tok, const float* sign, int64_t sign_batch_stride, const float* lambda,
                           int64_t lambda_batch_stride, float* out, void* stream) {

@@ -151,6 +151,8 @@ size_t attn_workspace_bytes(int batch, int kv_heads, int q_heads, int head_dim, 
                             int window);
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+// the write path with the rotation as an in-register FFT on the vector ALUs (comparison form)
+hipError_t launch_quantize_fft(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
 hipError_t launch_calibrate(const CalibArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream);

@@ -21,7 +21,7 @@ STATUS_NAMES = {
 }
 EXPORTS = (
     "kvq_version", "kvq_status_string", "kvq_last_error_message", "kvq_codes_bytes", "kvq_scales_bytes",
-    "kvq_quantize", "kvq_dequantize", "kvq_calibrate_lambda", "kvq_decode_attn_workspace_bytes",
+    "kvq_quantize", "kvq_quantize_fft", "kvq_dequantize", "kvq_calibrate_lambda", "kvq_decode_attn_workspace_bytes",
     "kvq_decode_attn", "kvq_decode_attn_append", "kvq_decode_attn_paged", "kvq_decode_attn_fp16",
     "kvq_launch_plan", "kvq_decode_attn_noalloc", "kvq_attn", "kvq_attn_workspace_bytes", "kvq_attn_launch_plan",
 )
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_scales_bytes.argtypes = [_LP]
         L.kvq_quantize.restype = ctypes.c_int
         L.kvq_quantize.argtypes = [_LP, _I32, _P, _I32, _I32, _P, _I64, _P, _I64, _P, _P, _P]
+        L.kvq_quantize_fft.restype = ctypes.c_int
+        L.kvq_quantize_fft.argtypes = [_LP, _I32, _P, _I32, _I32, _P, _I64, _P, _I64, _P, _P, _P]
         L.kvq_dequantize.restype = ctypes.c_int
         L.kvq_dequantize.argtypes = [_LP, _I32, _P, _P, _I32, _I32, _P, _I64, _P, _I64, _P, _P]
         L.kvq_calibrate_lambda.restype = ctypes.c_int
@@ -194,8 +196,20 @@ def kvq_decode_attn_workspace_bytes(layout: kvq_layout, max_seq_len: int) -> int
 
 def kvq_quantize(layout, bits, x, pos, n_tok, sign, sign_batch_stride, lam, lambda_batch_stride, codes, scales,
                  stream=None):
+    _quantize_call(lib().kvq_quantize, layout, bits, x, pos, n_tok, sign, sign_batch_stride, lam,
+                   lambda_batch_stride, codes, scales, stream)
+
+
+def kvq_quantize_fft(layout, bits, x, pos, n_tok, sign, sign_batch_stride, lam, lambda_batch_stride, codes, scales,
+                     stream=None):
+    _quantize_call(lib().kvq_quantize_fft, layout, bits, x, pos, n_tok, sign, sign_batch_stride, lam,
+                   lambda_batch_stride, codes, scales, stream)
+
+
+def _quantize_call(fn, layout, bits, x, pos, n_tok, sign, sign_batch_stride, lam, lambda_batch_stride, codes, scales,
+                   stream):
     d = layout.head_dim
-    _check(lib().kvq_quantize(
+    _check(fn(
         ctypes.byref(layout), bits, _ptr(x, _f16(), "x", layout.batch * layout.kv_heads * n_tok * d), pos, n_tok,
         _ptr(sign, _f32(), "sign"), sign_batch_stride, _ptr(lam, _f32(), "lambda"), lambda_batch_stride,
         _ptr(codes, _u8(), "codes", min_bytes=kvq_codes_bytes(layout, bits)),

@@ -45,9 +45,11 @@ def planes(layout, bits, fill=0xAB):
     return codes, scales
 
 
-def gpu_quantize(x16, s, lam, bits, capacity=None, pos=0, sign_bs=0, lambda_bs=None, transform="srft", group=16):
+def gpu_quantize(x16, s, lam, bits, capacity=None, pos=0, sign_bs=0, lambda_bs=None, transform="srft", group=16,
+                 entry=None):
     """x16 [B, H, n, d] fp16; lam [B?, H, d] or None.  Returns (codes u8 [B,H,cap,d*bits/8],
-    scales f16 [B,H,cap,d/group]) as numpy, plus the layout."""
+    scales f16 [B,H,cap,d/group]) as numpy, plus the layout.  entry: the write-path entry point
+    (kvq.kvq_quantize by default, or kvq.kvq_quantize_fft)."""
     B, H, n, d = x16.shape
     cap = capacity or (pos + n)
     lay = kvq.make_layout(B, H, H, d, cap, k_bits=bits, v_bits=4, transform=transform, group_size=group)
@@ -55,8 +57,8 @@ def gpu_quantize(x16, s, lam, bits, capacity=None, pos=0, sign_bs=0, lambda_bs=N
     lam_t = None if lam is None else dev(np.asarray(lam, np.float32))
     if lambda_bs is None:
         lambda_bs = 0 if lam is None or np.asarray(lam).ndim == 2 else H * d
-    kvq.kvq_quantize(lay, bits, dev(x16), pos, n, dev(np.asarray(s, np.float32)), sign_bs, lam_t, lambda_bs,
-                     codes, scales)
+    (entry or kvq.kvq_quantize)(lay, bits, dev(x16), pos, n, dev(np.asarray(s, np.float32)), sign_bs, lam_t,
+                                lambda_bs, codes, scales)
     torch.cuda.synchronize()
     cb = codes.cpu().numpy().reshape(B, H, cap, d * bits // 8)
     sc = scales.cpu().numpy().view(np.float16).reshape(B, H, cap, d // group)
