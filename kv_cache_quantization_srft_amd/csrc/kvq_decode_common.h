@@ -10,6 +10,7 @@
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_lds_rot.h"
 
 namespace kvq_impl {
 namespace dec {
@@ -361,15 +362,19 @@ constexpr int merge_lds_floats() {
   return 16 * D + 16 * 32 + 32;
 }
 
-// Operands of the inverse rotation of one wave (output blocks w, w + 4, ...) from the global
-// inverse table, all loaded ahead, and the output signs.
+// Values the inverse rotation takes from global memory, loaded ahead of the merge: this lane's
+// twiddles and output signs.
 template <int D>
 struct RotOps {
-  static constexpr int NBW = D / 16 / kWaves, NSTEP = D / 32;
-  static constexpr int NPRE = NBW;
-  uint4 bh[NPRE][NSTEP], bl[NPRE][NSTEP];
-  float sg[NBW];
+  RotTw<D> tw;
+  float sg[RotGeom<D>::E];
 };
+
+template <int D>
+__device__ __forceinline__ void rot_prefetch(RotOps<D>& o, const MergeArgs& a, int b) {
+  load_rot_tw<D, true>(o.tw);
+  load_inv_signs<D>(o.sg, a.sign + b * a.sign_bs, a.transform);
+}
 
 // Sequence and kv head of a unit; orow0 = output row of the unit's row 0, tt = its token tile.
 __device__ __forceinline__ void unit_coords(const MergeArgs& a, int unit, int& b, int& kvh, int64_t& orow0) {
@@ -390,78 +395,23 @@ __device__ __forceinline__ int64_t out_row(const MergeArgs& a, int unit, int64_t
   return orow0 + int64_t(i) * a.q_heads + (r - i * a.gt);
 }
 
+// out[h][n] = s_n (SRFT^-1 y[h])_n (SRHT: s_n d^-1/2 (H y[h])_n) for the rows h < head_tile of
+// the unit (the output rows of query tokens past the last are skipped), with y in LDS (pitch D).
 template <int D>
-__device__ __forceinline__ void rot_prefetch(RotOps<D>& o, const MergeArgs& a, int unit) {
+__device__ __forceinline__ void rotate_store(const MergeArgs& a, int unit, const float* y, const RotOps<D>& o) {
   int b, kvh;
   int64_t orow0;
   unit_coords(a, unit, b, kvh, orow0);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int j = 0; j < RotOps<D>::NBW; ++j) o.sg[j] = a.sign[b * a.sign_bs + 16 * (w + kWaves * j) + (lane & 15)];
-  const MfmaQTable<D>& T = mqtable<D>(a.transform);
-#pragma unroll
-  for (int j = 0; j < RotOps<D>::NPRE; ++j)
-#pragma unroll
-    for (int s = 0; s < RotOps<D>::NSTEP; ++s) {
-      o.bh[j][s] = ld4(T.inv_hi[w + kWaves * j][s][lane]);
-      o.bl[j][s] = ld4(T.inv_lo[w + kWaves * j][s][lane]);
-    }
-}
-
-// out[h][n] = s_n sum_c y[h][c] Q[c][n] for the heads h < head_tile of the unit, as MFMAs with
-// A = y split into fp16 hi + lo and B = 16 Q (the 1/16 is applied with the sign).
-template <int D>
-__device__ __forceinline__ void rotate_store(const MergeArgs& a, int unit, const float (*y)[D], const RotOps<D>& o) {
-  constexpr int NSTEP = D / 32, NBW = D / 16 / kWaves;
-  int b, kvh;
-  int64_t orow0;
-  unit_coords(a, unit, b, kvh, orow0);
-  const int GT = a.head_tile;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int n16 = lane & 15, r4 = lane >> 4;
-  // A operands: y[head n16][32 s + 8 r4 + (0..7)] split into hi + lo
-  v8h ahi[NSTEP], alo[NSTEP];
-#pragma unroll
-  for (int s = 0; s < NSTEP; ++s) {
-    const float4 y0 = *reinterpret_cast<const float4*>(&y[n16][32 * s + 8 * r4]);
-    const float4 y1 = *reinterpret_cast<const float4*>(&y[n16][32 * s + 8 * r4 + 4]);
-    uint32_t h4[4], l4[4];
-    split_pair(y0.x, y0.y, h4[0], l4[0]);
-    split_pair(y0.z, y0.w, h4[1], l4[1]);
-    split_pair(y1.x, y1.y, h4[2], l4[2]);
-    split_pair(y1.z, y1.w, h4[3], l4[3]);
-    ahi[s] = as_v8h(h4[0], h4[1], h4[2], h4[3]);
-    alo[s] = as_v8h(l4[0], l4[1], l4[2], l4[3]);
-  }
-#pragma unroll
-  for (int j = 0; j < NBW; ++j) {
-    const int nb = w + kWaves * j;
-    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int s = 0; s < NSTEP; ++s) {
-      uint4 ph, pl;
-      if (j < RotOps<D>::NPRE) {
-        ph = o.bh[j < RotOps<D>::NPRE ? j : 0][s];
-        pl = o.bl[j < RotOps<D>::NPRE ? j : 0][s];
-      } else {
-        const MfmaQTable<D>& T = mqtable<D>(a.transform);
-        ph = ld4(T.inv_hi[nb][s][lane]);
-        pl = ld4(T.inv_lo[nb][s][lane]);
-      }
-      const v8h bhi = as_v8h(ph.x, ph.y, ph.z, ph.w), blo = as_v8h(pl.x, pl.y, pl.z, pl.w);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[s], bhi, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[s], blo, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[s], bhi, acc, 0, 0, 0);
-    }
-    const int n = 16 * nb + n16;
-    const float sg = (o.sg[j] < 0.0f ? -1.0f : 1.0f) * 0.0625f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * r4 + i;
-      const int64_t orow = out_row(a, unit, orow0, h);
-      if (h < GT && orow >= 0) a.out[orow * D + n] = acc[i] * sg;
-    }
-  }
+  inv_wave<D>(
+      y, D, a.head_tile, a.transform, o.tw, o.sg,
+      [&](int h, int n, float v0, float v1) {
+        const int64_t orow = out_row(a, unit, orow0, h);
+        if (orow >= 0) *reinterpret_cast<float2*>(a.out + orow * D + n) = make_float2(v0, v1);
+      },
+      [&](int h, int n, float v) {
+        const int64_t orow = out_row(a, unit, orow0, h);
+        if (orow >= 0) a.out[orow * D + n] = v;
+      });
 }
 
 // Merge of the n_chunks partials of one unit from the workspace (the last work-group to
@@ -505,7 +455,7 @@ __device__ __forceinline__ void merge_unit(const MergeArgs& a, int unit, float* 
     }
   }
   RotOps<D> ro;
-  if constexpr (ROT) rot_prefetch<D>(ro, a, unit);
+  if constexpr (ROT) rot_prefetch<D>(ro, a, b);
   // per-head chunk weights exp2(m_i - M) and 1/l, one wave per head
   for (int h = w; h < GT; h += kWaves) {
     float mv[2], lv[2];
@@ -573,7 +523,7 @@ __device__ __forceinline__ void merge_unit(const MergeArgs& a, int unit, float* 
     for (int q = threadIdx.x + NQ * kThreads; 4 * q < 16 * D; q += kThreads)
       *reinterpret_cast<float4*>(&y[(4 * q) / D][(4 * q) % D]) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     __syncthreads();
-    rotate_store<D>(a, unit, y, ro);
+    rotate_store<D>(a, unit, &y[0][0], ro);
   }
 }
 
@@ -593,7 +543,7 @@ __device__ __forceinline__ void finish_direct(float (&m_run)[NSLOT], float (&l_r
   int64_t orow0;
   unit_coords(a, unit, b, kvh, orow0);
   RotOps<D> ro;
-  if constexpr (ROT) rot_prefetch<D>(ro, a, unit);
+  if constexpr (ROT) rot_prefetch<D>(ro, a, b);
   float4 lam4[NQ];
 #pragma unroll
   for (int k = 0; k < NQ; ++k) {
@@ -674,7 +624,7 @@ __device__ __forceinline__ void finish_direct(float (&m_run)[NSLOT], float (&l_r
       if (q < 16 * D / 4) *reinterpret_cast<float4*>(&y[(4 * q) / D][(4 * q) % D]) = yv[k];
     }
     __syncthreads();
-    rotate_store<D>(a, unit, y, ro);
+    rotate_store<D>(a, unit, &y[0][0], ro);
   }
 }
 

@@ -67,7 +67,10 @@ struct QGeom {
   static constexpr int LDS_P = 32 * kSB * 2;  // p as fp16 hi and lo parts, 16 heads each
   static constexpr int LDS_WAVE = LDS_V + LDS_S + LDS_K + LDS_P + 16 * 4;
   static constexpr int LDS_EPI = (kWaves * 16 * 2 + 16 * kWaves + 32 + kWaves * (D == 128 ? 16 : 8) * D) * 4;
-  static constexpr int LDS_Q = 4 * NS * 3 * 1024 + 256;  // prologue: digit operands + head maxima
+  // prologue: digit operands (256 bytes per operand: 4 row blocks x NS steps x 3 digits at most),
+  // head maxima, rotation scratch
+  static constexpr int DIG_BYTES = 4 * NS * 3 * 256;
+  static constexpr int LDS_Q = DIG_BYTES + 256 + 16 * RotGeom<D>::PITCH * 4;
   static constexpr int LDS_M = merge_lds_floats<D>() * 4;
   // append staging: K codes, K scales, V codes, V scales of the new token (16-byte aligned parts)
   static constexpr int APP_KS = KRB, APP_V = KRB + NG * 2, APP_VS = APP_V + VRB, APP_BYTES = APP_VS + NG * 2;
@@ -622,7 +625,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
     const QDecodeParams P) {
   using Gm = QGeom<D, KB, VB>;
   constexpr int NS = Gm::NS, NG = Gm::NG;
-  constexpr int NSTEP = D / 32, NBW = D / 16 / kWaves;
+  constexpr int NBW = D / 16 / kWaves;
   __shared__ __align__(16) uint8_t smem[Gm::LDS];
   __shared__ int last_flag;
   __shared__ __align__(16) uint8_t appbuf[Gm::APP_BYTES];
@@ -694,114 +697,84 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
 
   // ---------------- prologue: rotated query -> int8 digit operands ----------------
   // Its few loads go out first (loads complete in issue order), then the first superblock's.
-  // Every load here is unconditional (absent rows and a null lambda read valid memory whose
-  // value is then discarded), so that all of them are in flight together.
-  // A = the fp16 query of head row n16, signs flipped in the fp16 bits (exact).  An appending
+  // Rows of the rotation: row n = (query token i0 + n / GT, head h0 + n % GT); an appending
   // work-group (the one holding position L - 1 of its row; the head tile is then at most 14)
   // also rotates the new K vector as row 14 (signs s_K) and the new V vector as row 15 (s_V).
+  // Every load is unconditional per row (a null lambda reads valid memory whose value is then
+  // discarded), so that all of them are in flight together.
   const int t_app = L - 1;
   const bool app = APP && t_app >= t_begin && t_app < t_end;  // work-group uniform
-  const bool nrow = app && n16 >= 14;
-  // row n16 = (query token i0 + n16 / GT, head h0 + n16 % GT)
-  const int qr = min(n16, ROWS - 1);
-  const int qi = min(i0 + qr / GT, P.n_query - 1);
-  const bool live = (n16 < ROWS && i0 + n16 / GT < P.n_query) || nrow;
   const float* srow_k = P.sign_k + b * P.sign_bs;
-  const uint16_t* qrow = nrow ? (n16 == 14 ? P.k_new : P.v_new) + (int64_t(b) * P.kv_heads + kvh) * D
-                              : P.q + ((int64_t(b) * P.n_query + qi) * P.q_heads + h0 + qr % GT) * D;
-  const float* srow = nrow && n16 == 15 ? P.merge.sign + b * P.sign_bs : srow_k;
-  uint4 qv[NSTEP];
-  float4 sv0[NSTEP], sv1[NSTEP];
-#pragma unroll
-  for (int s = 0; s < NSTEP; ++s) {
-    qv[s] = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * r4);
-    sv0[s] = *reinterpret_cast<const float4*>(srow + 32 * s + 8 * r4);
-    sv1[s] = *reinterpret_cast<const float4*>(srow + 32 * s + 8 * r4 + 4);
-  }
-  // lambda_K and lambda_V of this lane's channels c = 16 (w + 4 j) + n16 (1 where absent)
+  const float* srow_v = P.merge.sign + b * P.sign_bs;
+  FwdIn<D> fin;
+  fwd_load<D>(fin, P.merge.transform, [&](int n, const uint16_t*& x, const float*& sg) -> bool {
+    if (app && n >= 14) {
+      x = (n == 14 ? P.k_new : P.v_new) + (int64_t(b) * P.kv_heads + kvh) * D;
+      sg = n == 14 ? srow_k : srow_v;
+      return true;
+    }
+    const int qr = min(n, ROWS - 1);
+    const int qi = min(i0 + qr / GT, P.n_query - 1);
+    x = P.q + ((int64_t(b) * P.n_query + qi) * P.q_heads + h0 + qr % GT) * D;
+    sg = srow_k;
+    return n < ROWS && i0 + n / GT < P.n_query;
+  });
+  RotTw<D> rtw;
+  load_rot_tw<D, false>(rtw);
+  // lambda_K of the channels this lane's query values take: c = 16 (w + 4 j) + kbyte_channel(n16),
+  // so that the four lanes of a quad hold the four bytes of one dword of the score operand
+  // (1 where absent); the append decision takes channel 16 (w + 4 j) + n16 of both lambdas
   const int64_t lofs = b * P.lambda_bs + int64_t(kvh) * D;
   const float* lkrow = P.lambda_k ? P.lambda_k + lofs : srow_k;
   const float* lvrow = P.merge.lambda ? P.merge.lambda + lofs : srow_k;
-  float nlk[NBW], nlv[NBW];
+  const int qch = kbyte_channel<KB>(n16);
+  float nlk[NBW], alk[NBW], alv[NBW];
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
-    nlk[j] = lkrow[16 * (w + kWaves * j) + n16];
-    nlv[j] = lvrow[16 * (w + kWaves * j) + n16];
-  }
-
-  // The B operands of this wave's channel blocks come from the global forward table (16 Q as
-  // fp16 hi + lo in operand order), all loaded here.
-  constexpr int NPRE = NBW;
-  const MfmaQTable<D>& T = mqtable<D>(P.merge.transform);
-  uint4 tbh[NPRE][NSTEP], tbl[NPRE][NSTEP];
-#pragma unroll
-  for (int j = 0; j < NPRE; ++j)
-#pragma unroll
-    for (int s = 0; s < NSTEP; ++s) {
-      tbh[j][s] = ld4(T.fwd_hi[w + kWaves * j][s][lane]);
-      tbl[j][s] = ld4(T.fwd_lo[w + kWaves * j][s][lane]);
+    nlk[j] = lkrow[16 * (w + kWaves * j) + qch];
+    if constexpr (APP) {
+      alk[j] = lkrow[16 * (w + kWaves * j) + n16];
+      alv[j] = lvrow[16 * (w + kWaves * j) + n16];
     }
+  }
 
   SBRegs<D, KB, VB> ra;
   int base = t_begin + w * kSB;
   int pos = P.ring ? base % P.capacity : base;  // row position of this wave's superblock
   if (base < t_end) load_superblock<D, KB, VB>(ra, kc, ks, vc, vs, sb_slot(pos, 0), min(L - base, kSB), lane);
 
-  // LDS of the prologue (aliases the main-loop tiles): digit operands, per-wave head maxima
-  constexpr int kDigBytes = (G1 ? 1 : NRB * 3) * NS * 1024;
-  uint8_t* dig = smem;
+  // LDS of the prologue (aliases the main-loop tiles): digit operands, per-wave head maxima, and
+  // the rotated rows
+  constexpr int kDigBytes = Gm::DIG_BYTES;
+  uint32_t* dig = reinterpret_cast<uint32_t*>(smem);
   float* pmax = reinterpret_cast<float*>(smem + kDigBytes);  // [kWaves][16]
-  for (int i = threadIdx.x; i < kDigBytes / 16; i += kThreads)
-    reinterpret_cast<uint4*>(dig)[i] = make_uint4(0u, 0u, 0u, 0u);
+  float* qo = reinterpret_cast<float*>(smem + kDigBytes + 256);  // [16][PITCH] rotated rows
   float lam[NBW];
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
     nlk[j] = P.lambda_k ? nlk[j] : 1.0f;
-    nlv[j] = P.merge.lambda ? nlv[j] : 1.0f;
-    lam[j] = nlk[j] * P.score_scale * 0.0625f;
+    lam[j] = nlk[j] * P.score_scale;
+    if constexpr (APP) {
+      alk[j] = P.lambda_k ? alk[j] : 1.0f;
+      alv[j] = P.merge.lambda ? alv[j] : 1.0f;
+    }
   }
-  v8h aq[NSTEP];
-#pragma unroll
-  for (int s = 0; s < NSTEP; ++s) {
-    uint4 v = live ? qv[s] : make_uint4(0u, 0u, 0u, 0u);
-    const float4 s0 = sv0[s], s1 = sv1[s];
-    v.x ^= (s0.x < 0.0f ? 0x8000u : 0u) | (s0.y < 0.0f ? 0x80000000u : 0u);
-    v.y ^= (s0.z < 0.0f ? 0x8000u : 0u) | (s0.w < 0.0f ? 0x80000000u : 0u);
-    v.z ^= (s1.x < 0.0f ? 0x8000u : 0u) | (s1.y < 0.0f ? 0x80000000u : 0u);
-    v.w ^= (s1.z < 0.0f ? 0x8000u : 0u) | (s1.w < 0.0f ? 0x80000000u : 0u);
-    aq[s] = as_v8h(v.x, v.y, v.z, v.w);
-  }
+  fwd_wave<D>(fin, rtw, P.merge.transform, qo);
   __syncthreads();
-  // q_hat[h][c] * lambda_c * score_scale for head h = 4 r4 + i and channel c = 16 (w + 4j) + n16
-  // (hi and lo products in separate chains, added at the end, as the write path does)
+  constexpr int QP = RotGeom<D>::PITCH;
+  // q_hat[h][c] * lambda_c * score_scale for head h = 4 r4 + i and channel c = 16 (w + 4j) + qch
   float qv_[NBW][4];
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
-    v4f qa = {0.0f, 0.0f, 0.0f, 0.0f}, ql = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int g = w + kWaves * j;
 #pragma unroll
-    for (int s = 0; s < NSTEP; ++s) {
-      uint4 ph, pl;
-      if (j < NPRE) {
-        ph = tbh[j < NPRE ? j : 0][s];
-        pl = tbl[j < NPRE ? j : 0][s];
-      } else {
-        ph = ld4(T.fwd_hi[w + kWaves * j][s][lane]);
-        pl = ld4(T.fwd_lo[w + kWaves * j][s][lane]);
-      }
-      const v8h bh = as_v8h(ph.x, ph.y, ph.z, ph.w), bl = as_v8h(pl.x, pl.y, pl.z, pl.w);
-      qa = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], bh, qa, 0, 0, 0);
-      ql = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[s], bl, ql, 0, 0, 0);
-    }
-    qa += ql;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) qv_[j][i] = qa[i] * lam[j];
+    for (int i = 0; i < 4; ++i) qv_[j][i] = qo[(4 * r4 + i) * QP + 16 * g + qch] * lam[j];
     if (app) {
       // the write path on rows 14 (K) and 15 (V), lanes 48..63, channel c = 16 g + n16:
-      // u = 16 SRFT(x)_c / (16 lambda_c), group absmax over the row's 16 lanes, fp16 scale,
-      // rounded codes, packed into the LDS staging of the new token
-      const int g = w + kWaves * j;
-      const float uk = qa[2] * __builtin_amdgcn_rcpf(16.0f * nlk[j]);
-      const float uv = qa[3] * __builtin_amdgcn_rcpf(16.0f * nlv[j]);
+      // u = SRFT(x)_c / lambda_c, group absmax over the row's 16 lanes, fp16 scale, rounded
+      // codes, packed into the LDS staging of the new token
+      const float uk = qo[14 * QP + 16 * g + n16] * __builtin_amdgcn_rcpf(alk[j]);
+      const float uv = qo[15 * QP + 16 * g + n16] * __builtin_amdgcn_rcpf(alv[j]);
       const _Float16 shk = static_cast<_Float16>(scale_of<KB>(row_max16(fabsf(uk))));
       const _Float16 shv = static_cast<_Float16>(scale_of<VB>(row_max16(fabsf(uv))));
       const float sfk = static_cast<float>(shk), sfv = static_cast<float>(shv);
@@ -907,16 +880,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
     rhi[rb] = real ? max(pr + 1, 0) : 0x7fffffff;
     rlo[rb] = real && P.window > 0 ? max(pr + 1 - P.window, 0) : 0;
   }
-  // the three int8 digits of every channel (Q = 65536 hi + 256 mid + lo), scattered into the score
-  // MFMA's A operands: for (row block rb, step s, digit dg) lane l holds row r = l%16 = (head
-  // 4rb + r/4, slot r%4) and the k bytes of lane group l/16; it is non-zero only when
-  // l/16 == r%4, where the 16 bytes are the digits of group g = (r%4) NS + s.  G1: one operand
-  // per step s, row r = 4 slot + digit (row 4 slot + 3 zero), non-zero where l/16 == slot.
+  // the three int8 digits of every channel (Q = 65536 hi + 256 mid + lo) as the score MFMA's A
+  // operands.  For (row block rb, step s, digit dg) lane l holds row r = l%16 = (head 4rb + r/4,
+  // slot r%4) and the k bytes of lane group l/16; it is non-zero only when l/16 == r%4, where the
+  // 16 bytes are the digits of group g = (r%4) NS + s in the byte order of the widened K codes.
+  // G1: one operand per step s, row r = 4 slot + digit (row 4 slot + 3 zero), non-zero where
+  // l/16 == slot.  Only the non-zero lanes' 16 bytes are staged: 256 bytes per operand, at
+  // (4 slot + head in block) * 16 (G1: (4 slot + digit) * 16).  The lanes of a quad hold the
+  // four bytes of one dword (channel kbyte_channel(n16)); two DPP swaps assemble it.
   {
-    int bt_of_c = 0;  // byte of the widened K codes that holds channel n16 of a group
-#pragma unroll
-    for (int bt = 0; bt < 16; ++bt)
-      if (kbyte_channel<KB>(bt) == n16) bt_of_c = bt;
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       const int g = w + kWaves * j;
@@ -924,25 +896,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int h = 4 * r4 + i;
-        if (h < ROWS) {
-          constexpr int QI = int(QTOT);
-          int Q = static_cast<int>(rintf(qv_[j][i] * (1.0f / sgm[i])));
-          Q = min(max(Q, -QI), QI);
-          const int t1 = (Q + 128) >> 8;  // in [-QI / 256, QI / 256]
-          const int lo = Q - 256 * t1;     // in [-128, 127]
-          const int hi = (t1 + 128) >> 8;  // in [-16, 16] (int8 keys: [-8, 8])
-          const int mid = t1 - 256 * hi;   // in [-128, 127]
+        constexpr int QI = int(QTOT);
+        int Q = static_cast<int>(rintf(qv_[j][i] * (1.0f / sgm[i])));
+        Q = min(max(Q, -QI), QI);
+        const int t1 = (Q + 128) >> 8;  // in [-QI / 256, QI / 256]
+        const int lo = Q - 256 * t1;     // in [-128, 127]
+        const int hi = (t1 + 128) >> 8;  // in [-16, 16] (int8 keys: [-8, 8])
+        const int mid = t1 - 256 * hi;   // in [-128, 127]
+        const int sh = 8 * (n16 & 3);
+        uint32_t dw[3] = {uint32_t(hi & 0xff) << sh, uint32_t(mid & 0xff) << sh, uint32_t(lo & 0xff) << sh};
+#pragma unroll
+        for (int dg = 0; dg < 3; ++dg) {
+          dw[dg] |= uint32_t(__builtin_amdgcn_mov_dpp(int(dw[dg]), 0xB1, 0xf, 0xf, false));  // quad [1,0,3,2]
+          dw[dg] |= uint32_t(__builtin_amdgcn_mov_dpp(int(dw[dg]), 0x4E, 0xf, 0xf, false));  // quad [2,3,0,1]
+        }
+        if ((n16 & 3) == 0 && h < ROWS) {
           if constexpr (G1) {
-            const int off = s * 1024 + (4 * slot + 16 * slot) * 16 + bt_of_c;
-            dig[off] = uint8_t(hi & 0xff);
-            dig[off + 16] = uint8_t(mid & 0xff);
-            dig[off + 32] = uint8_t(lo & 0xff);
+            if (h == 0) {
+#pragma unroll
+              for (int dg = 0; dg < 3; ++dg) dig[s * 64 + (4 * slot + dg) * 4 + (n16 >> 2)] = dw[dg];
+            }
           } else {
-            const int rb = h >> 2, row = (h & 3) * 4 + slot;
-            const int off = ((rb * NS + s) * 3) * 1024 + (row + 16 * slot) * 16 + bt_of_c;
-            dig[off] = uint8_t(hi & 0xff);
-            dig[off + 1024] = uint8_t(mid & 0xff);
-            dig[off + 2048] = uint8_t(lo & 0xff);
+#pragma unroll
+            for (int dg = 0; dg < 3; ++dg) dig[((r4 * NS + s) * 3 + dg) * 64 + (4 * slot + i) * 4 + (n16 >> 2)] = dw[dg];
           }
         }
       }
@@ -950,15 +926,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   }
   __syncthreads();
   v4i aop[G1 ? 1 : NRB][NS][G1 ? 1 : 3];
+  {
+    const int r = lane & 15, slot = lane >> 4;
 #pragma unroll
-  for (int rb = 0; rb < (G1 ? 1 : NRB); ++rb)
+    for (int rb = 0; rb < (G1 ? 1 : NRB); ++rb)
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+      for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int dg = 0; dg < (G1 ? 1 : 3); ++dg) {
-        const uint4 v = *reinterpret_cast<const uint4*>(dig + ((rb * NS + s) * (G1 ? 1 : 3) + dg) * 1024 + lane * 16);
-        aop[rb][s][dg] = v4i{int(v.x), int(v.y), int(v.z), int(v.w)};
-      }
+        for (int dg = 0; dg < (G1 ? 1 : 3); ++dg) {
+          bool on;
+          int off;
+          if constexpr (G1) {
+            on = (r >> 2) == slot && (r & 3) < 3;
+            off = s * 64 + r * 4;
+          } else {
+            on = (r & 3) == slot && 4 * rb + (r >> 2) < ROWS;
+            off = ((rb * NS + s) * 3 + dg) * 64 + (4 * slot + (r >> 2)) * 4;
+          }
+          const uint4 v = on ? *reinterpret_cast<const uint4*>(dig + off) : make_uint4(0u, 0u, 0u, 0u);
+          aop[rb][s][dg] = v4i{int(v.x), int(v.y), int(v.z), int(v.w)};
+        }
+  }
   __syncthreads();  // the main loop's tiles overwrite the prologue's LDS
 
   uint8_t* wbase = smem + w * Gm::LDS_WAVE;
