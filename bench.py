@@ -217,7 +217,7 @@ def decode_sources_sha():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "kv_cache_quantization_srft_amd", "csrc")
     for name in ("kvq_decode_q.h", "kvq_decode_q128.hip", "kvq_decode_q256.hip", "kvq_decode_common.h",
-                 "kvq_internal.h", "kvq_device.h", "kvq_plan.cpp"):
+                 "kvq_wave_rot.h", "kvq_internal.h", "kvq_device.h", "kvq_plan.cpp"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]

@@ -1,7 +1,7 @@
-// Shared pieces of the decode-attention kernels (gfx950): the SRFT entry table and the MFMA
-// operands generated from it, 16-lane DPP row reductions, the end of a chunk (work-group partial
-// of the online softmax) and the merge of the chunk partials of one (sequence, kv head, head
-// tile) with the single inverse rotation, done by the last work-group of the unit to finish.
+// Shared pieces of the decode-attention kernels (gfx950): 16-lane DPP row reductions, the end of
+// a chunk (work-group partial of the online softmax) and the merge of the chunk partials of one
+// (sequence, kv head, head tile) with the single inverse rotation, done by the last work-group of
+// the unit to finish.
 //
 // Partial results follow the tiled attention with online softmax of the hotdry blog
 // ("Flash Attention 与 Metal 内核融合"): every chunk keeps (m, l, acc) with scores in log2
@@ -10,7 +10,7 @@
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
-#include "kvq_lds_rot.h"
+#include "kvq_wave_rot.h"
 
 namespace kvq_impl {
 namespace dec {
@@ -29,102 +29,6 @@ typedef int v2i_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v2i_t lds_v2i_t;
 typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 fp16x4_t;
 typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4_t;
-
-// ------------------------------------------------------------------------------------------
-// twiddles: cos/sin(2 pi m / N), m < N, exact to float rounding (compile-time)
-// ------------------------------------------------------------------------------------------
-template <int N>
-struct TwTable {
-  float c[N];
-  float s[N];
-  constexpr TwTable() : c(), s() {
-    for (int m = 0; m < N; ++m) {
-      const CosSin v = cos_sin_turn(m, N);
-      c[m] = float(v.c);
-      s[m] = float(v.s);
-    }
-  }
-};
-
-template <int D>
-struct TwConst;
-template <>
-struct TwConst<128> {
-  static constexpr TwTable<128> t = TwTable<128>();
-};
-template <>
-struct TwConst<256> {
-  static constexpr TwTable<256> t = TwTable<256>();
-};
-
-// The real orthogonal SRFT matrix (without the sign flip), Q[c][n]:
-//   Q[0][n] = 1/sqrt(D), Q[1][n] = (-1)^n/sqrt(D),
-//   Q[2k][n] = sqrt(2/D) cos(2 pi k n/D), Q[2k+1][n] = -sqrt(2/D) sin(2 pi k n/D),
-// evaluated in double at compile time.  The tables hold 16*Q split into fp16 hi + lo (the x16
-// keeps lo out of the fp16 subnormal range) laid out as B operands of v_mfma_f32_16x16x32_f16:
-//   fwd[cb][s][lane][j] = 16 Q[16 cb + lane%16][32 s + 8 (lane/16) + j]   (q_hat = Q (s*q))
-//   inv[nb][s][lane][j] = 16 Q[32 s + 8 (lane/16) + j][16 nb + lane%16]   (x = Q^T y)
-// so one 16-byte load per lane fetches the operand of one MFMA.
-// inv = 1/sqrt(D), r2 = sqrt(2/D), tw[m] = (cos, sin)(2 pi m / D)
-constexpr double q_entry(int c, int n, int D, const CosSin* tw, double inv, double r2) {
-  if (c == 0) return inv;
-  if (c == 1) return (n & 1) ? -inv : inv;
-  const CosSin w = tw[((c >> 1) * n) % D];
-  return (c & 1) ? -r2 * w.s : r2 * w.c;
-}
-
-// The SRHT (Sylvester-ordered Walsh-Hadamard) counterpart, d^-1/2 H[c][n] with
-// H[c][n] = (-1)^popcount(c & n); inv = 1/sqrt(D).
-constexpr double h_entry(int c, int n, double inv) { return (__builtin_popcount(c & n) & 1) ? -inv : inv; }
-
-template <int D>
-struct MfmaQTable {
-  static constexpr int NB = D / 16, NSTEP = D / 32;
-  uint32_t fwd_hi[NB][NSTEP][64][4];
-  uint32_t fwd_lo[NB][NSTEP][64][4];
-  uint32_t inv_hi[NB][NSTEP][64][4];
-  uint32_t inv_lo[NB][NSTEP][64][4];
-  // had = false: the SRFT matrix Q; had = true: the SRHT matrix d^-1/2 H (symmetric, so the
-  // forward and inverse operands coincide)
-  constexpr MfmaQTable(bool had = false) : fwd_hi(), fwd_lo(), inv_hi(), inv_lo() {
-    CosSin tw[D] = {};
-    if (!had)
-      for (int m = 0; m < D; ++m) tw[m] = cos_sin_turn(m, D);
-    const double inv = 1.0 / csqrt(double(D)), r2 = csqrt(2.0 / double(D));
-    for (int b = 0; b < NB; ++b)
-      for (int s = 0; s < NSTEP; ++s)
-        for (int l = 0; l < 64; ++l)
-          for (int j = 0; j < 8; ++j) {
-            const int col = 16 * b + (l & 15), k = 32 * s + 8 * (l >> 4) + j;
-            for (int which = 0; which < 2; ++which) {
-              const int r = which == 0 ? col : k, cl = which == 0 ? k : col;  // Q[r][cl]
-              const double v = 16.0 * (had ? h_entry(r, cl, inv) : q_entry(r, cl, D, tw, inv, r2));
-              const float vf = float(v);
-              const _Float16 hi = static_cast<_Float16>(vf);
-              const _Float16 lo = static_cast<_Float16>(float(v - double(static_cast<float>(hi))));
-              const uint32_t hb = __builtin_bit_cast(uint16_t, hi), lb = __builtin_bit_cast(uint16_t, lo);
-              uint32_t(&H)[4] = which == 0 ? fwd_hi[b][s][l] : inv_hi[b][s][l];
-              uint32_t(&Lo)[4] = which == 0 ? fwd_lo[b][s][l] : inv_lo[b][s][l];
-              H[j >> 1] |= hb << (16 * (j & 1));
-              Lo[j >> 1] |= lb << (16 * (j & 1));
-            }
-          }
-  }
-};
-
-__device__ const MfmaQTable<128> kMQ128 = MfmaQTable<128>(false);
-__device__ const MfmaQTable<256> kMQ256 = MfmaQTable<256>(false);
-__device__ const MfmaQTable<128> kMH128 = MfmaQTable<128>(true);
-__device__ const MfmaQTable<256> kMH256 = MfmaQTable<256>(true);
-
-// transform: 0 = SRFT, 1 = SRHT (uniform across the launch)
-template <int D>
-__device__ __forceinline__ const MfmaQTable<D>& mqtable(int transform) {
-  if constexpr (D == 128)
-    return transform ? kMH128 : kMQ128;
-  else
-    return transform ? kMH256 : kMQ256;
-}
 
 __device__ __forceinline__ v8h as_v8h(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   v4i t = {int(a), int(b), int(c), int(d)};

@@ -44,6 +44,66 @@ struct FastDiv {
 
 namespace mq {
 
+// The real orthogonal SRFT matrix (without the sign flip), Q[c][n]:
+//   Q[0][n] = 1/sqrt(D), Q[1][n] = (-1)^n/sqrt(D),
+//   Q[2k][n] = sqrt(2/D) cos(2 pi k n/D), Q[2k+1][n] = -sqrt(2/D) sin(2 pi k n/D),
+// evaluated in double at compile time.  The table holds 16*Q split into fp16 hi + lo (the x16
+// keeps lo out of the fp16 subnormal range) laid out as operands of v_mfma_f32_16x16x32_f16:
+//   fwd[cb][s][lane][j] = 16 Q[16 cb + lane%16][32 s + 8 (lane/16) + j]   (u = Q (s*x))
+// so one 16-byte load per lane fetches the operand of one MFMA.
+// inv = 1/sqrt(D), r2 = sqrt(2/D), tw[m] = (cos, sin)(2 pi m / D)
+constexpr double q_entry(int c, int n, int D, const CosSin* tw, double inv, double r2) {
+  if (c == 0) return inv;
+  if (c == 1) return (n & 1) ? -inv : inv;
+  const CosSin w = tw[((c >> 1) * n) % D];
+  return (c & 1) ? -r2 * w.s : r2 * w.c;
+}
+
+// The SRHT (Sylvester-ordered Walsh-Hadamard) counterpart, d^-1/2 H[c][n] with
+// H[c][n] = (-1)^popcount(c & n); inv = 1/sqrt(D).
+constexpr double h_entry(int c, int n, double inv) { return (__builtin_popcount(c & n) & 1) ? -inv : inv; }
+
+template <int D>
+struct MfmaQTable {
+  static constexpr int NB = D / 16, NSTEP = D / 32;
+  uint32_t fwd_hi[NB][NSTEP][64][4];
+  uint32_t fwd_lo[NB][NSTEP][64][4];
+  // had = false: the SRFT matrix Q; had = true: the SRHT matrix d^-1/2 H
+  constexpr MfmaQTable(bool had = false) : fwd_hi(), fwd_lo() {
+    CosSin tw[D] = {};
+    if (!had)
+      for (int m = 0; m < D; ++m) tw[m] = cos_sin_turn(m, D);
+    const double inv = 1.0 / csqrt(double(D)), r2 = csqrt(2.0 / double(D));
+    for (int b = 0; b < NB; ++b)
+      for (int s = 0; s < NSTEP; ++s)
+        for (int l = 0; l < 64; ++l)
+          for (int j = 0; j < 8; ++j) {
+            const int r = 16 * b + (l & 15), cl = 32 * s + 8 * (l >> 4) + j;  // Q[r][cl]
+            const double v = 16.0 * (had ? h_entry(r, cl, inv) : q_entry(r, cl, D, tw, inv, r2));
+            const float vf = float(v);
+            const _Float16 hi = static_cast<_Float16>(vf);
+            const _Float16 lo = static_cast<_Float16>(float(v - double(static_cast<float>(hi))));
+            const uint32_t hb = __builtin_bit_cast(uint16_t, hi), lb = __builtin_bit_cast(uint16_t, lo);
+            fwd_hi[b][s][l][j >> 1] |= hb << (16 * (j & 1));
+            fwd_lo[b][s][l][j >> 1] |= lb << (16 * (j & 1));
+          }
+  }
+};
+
+__device__ const MfmaQTable<128> kMQ128 = MfmaQTable<128>(false);
+__device__ const MfmaQTable<256> kMQ256 = MfmaQTable<256>(false);
+__device__ const MfmaQTable<128> kMH128 = MfmaQTable<128>(true);
+__device__ const MfmaQTable<256> kMH256 = MfmaQTable<256>(true);
+
+// transform: 0 = SRFT, 1 = SRHT (uniform across the launch)
+template <int D>
+__device__ __forceinline__ const MfmaQTable<D>& mqtable(int transform) {
+  if constexpr (D == 128)
+    return transform ? kMH128 : kMQ128;
+  else
+    return transform ? kMH256 : kMQ256;
+}
+
 using dec::v8h;
 using dec::v4f;
 
@@ -95,7 +155,7 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
   const int n16 = lane & 15, r4 = lane >> 4;
 
   // A operands of this wave's two channel blocks (constant for the kernel)
-  const dec::MfmaQTable<D>& T = dec::mqtable<D>(transform);
+  const MfmaQTable<D>& T = mqtable<D>(transform);
   v8h ahi[2][NSTEP], alo[2][NSTEP];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
