@@ -707,16 +707,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   const float* srow_k = P.sign_k + b * P.sign_bs;
   const float* srow_v = P.merge.sign + b * P.sign_bs;
   FwdIn<D> fin;
-  fwd_load<D>(fin, P.merge.transform, [&](int n, const uint16_t*& x, const float*& sg) -> bool {
+  fwd_load<D>(fin, P.merge.transform, srow_k, app ? srow_v : nullptr, [&](int n, const uint16_t*& x) -> bool {
     if (app && n >= 14) {
       x = (n == 14 ? P.k_new : P.v_new) + (int64_t(b) * P.kv_heads + kvh) * D;
-      sg = n == 14 ? srow_k : srow_v;
       return true;
     }
     const int qr = min(n, ROWS - 1);
     const int qi = min(i0 + qr / GT, P.n_query - 1);
     x = P.q + ((int64_t(b) * P.n_query + qi) * P.q_heads + h0 + qr % GT) * D;
-    sg = srow_k;
     return n < ROWS && i0 + n / GT < P.n_query;
   });
   RotTw<D> rtw;
@@ -762,13 +760,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   fwd_wave<D>(fin, rtw, P.merge.transform, qo);
   __syncthreads();
   constexpr int QP = RotGeom<D>::PITCH;
-  // q_hat[h][c] * lambda_c * score_scale for head h = 4 r4 + i and channel c = 16 (w + 4j) + qch
-  float qv_[NBW][4];
+  // q_hat[h][c] * lambda_c * score_scale for the heads h = r4 + 4 i (i < NRB: the row blocks of
+  // the score operands) and channel c = 16 (w + 4j) + qch
+  float qv_[NBW][NRB];
 #pragma unroll
   for (int j = 0; j < NBW; ++j) {
     const int g = w + kWaves * j;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) qv_[j][i] = qo[(4 * r4 + i) * QP + 16 * g + qch] * lam[j];
+    for (int i = 0; i < NRB; ++i) qv_[j][i] = qo[(r4 + 4 * i) * QP + 16 * g + qch] * lam[j];
     if (app) {
       // the write path on rows 14 (K) and 15 (V), lanes 48..63, channel c = 16 g + n16:
       // u = SRFT(x)_c / lambda_c, group absmax over the row's 16 lanes, fp16 scale, rounded
@@ -802,12 +801,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   }
   // per-head maximum of |q_hat| over this wave's channels (16-lane DPP rows), then over waves
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NRB; ++i) {
     float m = 0.0f;
 #pragma unroll
     for (int j = 0; j < NBW; ++j) m = fmaxf(m, fabsf(qv_[j][i]));
     m = row_max16(m);
-    if (n16 == 0) pmax[w * 16 + 4 * r4 + i] = m;
+    if (n16 == 0) pmax[w * 16 + r4 + 4 * i] = m;
   }
   __syncthreads();
   if (app && ht == 0) {
@@ -843,17 +842,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   // channel, left score errors up to ~1e-2 when lambda_K spans a decade and keys exceed the
   // calibration range)
   constexpr float QTOT = KB == 4 ? 1048576.0f : 524288.0f;
-  float sgm[4];
-  {
-    float4 mx = *reinterpret_cast<const float4*>(pmax + 4 * r4);
+  // step of head r4 + 4 i (the heads of this lane's query values)
+  float sgm[NRB];
 #pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) {
-      const float4 o = *reinterpret_cast<const float4*>(pmax + ww * 16 + 4 * r4);
-      mx = make_float4(fmaxf(mx.x, o.x), fmaxf(mx.y, o.y), fmaxf(mx.z, o.z), fmaxf(mx.w, o.w));
-    }
-    const float m4[4] = {mx.x, mx.y, mx.z, mx.w};
+  for (int i = 0; i < NRB; ++i) {
+    float mxh = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sgm[i] = m4[i] > 0.0f ? m4[i] / QTOT : 1.0f;
+    for (int ww = 0; ww < kWaves; ++ww) mxh = fmaxf(mxh, pmax[ww * 16 + r4 + 4 * i]);
+    sgm[i] = mxh > 0.0f ? mxh / QTOT : 1.0f;
   }
   // score multiplier of the rows this lane's scores belong to: heads 4 rb + r4 (G1: head 0 in
   // every lane)
@@ -887,15 +883,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
   // G1: one operand per step s, row r = 4 slot + digit (row 4 slot + 3 zero), non-zero where
   // l/16 == slot.  Only the non-zero lanes' 16 bytes are staged: 256 bytes per operand, at
   // (4 slot + head in block) * 16 (G1: (4 slot + digit) * 16).  The lanes of a quad hold the
-  // four bytes of one dword (channel kbyte_channel(n16)); two DPP swaps assemble it.
+  // four bytes of one dword (channel kbyte_channel(n16)); two DPP swaps assemble it.  Lane (n16,
+  // r4) holds head r4 + 4 i of row block i.
   {
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
       const int g = w + kWaves * j;
       const int slot = g / NS, s = g % NS;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int h = 4 * r4 + i;
+      for (int i = 0; i < NRB; ++i) {
+        const int h = r4 + 4 * i;
         constexpr int QI = int(QTOT);
         int Q = static_cast<int>(rintf(qv_[j][i] * (1.0f / sgm[i])));
         Q = min(max(Q, -QI), QI);
@@ -918,7 +915,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 1
             }
           } else {
 #pragma unroll
-            for (int dg = 0; dg < 3; ++dg) dig[((r4 * NS + s) * 3 + dg) * 64 + (4 * slot + i) * 4 + (n16 >> 2)] = dw[dg];
+            for (int dg = 0; dg < 3; ++dg) dig[((i * NS + s) * 3 + dg) * 64 + (4 * slot + r4) * 4 + (n16 >> 2)] = dw[dg];
           }
         }
       }

@@ -16,36 +16,12 @@
 // SRHT (the Walsh-Hadamard alternative): lane l holds values n = l + 64 e; the Hadamard stages
 // are the same butterflies without twiddles, in natural order.
 //
-// All arithmetic is float32; the only table is the d twiddles (1 or 2 KB, read once per lane).
+// All arithmetic is float32; the only table is each lane's twiddles (64 or 96 bytes per lane).
 #pragma once
 #include "kvq_device.h"
 
 namespace kvq_impl {
 namespace dec {
-
-// c[t] = cos(2 pi t / D), s[t] = sin(2 pi t / D), t < D, rounded from double at compile time.
-template <int D>
-struct TwiddleTable {
-  float c[D];
-  float s[D];
-  constexpr TwiddleTable() : c(), s() {
-    for (int t = 0; t < D; ++t) {
-      const kvqd::CosSin v = kvqd::cos_sin_turn(t, D);
-      c[t] = float(v.c);
-      s[t] = float(v.s);
-    }
-  }
-};
-__device__ const TwiddleTable<128> kTwid128{};
-__device__ const TwiddleTable<256> kTwid256{};
-
-template <int D>
-__device__ __forceinline__ const TwiddleTable<D>& twiddle_table() {
-  if constexpr (D == 128)
-    return kTwid128;
-  else
-    return kTwid256;
-}
 
 template <int D>
 struct RotGeom {
@@ -85,12 +61,18 @@ __device__ __forceinline__ float lane_xor(float v) {
   }
 }
 
-// Per-lane twiddles of the transforms, read from the table.
-//   sc[j], ss[j]: stage j (span H = M >> (j+1)) twiddle W_M^{(m mod H) M/(2H)} of this lane's upper
-//          points ((1, 0) on the lower points of a cross-lane stage; the span-64 stage of d = 256
-//          uses the lane's own point m = l)
-//   uc[p], us[p]: forward unpack, W_D^k for the bin k = bitrev(l + 64 p) the lane holds after the FFT;
-//          inverse pack: W_D^k for k = l + 64 p
+// m with its LOGM low bits reversed
+template <int D>
+__host__ __device__ constexpr int bitrev_m(int m) {
+  return int(__builtin_bitreverse32(uint32_t(m)) >> (32 - RotGeom<D>::LOGM));
+}
+
+// Per-lane twiddles of the transforms, one contiguous record per lane (read with 16-byte loads):
+//   sc[j], ss[j]: stage j (span H = M >> (j+1)) twiddle W_M^{(m mod H) M/(2H)} of this lane's
+//          upper points ((1, 0) on the lower points of a cross-lane stage; the span-64 stage of
+//          d = 256 uses the lane's own point m = l)
+//   uc[p], us[p]: forward unpack, W_D^k for the bin k = bitrev(l + 64 p) the lane holds after
+//          the FFT; inverse pack (INVERSE): W_D^k for k = l + 64 p
 template <int D>
 struct RotTw {
   float sc[RotGeom<D>::NST], ss[RotGeom<D>::NST];
@@ -98,35 +80,61 @@ struct RotTw {
 };
 
 template <int D>
-__device__ __forceinline__ int bitrev_m(int m) {
-  return int(__builtin_bitreverse32(uint32_t(m)) >> (32 - RotGeom<D>::LOGM));
-}
+struct LaneTwiddles {
+  static constexpr int NST = RotGeom<D>::NST, P = RotGeom<D>::P;
+  static constexpr int F = 2 * (NST + 2 * P);  // stages, forward unpack, inverse pack
+  static constexpr int Q4 = (F + 3) / 4;       // float4 per lane
+  float v[64][4 * Q4];
+  constexpr LaneTwiddles() : v() {
+    constexpr int M = RotGeom<D>::M;
+    for (int l = 0; l < 64; ++l) {
+      for (int j = 0; j < NST; ++j) {
+        const int H = M >> (j + 1);
+        const bool one = H < 64 && (l & H) == 0;
+        const int t = H == 64 ? 2 * l : 2 * (l & (H - 1)) * (M / (2 * H));
+        const kvqd::CosSin cs = kvqd::cos_sin_turn(t, D);
+        v[l][2 * j] = one ? 1.0f : float(cs.c);
+        v[l][2 * j + 1] = one ? 0.0f : float(cs.s);
+      }
+      for (int p = 0; p < P; ++p) {
+        const kvqd::CosSin f = kvqd::cos_sin_turn(bitrev_m<D>(l + 64 * p), D);
+        const kvqd::CosSin i = kvqd::cos_sin_turn(l + 64 * p, D);
+        v[l][2 * NST + 2 * p] = float(f.c);
+        v[l][2 * NST + 2 * p + 1] = float(f.s);
+        v[l][2 * NST + 2 * P + 2 * p] = float(i.c);
+        v[l][2 * NST + 2 * P + 2 * p + 1] = float(i.s);
+      }
+    }
+  }
+};
+__device__ const LaneTwiddles<128> kLaneTw128{};
+__device__ const LaneTwiddles<256> kLaneTw256{};
 
 template <int D, bool INVERSE>
 __device__ __forceinline__ void load_rot_tw(RotTw<D>& tw) {
-  using G = RotGeom<D>;
-  const TwiddleTable<D>& T = twiddle_table<D>();
+  using LT = LaneTwiddles<D>;
   const int lane = threadIdx.x & 63;
+  const float* src;
+  if constexpr (D == 128)
+    src = kLaneTw128.v[lane];
+  else
+    src = kLaneTw256.v[lane];
+  float f[4 * LT::Q4];
 #pragma unroll
-  for (int j = 0; j < G::NST; ++j) {
-    const int H = G::M >> (j + 1);
-    int t;  // exponent in units of W_D
-    bool one;
-    if (H == 64) {
-      t = 2 * lane;  // W_M^l
-      one = false;
-    } else {
-      t = 2 * (lane & (H - 1)) * (G::M / (2 * H));
-      one = (lane & H) == 0;
-    }
-    tw.sc[j] = one ? 1.0f : T.c[t];
-    tw.ss[j] = one ? 0.0f : T.s[t];
+  for (int q = 0; q < LT::Q4; ++q) {
+    const float4 x = reinterpret_cast<const float4*>(src)[q];
+    f[4 * q] = x.x, f[4 * q + 1] = x.y, f[4 * q + 2] = x.z, f[4 * q + 3] = x.w;
   }
 #pragma unroll
-  for (int p = 0; p < G::P; ++p) {
-    const int k = INVERSE ? lane + 64 * p : bitrev_m<D>(lane + 64 * p);
-    tw.uc[p] = T.c[k];
-    tw.us[p] = T.s[k];
+  for (int j = 0; j < LT::NST; ++j) {
+    tw.sc[j] = f[2 * j];
+    tw.ss[j] = f[2 * j + 1];
+  }
+  constexpr int U = 2 * LT::NST + (INVERSE ? 2 * LT::P : 0);
+#pragma unroll
+  for (int p = 0; p < LT::P; ++p) {
+    tw.uc[p] = f[U + 2 * p];
+    tw.us[p] = f[U + 2 * p + 1];
   }
 }
 
@@ -200,50 +208,60 @@ __device__ __forceinline__ void wht_wave(float (&v)[RotGeom<D>::E], int lane) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Forward rotation of rows w + 4 i (wave w, i < 4).  fwd_load issues the loads (row_src(r, x, s)
-// returns whether row r has an input and sets its fp16 row and sign row); fwd_wave transforms
-// and writes the rows to qo (LDS, pitch PITCH; rows without input are written as zeros).  The
-// caller's barrier then publishes qo.
+// Forward rotation of rows w + 4 i (wave w, i < 4).  fwd_load issues the loads (row_src(r, x)
+// returns whether row r has an input and sets its fp16 row; every row takes the signs srow,
+// except row 15 when s15 is not null); fwd_wave transforms and writes the rows to qo (LDS,
+// pitch PITCH; rows without input are written as zeros).  The caller's barrier publishes qo.
 // ---------------------------------------------------------------------------------------------
 template <int D>
 struct FwdIn {
   uint32_t x[4][RotGeom<D>::E];  // SRFT: dwords l + 64 p (P of them); SRHT: halves l + 64 e
-  float s[4][RotGeom<D>::E];     // SRFT: sign pairs of those dwords; SRHT: signs
+  float s[RotGeom<D>::E];        // signs of those values (SRFT: pairs) in the sign row of all rows
+  float s15[RotGeom<D>::E];      // ... in the sign row of row 15 when it has its own
   bool live[4];
+  bool own15;                    // row 15 of this wave takes s15
 };
 
+template <int D>
+__device__ __forceinline__ void load_signs(float (&sv)[RotGeom<D>::E], const float* srow, int transform) {
+  using G = RotGeom<D>;
+  const int lane = threadIdx.x & 63;
+  if (transform) {
+#pragma unroll
+    for (int e = 0; e < G::E; ++e) sv[e] = srow[lane + 64 * e];
+  } else {
+#pragma unroll
+    for (int p = 0; p < G::P; ++p) {
+      const float2 v = reinterpret_cast<const float2*>(srow)[lane + 64 * p];
+      sv[2 * p] = v.x;
+      sv[2 * p + 1] = v.y;
+    }
+  }
+}
+
 template <int D, typename RowSrc>
-__device__ __forceinline__ void fwd_load(FwdIn<D>& in, int transform, RowSrc&& row_src) {
+__device__ __forceinline__ void fwd_load(FwdIn<D>& in, int transform, const float* srow, const float* s15,
+                                         RowSrc&& row_src) {
   using G = RotGeom<D>;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     const uint16_t* x = nullptr;
-    const float* s = nullptr;
-    in.live[rr] = row_src(w + 4 * rr, x, s);
+    in.live[rr] = row_src(w + 4 * rr, x);
 #pragma unroll
-    for (int e = 0; e < G::E; ++e) {
-      in.x[rr][e] = 0u;
-      in.s[rr][e] = 1.0f;
-    }
+    for (int e = 0; e < G::E; ++e) in.x[rr][e] = 0u;
     if (!in.live[rr]) continue;
     if (transform) {
 #pragma unroll
-      for (int e = 0; e < G::E; ++e) {
-        in.x[rr][e] = x[lane + 64 * e];
-        in.s[rr][e] = s[lane + 64 * e];
-      }
+      for (int e = 0; e < G::E; ++e) in.x[rr][e] = x[lane + 64 * e];
     } else {
 #pragma unroll
-      for (int p = 0; p < G::P; ++p) {
-        const int m = lane + 64 * p;
-        in.x[rr][p] = reinterpret_cast<const uint32_t*>(x)[m];
-        const float2 v = reinterpret_cast<const float2*>(s)[m];
-        in.s[rr][2 * p] = v.x;
-        in.s[rr][2 * p + 1] = v.y;
-      }
+      for (int p = 0; p < G::P; ++p) in.x[rr][p] = reinterpret_cast<const uint32_t*>(x)[lane + 64 * p];
     }
   }
+  load_signs<D>(in.s, srow, transform);
+  in.own15 = s15 != nullptr && w == 3 && in.live[3];
+  if (in.own15) load_signs<D>(in.s15, s15, transform);
 }
 
 __device__ __forceinline__ float signed_half(uint32_t bits16, float s) {
@@ -265,20 +283,22 @@ __device__ __forceinline__ void fwd_wave(const FwdIn<D>& in, const RotTw<D>& tw,
       continue;
     }
     if (transform) {
+      const bool o15 = rr == 3 && in.own15;
       float v[G::E];
 #pragma unroll
-      for (int e = 0; e < G::E; ++e) v[e] = signed_half(in.x[rr][e] & 0xffffu, in.s[rr][e]);
+      for (int e = 0; e < G::E; ++e) v[e] = signed_half(in.x[rr][e] & 0xffffu, o15 ? in.s15[e] : in.s[e]);
       wht_wave<D>(v, lane);
       constexpr float nrm = kvqd::inv_sqrt_d<D>();
 #pragma unroll
       for (int e = 0; e < G::E; ++e) o[lane + 64 * e] = v[e] * nrm;
       continue;
     }
+    const bool o15 = rr == 3 && in.own15;
     float zr[G::P], zi[G::P];
 #pragma unroll
     for (int p = 0; p < G::P; ++p) {
-      zr[p] = signed_half(in.x[rr][p] & 0xffffu, in.s[rr][2 * p]);
-      zi[p] = signed_half(in.x[rr][p] >> 16, in.s[rr][2 * p + 1]);
+      zr[p] = signed_half(in.x[rr][p] & 0xffffu, o15 ? in.s15[2 * p] : in.s[2 * p]);
+      zi[p] = signed_half(in.x[rr][p] >> 16, o15 ? in.s15[2 * p + 1] : in.s[2 * p + 1]);
     }
     fft_wave<D, false>(zr, zi, tw, lane);
     // lane l, point p now holds Z_k, k = bitrev(l + 64 p); fetch Z_{M-k} from the lane holding it
