@@ -106,6 +106,15 @@ __device__ __forceinline__ void nibbles_to_half16(uint32_t x, uint32_t m_lo, uin
   }
 }
 
+// int4 V tile: the 16-byte unit k of token t sits at slot k ^ vswz4(t) of the token's row, so
+// that the transposed reads of one group by the 64 tokens of a superblock (8 bytes each, rows of
+// 64 or 128 bytes) spread over the LDS banks instead of hitting the same 4 (d 128) or 2 (d 256)
+// bank groups: the XOR varies with the token bits above those that already change the bank.
+template <int D>
+__device__ __forceinline__ int vswz4(int t) {
+  return D == 128 ? (t >> 2) & 3 : (t >> 1) & 7;
+}
+
 // Global data of one 64-token superblock held in registers (prefetched one superblock ahead).
 template <int D, int KB, int VB>
 struct SBRegs {
@@ -353,7 +362,9 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int bas
   for (int i = 0; i < Gm::VLU; ++i) {
     const int u = i * 64 + lane;  // 16-byte unit of the superblock, token-major
     if constexpr (VB == 4) {
-      *reinterpret_cast<uint4*>(vtile + u * 16) = r.vw[i];
+      constexpr int UPT = Gm::VRB / 16;
+      const int tk = u / UPT, k = u % UPT;
+      *reinterpret_cast<uint4*>(vtile + tk * Gm::VRB + 16 * (k ^ vswz4<D>(tk))) = r.vw[i];
     } else {
       // int8: unit k (group k) of token t goes to slot k ^ (t & 7) of the token's row, so that
       // the transposed reads of 8 tokens of one group hit 8 different bank quads
@@ -558,7 +569,8 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int bas
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     // lane r of each 16-lane group points at token 16*r4 + r, group g
-    lds_v2i_t* src = (lds_v2i_t*)(vtile + (16 * r4 + n16) * Gm::VRB + 8 * g);
+    const int tk = 16 * r4 + n16;
+    lds_v2i_t* src = (lds_v2i_t*)(vtile + tk * Gm::VRB + 16 * ((g >> 1) ^ vswz4<D>(tk)) + 8 * (g & 1));
     const v2i_t tr = __builtin_amdgcn_ds_read_tr4_b64_v2i32(src);
     const uint4 s0 = *reinterpret_cast<const uint4*>(stile + g * kSB + 16 * r4);
     const uint4 s1 = *reinterpret_cast<const uint4*>(stile + g * kSB + 16 * r4 + 8);

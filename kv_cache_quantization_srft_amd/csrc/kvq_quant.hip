@@ -192,12 +192,18 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
                                           *reinterpret_cast<const float4*>(sign + spc * 8 + 4))
                               : make_uint4(0u, 0u, 0u, 0u);
   uint4 pd[2][H], pm[2][SHARED ? 1 : H];
-  // A vector past the end reads the last vector again (no divergent branch around the load); its
-  // column of the product is never stored, and columns do not mix.
+  // A block is read through a buffer resource over its vectors (a scalar base at its first
+  // vector) at the thread's fixed byte offset; a vector past the end reads zeros, and its
+  // column of the product is never stored (columns do not mix).
+  const int loff = (sv * D + spc * 8) * 2;
   auto load_piece = [&](uint32_t blk_, uint4& d_, uint4& m_) {
-    const uint32_t gv = min(blk_ * kVecs + sv, n_vec - 1u);
-    d_ = *reinterpret_cast<const uint4*>(x + int64_t(gv) * D + spc * 8);
+    const uint32_t g0 = blk_ * kVecs;
+    const uint32_t nv = min(n_vec - g0, uint32_t(kVecs));
+    const __amdgpu_buffer_rsrc_t r = dec::buf_rsrc(x + int64_t(g0) * D, int64_t(nv) * D * 2);
+    const dec::v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, loff, 0, 0);
+    d_ = make_uint4(uint32_t(v[0]), uint32_t(v[1]), uint32_t(v[2]), uint32_t(v[3]));
     if constexpr (!SHARED) {
+      const uint32_t gv = min(g0 + sv, n_vec - 1u);
       const int b = int(fd_heads.div(fd_tok.div(gv)));
       m_ = sign_mask(*reinterpret_cast<const float4*>(sign + b * sign_bs + spc * 8),
                      *reinterpret_cast<const float4*>(sign + b * sign_bs + spc * 8 + 4));
@@ -309,7 +315,19 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
       auto vslot = [&](uint32_t gvs, int v) { return one_row ? slot0 + v : slot_of(gvs); };
       constexpr int UNITS = kVecs * CB / 16;  // 16-byte code units
       constexpr int SUNITS = kVecs * NG / 8;  // 16-byte scale units
-      if (tid < UNITS) {
+      if (one_row && gv0 + kVecs <= n_vec) {
+        // the block's 16 slots are consecutive: unit u of the LDS tiles goes to unit u of the
+        // planes after the first slot (scalar base plus the thread's offset)
+        if (tid < UNITS) {
+          *reinterpret_cast<uint4*>(codes + slot0 * CB + 16 * tid) =
+              *reinterpret_cast<const uint4*>(&ct[buf][0][0] + 16 * tid);
+        } else if (PT && tid < UNITS + kVecs) {
+          scales[slot0 + (tid - UNITS)] = st[buf][tid - UNITS][0];
+        } else if (!PT && tid < UNITS + SUNITS) {
+          *reinterpret_cast<uint4*>(scales + slot0 * NG + 8 * (tid - UNITS)) =
+              *reinterpret_cast<const uint4*>(&st[buf][0][0] + 8 * (tid - UNITS));
+        }
+      } else if (tid < UNITS) {
         const int v = tid / (CB / 16), pc = tid - v * (CB / 16);
         const uint32_t gvs = blk * kVecs + v;
         if (gvs < n_vec)
