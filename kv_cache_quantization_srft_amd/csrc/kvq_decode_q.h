@@ -61,7 +61,11 @@ struct QGeom {
   static constexpr int VLU = kSB * VRB / 64 / 16;  // 16-byte V units per lane per superblock
   static constexpr int SLW = NG * 2 / 4;        // scale dwords per token
   // LDS (bytes) per wave: V codes, V scales (transposed, k order), K scales, P, alpha
-  static constexpr int LDS_V = kSB * VRB;
+  // int4 V rows are padded by 16 bytes: the transposed reads of one group by the 64 tokens of a
+  // superblock (8 bytes each) then spread over 16 bank quads instead of 4 (d 128) or 2 (d 256),
+  // and every address stays a per-lane base plus an immediate
+  static constexpr int VROW = VB == 4 ? VRB + 16 : VRB;
+  static constexpr int LDS_V = kSB * VROW;
   static constexpr int LDS_S = NG * kSB * 2;
   static constexpr int LDS_K = kSB * NG * 2;
   static constexpr int LDS_P = 32 * kSB * 2;  // p as fp16 hi and lo parts, 16 heads each
@@ -104,15 +108,6 @@ __device__ __forceinline__ void nibbles_to_half16(uint32_t x, uint32_t m_lo, uin
     const v2h c = __builtin_elementwise_fma(__builtin_bit_cast(v2h, t[i]), (i & 1) ? f_hi : f_lo, (i & 1) ? o_hi : o_lo);
     p[i] = __builtin_bit_cast(uint32_t, c);
   }
-}
-
-// int4 V tile: the 16-byte unit k of token t sits at slot k ^ vswz4(t) of the token's row, so
-// that the transposed reads of one group by the 64 tokens of a superblock (8 bytes each, rows of
-// 64 or 128 bytes) spread over the LDS banks instead of hitting the same 4 (d 128) or 2 (d 256)
-// bank groups: the XOR varies with the token bits above those that already change the bank.
-template <int D>
-__device__ __forceinline__ int vswz4(int t) {
-  return D == 128 ? (t >> 2) & 3 : (t >> 1) & 7;
 }
 
 // Global data of one 64-token superblock held in registers (prefetched one superblock ahead).
@@ -364,7 +359,7 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int bas
     if constexpr (VB == 4) {
       constexpr int UPT = Gm::VRB / 16;
       const int tk = u / UPT, k = u % UPT;
-      *reinterpret_cast<uint4*>(vtile + tk * Gm::VRB + 16 * (k ^ vswz4<D>(tk))) = r.vw[i];
+      *reinterpret_cast<uint4*>(vtile + tk * Gm::VROW + 16 * k) = r.vw[i];
     } else {
       // int8: unit k (group k) of token t goes to slot k ^ (t & 7) of the token's row, so that
       // the transposed reads of 8 tokens of one group hit 8 different bank quads
@@ -569,8 +564,7 @@ __device__ __forceinline__ void process_superblock(SBRegs<D, KB, VB>& r, int bas
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     // lane r of each 16-lane group points at token 16*r4 + r, group g
-    const int tk = 16 * r4 + n16;
-    lds_v2i_t* src = (lds_v2i_t*)(vtile + tk * Gm::VRB + 16 * ((g >> 1) ^ vswz4<D>(tk)) + 8 * (g & 1));
+    lds_v2i_t* src = (lds_v2i_t*)(vtile + (16 * r4 + n16) * Gm::VROW + 8 * g);
     const v2i_t tr = __builtin_amdgcn_ds_read_tr4_b64_v2i32(src);
     const uint4 s0 = *reinterpret_cast<const uint4*>(stile + g * kSB + 16 * r4);
     const uint4 s1 = *reinterpret_cast<const uint4*>(stile + g * kSB + 16 * r4 + 8);
