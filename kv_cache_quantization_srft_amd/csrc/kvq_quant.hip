@@ -109,13 +109,25 @@ using dec::v4f;
 
 constexpr int kVecs = kQuantVecs;  // vectors per block (MFMA columns)
 
-// max over the four 16-lane rows for every lane position (v_permlane32_swap, v_permlane16_swap)
-// of a non-negative float given as its bit pattern (non-negative floats order like their bits)
-__device__ __forceinline__ uint32_t rows_max4(uint32_t a) {
-  const auto r32 = __builtin_amdgcn_permlane32_swap(a, a, false, false);
-  a = max(uint32_t(r32[0]), uint32_t(r32[1]));
-  const auto r16 = __builtin_amdgcn_permlane16_swap(a, a, false, false);
-  return max(uint32_t(r16[0]), uint32_t(r16[1]));
+// Codes by magic-number rounding: fma(u, 1/scale, M) rounds u/scale to an integer (ties to even)
+// for M = 1.5 * 2^23, whose neighbourhood has unit spacing and whose low bits are zero, so the
+// low 4 (8) bits of the clamped sum are the code in two's complement.
+template <int BITS>
+struct TwosMagic {
+  static constexpr float qmax = BITS == 4 ? 7.0f : 127.0f;
+  static constexpr float magic = 12582912.0f;  // 1.5 * 2^23
+};
+
+// fp32 a / (F qmax) for a power of two F, correctly rounded (reciprocal product plus one exact
+// residual correction) and saturated at the fp16 maximum: the scale of a group whose absmax is
+// a / F (the division by F is exact, and 1/(F qmax) rounds like 1/qmax scaled by 1/F)
+template <int BITS, int F>
+__device__ __forceinline__ float scale_of_scaled(float a) {
+  constexpr float q = (BITS == 4 ? 7.0f : 127.0f) * F;
+  constexpr float rq = 1.0f / q;
+  const float y = a * rq;
+  const float r = fmaf(-y, q, a);
+  return fminf(fmaf(r, rq, y), 65504.0f);
 }
 
 // XOR mask that flips the fp16 signs of 8 consecutive channels where sign < 0
@@ -144,7 +156,7 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
   constexpr int NSTEP = D / 32;     // k steps of 32 inputs
   constexpr int CB = D * BITS / 8;  // code bytes per vector
   constexpr int NG = D / 16;        // groups (= channel blocks) per vector
-  using CM = CodeMagic<BITS>;
+  using CM = TwosMagic<BITS>;
   constexpr int HX = SHARED ? 4 : 1;                      // blocks staged per half
   __shared__ __align__(16) uint4 xt[HX][kVecs][NP];       // inputs, piece p of vector v at p ^ v
   __shared__ __align__(16) uint8_t ct[2][kVecs][CB];      // packed codes
@@ -258,50 +270,78 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
         }
       }
     }
-    // u = acc / (16 lambda).  Without lambda the factor is the exact 1/16, applied to the group
-    // maximum and to the group's reciprocal instead of to every value (bit-identical codes)
-    float u[2][4], a[2];
+    // u = acc / (16 lambda).  Without lambda the factor is the exact 1/16, folded into the scale's
+    // divisor and into the group's reciprocal instead of applied to every value (bit-identical
+    // codes), so the maxima below are 16 times the group maxima there
+    float u[2][4], am[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) u[i][j] = HAS_LAMBDA ? acc[i][j] * linv[i][j] : acc[i][j];
-      const uint32_t am = max(max(__float_as_uint(fabsf(u[i][0])), __float_as_uint(fabsf(u[i][1]))),
-                              max(__float_as_uint(fabsf(u[i][2])), __float_as_uint(fabsf(u[i][3]))));
-      a[i] = __uint_as_float(rows_max4(am)) * (HAS_LAMBDA ? 1.0f : 0.0625f);
+      // NaN-propagating maxima of the magnitudes (v_maximum3_f32 with abs modifiers)
+      am[i] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(fabsf(u[i][0]), fabsf(u[i][1])),
+                                            __builtin_elementwise_maximum(fabsf(u[i][2]), fabsf(u[i][3])));
     }
+    // Group maxima over the four 16-lane rows, both groups at once: one v_permlane32_swap of the
+    // two groups' values leaves one group's pairs in one half of the wave and the other group's in
+    // the other half, so after the max and a v_permlane16_swap step each half holds one group's
+    // maximum for every vector.  The scale is then computed once per lane, and a second
+    // v_permlane32_swap hands every lane both groups' values (non-negative floats order like their
+    // bit patterns, NaN above all).
+    uint32_t mh;
+    {
+      const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(am[0]), __float_as_uint(am[1]), false, false);
+      mh = max(uint32_t(r32[0]), uint32_t(r32[1]));
+      const auto r16 = __builtin_amdgcn_permlane16_swap(mh, mh, false, false);
+      mh = max(uint32_t(r16[0]), uint32_t(r16[1]));
+    }
+    float inv[2];
+    uint32_t shb[2];
     if constexpr (PT) {
       // one scale per vector: the absmax over all channels, i.e. over this wave's two groups and
       // then over the waves (every lane of vector n16 holds the same per-wave value)
-      if (r4 == 0) tmax[w][n16] = fmaxf(a[0], a[1]);
+      const auto r = __builtin_amdgcn_permlane32_swap(mh, mh, false, false);
+      if (r4 == 0) tmax[w][n16] = __uint_as_float(max(uint32_t(r[0]), uint32_t(r[1])));
       __syncthreads();
       float m = 0.0f;
 #pragma unroll
       for (int ww = 0; ww < D / 32; ++ww) m = fmaxf(m, tmax[ww][n16]);
-      a[0] = a[1] = m;
+      const _Float16 sh = static_cast<_Float16>(scale_of_scaled<BITS, HAS_LAMBDA ? 1 : 16>(m));
+      const float sf = static_cast<float>(sh);
+      inv[0] = inv[1] = (sf > 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f) * (HAS_LAMBDA ? 1.0f : 0.0625f);
+      shb[0] = shb[1] = __builtin_bit_cast(uint16_t, sh);
+    } else {
+      const _Float16 sh = static_cast<_Float16>(scale_of_scaled<BITS, HAS_LAMBDA ? 1 : 16>(__uint_as_float(mh)));
+      const float sf = static_cast<float>(sh);
+      const float iv = (sf > 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f) * (HAS_LAMBDA ? 1.0f : 0.0625f);
+      const auto ri = __builtin_amdgcn_permlane32_swap(__float_as_uint(iv), __float_as_uint(iv), false, false);
+      inv[0] = __uint_as_float(ri[0]);
+      inv[1] = __uint_as_float(ri[1]);
+      const uint32_t sb = __builtin_bit_cast(uint16_t, sh);
+      const auto rs = __builtin_amdgcn_permlane32_swap(sb, sb, false, false);
+      shb[0] = rs[0];
+      shb[1] = rs[1];
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int g = 2 * w + i;
-      const _Float16 sh = static_cast<_Float16>(scale_of<BITS>(a[i]));
-      const float sf = static_cast<float>(sh);
-      const float inv = (sf > 0.0f ? __builtin_amdgcn_rcpf(sf) : 0.0f) * (HAS_LAMBDA ? 1.0f : 0.0625f);
       uint32_t tq[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        float vq = fmaf(u[i][j], inv, CM::magic);
+        float vq = fmaf(u[i][j], inv[i], CM::magic);
         vq = fminf(fmaxf(vq, CM::magic - CM::qmax), CM::magic + CM::qmax);
         tq[j] = __float_as_uint(vq);
       }
+      // pack the low nibbles (bytes): two shift-or pairs, then one byte permute
       if constexpr (BITS == 4) {
-        const uint32_t byte0 = ((tq[1] << 4) | (tq[0] & 0xfu)) & 0xffu;
-        const uint32_t byte1 = ((tq[3] << 4) | (tq[2] & 0xfu)) & 0xffu;
-        *reinterpret_cast<uint16_t*>(&ct[buf][n16][8 * g + 2 * r4]) = uint16_t((byte0 | (byte1 << 8)) ^ 0x8888u);
+        const uint32_t b0 = (tq[0] & 0xfu) | (tq[1] << 4), b1 = (tq[2] & 0xfu) | (tq[3] << 4);
+        *reinterpret_cast<uint16_t*>(&ct[buf][n16][8 * g + 2 * r4]) = uint16_t(__builtin_amdgcn_perm(b1, b0, 0x0c0c0400u));
       } else {
-        const uint32_t word = ((tq[0] & 0xffu) | ((tq[1] & 0xffu) << 8) | ((tq[2] & 0xffu) << 16) | (tq[3] << 24)) ^
-                              CM::to_twos;
-        *reinterpret_cast<uint32_t*>(&ct[buf][n16][16 * g + 4 * r4]) = word;
+        const uint32_t lo = __builtin_amdgcn_perm(tq[1], tq[0], 0x0c0c0400u);
+        const uint32_t hi = __builtin_amdgcn_perm(tq[3], tq[2], 0x0c0c0400u);
+        *reinterpret_cast<uint32_t*>(&ct[buf][n16][16 * g + 4 * r4]) = lo | (hi << 16);
       }
-      if (r4 == 0 && (!PT || g == 0)) st[buf][n16][g] = __builtin_bit_cast(uint16_t, sh);
+      if (r4 == 0 && (!PT || g == 0)) st[buf][n16][g] = uint16_t(shb[i]);
     }
     __syncthreads();
     // ---- store codes (16 B per thread) and scales ----
