@@ -204,32 +204,47 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
                                           *reinterpret_cast<const float4*>(sign + spc * 8 + 4))
                               : make_uint4(0u, 0u, 0u, 0u);
   uint4 pd[2][H], pm[2][SHARED ? 1 : H];
-  // A block is read through a buffer resource over its vectors (a scalar base at its first
-  // vector) at the thread's fixed byte offset; a vector past the end reads zeros, and its
-  // column of the product is never stored (columns do not mix).
-  const int loff = (sv * D + spc * 8) * 2;
-  auto load_piece = [&](uint32_t blk_, uint4& d_, uint4& m_) {
-    const uint32_t g0 = blk_ * kVecs;
-    const uint32_t nv = min(n_vec - g0, uint32_t(kVecs));
-    const __amdgpu_buffer_rsrc_t r = dec::buf_rsrc(x + int64_t(g0) * D, int64_t(nv) * D * 2);
-    const dec::v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, loff, 0, 0);
-    d_ = make_uint4(uint32_t(v[0]), uint32_t(v[1]), uint32_t(v[2]), uint32_t(v[3]));
-    if constexpr (!SHARED) {
-      const uint32_t gv = min(g0 + sv, n_vec - 1u);
-      const int b = int(fd_heads.div(fd_tok.div(gv)));
-      m_ = sign_mask(*reinterpret_cast<const float4*>(sign + b * sign_bs + spc * 8),
-                     *reinterpret_cast<const float4*>(sign + b * sign_bs + spc * 8 + 4));
-    }
-  };
   // this work-group's blocks: a contiguous range, so consecutive blocks share a row (and its
   // lambda) except at row boundaries
   const uint32_t nblk = (n_vec + kVecs - 1) / kVecs;
+  const uint32_t blk_begin = uint32_t(uint64_t(blockIdx.x) * nblk / gridDim.x);
   const uint32_t blk_end = uint32_t(uint64_t(blockIdx.x + 1) * nblk / gridDim.x);
+  const uint32_t v_end = min(blk_end * uint32_t(kVecs), n_vec);  // the range's vectors end here
+  // A half's H input blocks are read through one buffer resource over the range's vectors from
+  // the half's first block on (a scalar base), at the thread's fixed byte offset in each block:
+  // a vector past the range reads zeros, a block past it is never processed, and a vector past
+  // the range inside a processed block has its column of the product never stored (columns do
+  // not mix).
+  const int loff = (sv * D + spc * 8) * 2;
+  auto load_half = [&](uint32_t first, uint4 (&d_)[H], uint4 (&m_)[SHARED ? 1 : H]) {
+    const uint32_t g0 = first * kVecs;
+    const uint32_t nv = v_end > g0 ? min(v_end - g0, uint32_t(H * kVecs)) : 0u;
+    const __amdgpu_buffer_rsrc_t r = dec::buf_rsrc(x + int64_t(g0) * D, int64_t(nv) * D * 2);
 #pragma unroll
-  for (int i = 0; i < H; ++i) {
-    const uint32_t b0 = uint32_t(uint64_t(blockIdx.x) * nblk / gridDim.x);
-    if (b0 + uint32_t(i) < blk_end) load_piece(b0 + uint32_t(i), pd[0][i], pm[0][SHARED ? 0 : i]);
-  }
+    for (int i = 0; i < H; ++i) {
+      const dec::v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, loff + i * kVecs * D * 2, 0, 0);
+      d_[i] = make_uint4(uint32_t(v[0]), uint32_t(v[1]), uint32_t(v[2]), uint32_t(v[3]));
+      if constexpr (!SHARED) {
+        const uint32_t gv = min(g0 + uint32_t(i * kVecs + sv), n_vec - 1u);
+        const int b = int(fd_heads.div(fd_tok.div(gv)));
+        m_[i] = sign_mask(*reinterpret_cast<const float4*>(sign + b * sign_bs + spc * 8),
+                          *reinterpret_cast<const float4*>(sign + b * sign_bs + spc * 8 + 4));
+      }
+    }
+  };
+  load_half(blk_begin, pd[0], pm[0]);
+  // first slot and in-row position of the block to be stored next (work-group uniform), carried
+  // from block to block: the next block starts kVecs tokens later in the same row unless the row
+  // ends inside this one
+  uint32_t cur_t0 = 0;
+  int64_t cur_slot0 = 0;
+  auto seek = [&](uint32_t b) {
+    const uint32_t gv0 = b * kVecs;
+    const uint32_t row0 = fd_tok.div(gv0);
+    cur_t0 = gv0 - row0 * fd_tok.d;
+    cur_slot0 = int64_t(row0) * capacity + pos + cur_t0;
+  };
+  seek(blk_begin);
 
   // block blk from staged tile f (0..H-1); codes and scales go through LDS buffer f & 1
   auto do_block = [&](uint32_t blk, auto F) {
@@ -348,10 +363,15 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
     {
       // the block's first slot (work-group uniform); a block inside one row needs no division
       const uint32_t gv0 = blk * kVecs;
-      const uint32_t row0 = fd_tok.div(gv0);
-      const uint32_t t0 = gv0 - row0 * fd_tok.d;
+      const uint32_t t0 = cur_t0;
+      const int64_t slot0 = cur_slot0;
       const bool one_row = t0 + kVecs <= fd_tok.d;
-      const int64_t slot0 = int64_t(row0) * capacity + pos + t0;
+      if (t0 + kVecs < fd_tok.d) {
+        cur_t0 = t0 + kVecs;
+        cur_slot0 = slot0 + kVecs;
+      } else {
+        seek(blk + 1);
+      }
       auto vslot = [&](uint32_t gvs, int v) { return one_row ? slot0 + v : slot_of(gvs); };
       constexpr int UNITS = kVecs * CB / 16;  // 16-byte code units
       constexpr int SUNITS = kVecs * NG / 8;  // 16-byte scale units
@@ -387,7 +407,7 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
       }
     }
   };
-  uint32_t blk = uint32_t(uint64_t(blockIdx.x) * nblk / gridDim.x);
+  uint32_t blk = blk_begin;
   while (blk < blk_end) {  // blk advances inside the halves
     static_for<0, 2>([&](auto HF) {
       constexpr int hf = decltype(HF)::value;
@@ -399,11 +419,8 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
         const uint4 v = pd[hf][i];
         xt[i][sv][spc ^ sv] = make_uint4(v.x ^ m.x, v.y ^ m.y, v.z ^ m.z, v.w ^ m.w);
       }
-      // ---- request the next half's blocks of this range (a slot past the range keeps stale data
-      //      and is never processed) ----
-#pragma unroll
-      for (int i = 0; i < H; ++i)
-        if (blk + uint32_t(H + i) < blk_end) load_piece(blk + uint32_t(H + i), pd[1 - hf][i], pm[1 - hf][SHARED ? 0 : i]);
+      // ---- request the next half's blocks of this range ----
+      load_half(blk + uint32_t(H), pd[1 - hf], pm[1 - hf]);
       __syncthreads();
       static_for<0, H>([&](auto F) {
         const uint32_t bk = blk + uint32_t(decltype(F)::value);
