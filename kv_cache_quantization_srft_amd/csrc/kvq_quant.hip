@@ -141,10 +141,11 @@ __device__ __forceinline__ uint4 sign_mask(float4 s0, float4 s1) {
 // Write path of D-dim vectors, 16 vectors per block, 2D threads per work-group: every thread
 // stages one 16-byte piece of one vector; wave w rotates channel blocks 2w, 2w + 1 of all 16
 // vectors with MFMAs (A = 16 Q as fp16 hi + lo from the constant table, B = the sign-flipped
-// fp16 inputs), then scales, rounds and packs them.  Blocks are processed in a grid-stride loop
-// with kPF blocks' inputs in flight; LDS tiles are double-buffered.  SHARED: every row uses sign
-// row 0 (sign_bs == 0), so the sign mask is fixed per thread and the prefetch ring holds data
-// only, which leaves the registers for a deeper ring.
+// fp16 inputs), then scales, rounds and packs them.  Each work-group takes a contiguous range of
+// blocks and walks it in halves, the next half's inputs in flight while the current one is
+// transformed; the code and scale tiles are double-buffered.  SHARED: every row uses sign row 0
+// (sign_bs == 0), so the sign mask is fixed per thread and the in-flight registers hold data
+// only, which leaves room for four blocks per half (one with per-row signs).
 template <int D, int BITS, bool HAS_LAMBDA, bool SHARED, bool PT>
 __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 ? 3 : 2))) void quantize_mfma_kernel(const uint16_t* __restrict__ x, FastDiv fd_tok,
                                                               FastDiv fd_heads, int pos, int capacity,
@@ -193,7 +194,7 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(D == 128 
 
   // this thread's piece: vector sv of the block, channels 8 spc .. 8 spc + 7
   const int sv = tid / NP, spc = tid % NP;
-  // Blocks are processed in halves of H blocks (H = blocks of the grid stride).  A half first
+  // Blocks are processed in halves of H blocks (four, or one with per-row signs).  A half first
   // stages all of its H input blocks (loaded one half earlier) in LDS, then requests the next
   // half's blocks into the other register set, then transforms and stores its blocks.  The
   // loads and stores of a wave share one completion counter and may complete out of order, so
