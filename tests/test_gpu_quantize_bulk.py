@@ -35,6 +35,9 @@ BULK = [
     (256, 4, 2, 3, 3000, True, False, 16, 0, 0, 4),
     (256, 8, 2, 3, 3000, False, True, 16, 5, 40, 4),
     (256, 8, 3, 2, 2999, True, False, 256, 0, 0, 4),
+    # rows of 3 tokens: every block spans several rows, several blocks per work-group
+    (128, 4, 128, 80, 3, True, False, 16, 2, 1, 2),
+    (256, 8, 64, 50, 3, False, True, 16, 0, 0, 2),
 ]
 
 
