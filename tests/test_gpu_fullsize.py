@@ -7,7 +7,8 @@ benchmark times (all layers folded into the batch, one launch per call):
 Decode: the cache is random in-range code bytes and fp16 scales drawn on the device with a seeded
 generator (10.7 GB of planes for the serving shard); sampled (sequence, kv head) units are read
 back and compared with the oracle's attention over those planes, 2e-3 max-abs.  The fused
-append (the benchmark's decode step) is checked the same way plus the new token's bytes.
+append (the benchmark's decode step) is checked the same way plus the new token's bytes, and so
+are the serving shard's multi-token attention (4 query tokens, causal) and 4096-position window.
 
 Write path: the whole prefill of one tensor (K) is quantized in one call from fp16 values drawn on
 the device; sampled vectors (random ones, the first and last vectors of work-group ranges and
@@ -105,6 +106,46 @@ def test_decode_full_size(cid, append):
         worst = max(worst, err)
         assert err <= ATTN_ATOL, f"{w.name} unit ({b}, {j}): max-abs {err:.3g}"
     say("full-size decode", w.name, call, "worst max-abs", f"{worst:.3g}", "max |out|", f"{np.abs(got).max():.3g}")
+
+
+@pytest.mark.parametrize("T,window", [(4, 0), (1, 4096)])
+def test_attn_full_size(T, window):
+    """kvq_attn on the full serving-shard cache in the benchmark's configuration: 4 query tokens per
+    sequence (causal, speculative verification) and a 4096-position sliding window."""
+    w = W[5]
+    rng = np.random.default_rng(50 + T + window)
+    lay, (kc, ks, vc, vs) = _device_planes(w, 1005)
+    LB, H, G, d, S = lay.batch, lay.kv_heads, w.q_heads // w.kv_heads, w.head_dim, w.seq_len
+    opts = kvq.make_attn_opts(n_query=T, window=window)
+    p = kvq.kvq_attn_launch_plan(lay, opts, S)
+    pl = {f: getattr(p, f) for f, _ in p._fields_}
+    say("full-size attn", w.name, T, window, pl)
+    q = synth.to_fp16(rng.standard_normal((LB, T, w.q_heads, d)))
+    s = synth.signs(w)
+    ws = torch.zeros(kvq.kvq_attn_workspace_bytes(lay, opts, S), dtype=torch.uint8, device="cuda")
+    out = torch.full((LB, T, w.q_heads, d), float("nan"), dtype=torch.float32, device="cuda")
+    kvq.kvq_attn(lay, opts, dev(q), kc, ks, vc, vs, None, 0, 0, 0, S, None, dev(s), dev(s), 0, None, None, 0, 0.0,
+                 ws, out)
+    torch.cuda.synchronize()
+    assert int(ws[:65536].count_nonzero()) == 0, "completion counters not left at zero"
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    worst = 0.0
+    for b, j in _sample_units(rng, lay, 5):
+        kb = _row(kc, lay, b, j, d * w.k_bits // 8, np.uint8)
+        kss = _row(ks, lay, b, j, d // 16, np.float16)
+        vb = _row(vc, lay, b, j, d * w.v_bits // 8, np.uint8)
+        vss = _row(vs, lay, b, j, d // 16, np.float16)
+        # a window reads only the latest positions: the oracle takes those (and 64 before them)
+        t0 = max(S - window - 64, 0) if window else 0
+        kcodes = O.unpack_codes(kb[t0:S], w.k_bits)[None, None]
+        vcodes = O.unpack_codes(vb[t0:S], w.v_bits)[None, None]
+        ref = O.prefix_attention_quantized(q[b:b + 1, :, j * G:(j + 1) * G], kcodes, kss[t0:S][None, None], vcodes,
+                                           vss[t0:S][None, None], s, s, 1.0, 1.0, S - t0, T, window)[0]
+        err = float(np.abs(got[b, :, j * G:(j + 1) * G] - ref).max())
+        worst = max(worst, err)
+        assert err <= ATTN_ATOL, f"{w.name} T {T} window {window} unit ({b}, {j}): max-abs {err:.3g}"
+    say("full-size attn", w.name, T, window, "worst max-abs", f"{worst:.3g}", "max |out|", f"{np.abs(got).max():.3g}")
 
 
 def _device_values(w, seed):
