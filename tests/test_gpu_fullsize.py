@@ -8,7 +8,8 @@ Decode: the cache is random in-range code bytes and fp16 scales drawn on the dev
 generator (10.7 GB of planes for the serving shard); sampled (sequence, kv head) units are read
 back and compared with the oracle's attention over those planes, 2e-3 max-abs.  The fused
 append (the benchmark's decode step) is checked the same way plus the new token's bytes, and so
-are the serving shard's multi-token attention (4 query tokens, causal) and 4096-position window.
+are the serving shard's multi-token attention (4 query tokens, causal) and 4096-position window,
+and the paged decode over the cache cut into shuffled 256-token pages.
 
 Write path: the whole prefill of one tensor (K) is quantized in one call from fp16 values drawn on
 the device; sampled vectors (random ones, the first and last vectors of work-group ranges and
@@ -106,6 +107,63 @@ def test_decode_full_size(cid, append):
         worst = max(worst, err)
         assert err <= ATTN_ATOL, f"{w.name} unit ({b}, {j}): max-abs {err:.3g}"
     say("full-size decode", w.name, call, "worst max-abs", f"{worst:.3g}", "max |out|", f"{np.abs(got).max():.3g}")
+
+
+def _paged_copy(planes, LB, H, S, page, seed):
+    """The planes cut into pages of `page` tokens and stored in a shuffled page order; returns the
+    paged planes and the page table [LB, S / page]."""
+    pps = S // page
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    perm = torch.randperm(LB * pps, generator=g).to("cuda")
+    out = []
+    for t in planes:
+        wb = t.numel() // (LB * H * S)
+        nat = t.view(LB, H, pps, page, wb).permute(0, 2, 1, 3, 4).reshape(LB * pps, H, page, wb)
+        pg = torch.empty_like(nat)
+        pg[perm] = nat
+        out.append(pg.view(-1))
+    return out, perm.view(LB, pps).to(torch.int32).contiguous()
+
+
+@pytest.mark.parametrize("cid", [4, 5])
+def test_paged_decode_full_size(cid):
+    """kvq_decode_attn_paged over the full cache cut into 256-token pages in a shuffled order, as
+    benchmarked; sampled units against the oracle over the logical rows."""
+    w = W[cid]
+    rng = np.random.default_rng(70 + cid)
+    lay, planes = _device_planes(w, 1000 + cid)
+    LB, H, G, d, S = lay.batch, lay.kv_heads, w.q_heads // w.kv_heads, w.head_dim, w.seq_len
+    page = 256
+    paged, table = _paged_copy(planes, LB, H, S, page, 9 + cid)
+    pl = plan(lay, "decode_paged", S)
+    say("full-size paged decode", w.name, pl)
+    q = synth.to_fp16(rng.standard_normal((LB, w.q_heads, d)))
+    s = synth.signs(w)
+    lk = synth.random_lambda(rng, (LB, H, d), 0.5, 2.0) if w.calibrate else None
+    lv = synth.random_lambda(rng, (LB, H, d), 0.5, 2.0) if w.calibrate else None
+    lbs = H * d if w.calibrate else 0
+    ws = torch.zeros(kvq.kvq_decode_attn_workspace_bytes(lay, S), dtype=torch.uint8, device="cuda")
+    out = torch.full((LB, w.q_heads, d), float("nan"), dtype=torch.float32, device="cuda")
+    kvq.kvq_decode_attn_paged(lay, dev(q), None, None, *paged, table, S // page, page, LB * (S // page), S, None,
+                              dev(s), dev(s), 0, None if lk is None else dev(lk), None if lv is None else dev(lv), lbs,
+                              0.0, ws, out)
+    torch.cuda.synchronize()
+    del paged
+    assert int(ws[:65536].count_nonzero()) == 0, "completion counters not left at zero"
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    kc, ks, vc, vs = planes
+    worst = 0.0
+    for b, j in _sample_units(rng, lay, 5):
+        rows = (_row(kc, lay, b, j, d * w.k_bits // 8, np.uint8), _row(ks, lay, b, j, d // 16, np.float16),
+                _row(vc, lay, b, j, d * w.v_bits // 8, np.uint8), _row(vs, lay, b, j, d // 16, np.float16))
+        ref = oracle_unit(q[b, j * G:(j + 1) * G], *rows, w.k_bits, w.v_bits, s, s,
+                          None if lk is None else lk[b, j], None if lv is None else lv[b, j], S)
+        err = float(np.abs(got[b, j * G:(j + 1) * G] - ref).max())
+        worst = max(worst, err)
+        assert err <= ATTN_ATOL, f"{w.name} paged unit ({b}, {j}): max-abs {err:.3g}"
+    say("full-size paged decode", w.name, "worst max-abs", f"{worst:.3g}", "max |out|", f"{np.abs(got).max():.3g}")
 
 
 @pytest.mark.parametrize("T,window", [(4, 0), (1, 4096)])
